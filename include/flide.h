@@ -1,0 +1,340 @@
+/*
+ * flide.h — C ABI of the ForkAttention hot path for one MI355X (gfx950).
+ *
+ * One round of decision requests (a shared trunk s of P tokens plus questions
+ * q_1..q_n per request) is executed as one flat, padding-free token stream
+ * whose tree structure lives in device-resident metadata.  Sources, cited by
+ * page title and section:
+ *
+ *  [ZH] "Flide: Accelerating Decision Inference with Exact State Forking"
+ *       (paper.rainbus.top/paper/2610.42148): §前置知识 (Eq. (1), the gated
+ *       delta rule), §核心方法 (flat stream, (j, c, t) metadata, two-call GDN,
+ *       graphs bucketed by stream length T), §方法步骤详情 (stream order,
+ *       visibility rule, sliding window, conv tail read by index, capacity
+ *       split, selective readout, checkpoints at m).
+ *  [KO] "Flide는 공유 상태를 정확히 분기해 결정 추론을 최대 9.5배 빠르게 한다"
+ *       (onedev.kr/papers/1551): §어떻게 동작하나 (problem, Eq. (1)),
+ *       §무엇과 다른가 (positions continue from P, Proposition 3.1),
+ *       §어떻게 쓰나 (flat-graph execution, tail-only padding, request-boundary
+ *       splitting, eager path for one oversized request, checkpoints,
+ *       deterministic mode).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every function returns a flide_status; no C++ exception crosses the ABI.
+ *  - Host-side validation runs before anything is enqueued: on an error
+ *    nothing is launched and no caller memory is written.
+ *  - "host" pointers point to CPU memory, "device" pointers to memory on the
+ *    context's GPU.  The caller owns every buffer it passes; the library owns
+ *    only what hangs off a flide_ctx (pinned staging, rotary tables, graphs).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    device work is stream ordered and asynchronous; only flide_check_device
+ *    synchronises.
+ *  - Outputs must not alias inputs.
+ *  - One host thread at a time per flide_ctx.
+ *
+ * Stream layout (Flide summary [ZH] §方法步骤详情): all trunks in request
+ * order, then all questions grouped by request, in question order.  Row
+ * metadata (j, c, t): request, branch (0 = trunk, i = question i, 1-based),
+ * position; question positions continue from P ([KO] §무엇과 다른가).  Rows
+ * past T up to the capacity are tail padding with (j, c, t) = (-1, -1, -1);
+ * kernels leave their outputs untouched.
+ */
+#ifndef FLIDE_H
+#define FLIDE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLIDE_OK = 0,
+  FLIDE_E_INVALID_ARG = 1, /* a host-side check failed; nothing was enqueued        */
+  FLIDE_E_CAPACITY = 2,    /* the round does not fit the capacity / no bucket fits  */
+  FLIDE_E_UNSUPPORTED = 3, /* a shape or dtype the kernels do not implement         */
+  FLIDE_E_HIP = 4,         /* a HIP runtime call failed (see flide_last_error)      */
+  FLIDE_E_DEVICE = 5,      /* a device-side metadata check tripped                  */
+  FLIDE_E_INTERNAL = 6     /* unexpected failure inside the library                 */
+} flide_status;
+
+typedef enum { FLIDE_F32 = 0, FLIDE_BF16 = 1 } flide_dtype;
+
+typedef struct flide_ctx flide_ctx;
+
+/* Static description of the status code (never NULL). */
+const char* flide_status_string(int32_t status);
+/* Library version string (never NULL). */
+const char* flide_version(void);
+
+/* ------------------------------------------------------------------------
+ * Requests and capacities (host structures)
+ * ------------------------------------------------------------------------ */
+
+/* One decision request r = (s, q_1..q_n) ([KO] §어떻게 동작하나).
+ *  P         trunk length including any checkpointed prefix, >= 0
+ *  m         resume position, 0 <= m <= P; the stream holds trunk positions m..P-1
+ *            (checkpoint resume, [KO] §어떻게 쓰나)
+ *  n_q       number of questions, >= 0
+ *  q_len     host array of n_q lengths, each >= 1 (may be NULL when n_q == 0)
+ *  ckpt_slot pool slot holding the checkpoint at m (GDN state, conv window,
+ *            attention K/V of positions 0..m-1); required when m > 0, else -1
+ *  out_slot  pool slot that receives S_P and the conv window after the trunk,
+ *            >= 0 and != ckpt_slot when m > 0                                  */
+typedef struct {
+  int32_t P;
+  int32_t m;
+  int32_t n_q;
+  const int32_t* q_len;
+  int32_t ckpt_slot;
+  int32_t out_slot;
+} flide_request;
+
+/* Capacity of a metadata image / graph bucket: stream rows, requests, questions. */
+typedef struct {
+  int32_t T_cap;
+  int32_t R_cap;
+  int32_t Q_cap;
+} flide_caps;
+
+/* Word offsets (int32 units) of the arrays inside a metadata image.  The first
+ * `host_words` words are written by flide_plan_round and uploaded as is; the
+ * per-row arrays tok_j/tok_c/tok_t and the device error words are filled on the
+ * device.  Segments are ordered trunks first (index j = request j), then
+ * questions in stream order.
+ *   hdr[0..15]  T, R, n_seg, n_qst, n_tiles, max_pos, 0..., magic
+ *   seg_*       [seg_cap]  row0, len, req, branch, pos0, state (slot or -1)
+ *   req_*       [R_cap]    trunk_row0, P, m, ckpt_slot, out_slot, q_seg0, n_q
+ *   qfin_row    [Q_cap]    last stream row of every question (stream order)
+ *   tile_seg    [tile_cap] attention work list: segment of each tile
+ *   tile_row0   [tile_cap]                      first stream row of each tile
+ *   tok_j/c/t   [T_cap]    per-row metadata (device only)
+ *   dev_error   [4]        device error word (device only)                     */
+typedef struct {
+  int64_t host_words;
+  int64_t dev_words;
+  int64_t hdr;
+  int64_t seg_row0, seg_len, seg_req, seg_branch, seg_pos0, seg_state;
+  int64_t req_trunk_row0, req_P, req_m, req_ckpt, req_out, req_q_seg0, req_nq;
+  int64_t qfin_row;
+  int64_t tile_seg, tile_row0;
+  int64_t tok_j, tok_c, tok_t;
+  int64_t dev_error;
+  int32_t seg_cap;
+  int32_t tile_cap;
+  int32_t tile_rows; /* query rows per attention tile */
+  int32_t reserved;
+} flide_meta_layout;
+
+/* Offsets and sizes of a metadata image for `caps` (host only, no GPU needed).
+ * Errors: FLIDE_E_INVALID_ARG for NULL pointers or capacities < 1 or too large. */
+flide_status flide_meta_layout_for(const flide_caps* caps, flide_meta_layout* out);
+
+/* Stream rows T, segments and questions a round needs (host only).
+ * Errors: FLIDE_E_INVALID_ARG for an invalid request (m > P, |q| < 1, m > 0
+ * without a checkpoint slot, negative sizes, ...).                            */
+flide_status flide_plan_sizes(const flide_request* reqs, int32_t R, int32_t* T, int32_t* n_seg,
+                              int32_t* n_qst);
+
+/* Host planner ([ZH] §方法步骤详情 first step; [KO] §어떻게 쓰나): writes the
+ * metadata image of the round into `image` (host, `image_words` >= host_words
+ * of the layout for `caps`).  Segment lengths, positions, key ranges (via the
+ * request table) and state indices; the attention tile list; question-final
+ * rows.  Errors: FLIDE_E_INVALID_ARG (bad request), FLIDE_E_CAPACITY (T, R or
+ * the number of questions exceeds `caps`).  `image` is untouched on error.     */
+flide_status flide_plan_round(const flide_request* reqs, int32_t R, const flide_caps* caps, int32_t* image,
+                              int64_t image_words);
+
+/* Request-boundary split ([KO] §어떻게 쓰나; [ZH] §方法步骤详情 third step):
+ * greedy in request order, at most T_max rows per sub-round; a request with
+ * more than T_max rows is a sub-round of its own flagged eager (run without a
+ * graph).  sub_first (host, R+1 entries) receives the first request of every
+ * sub-round plus a final R; eager (host, R entries) one flag per sub-round;
+ * *n_sub the number of sub-rounds.  Errors: FLIDE_E_INVALID_ARG.              */
+flide_status flide_split_round(const flide_request* reqs, int32_t R, int32_t T_max, int32_t* sub_first,
+                               int32_t* n_sub, uint8_t* eager);
+
+/* ------------------------------------------------------------------------
+ * Context
+ * ------------------------------------------------------------------------ */
+
+/* Create a context on HIP device `device` (makes it current on this thread).
+ * Errors: FLIDE_E_INVALID_ARG (NULL out), FLIDE_E_HIP (no such device, or not gfx950). */
+flide_status flide_create(flide_ctx** out, int32_t device);
+/* Free graphs, pinned staging and rotary tables.  Never frees caller memory.
+ * Synchronises the device first.  NULL is a no-op. */
+void flide_destroy(flide_ctx* ctx);
+/* Message of the last failing call on this context ("" if none; never NULL). */
+const char* flide_last_error(const flide_ctx* ctx);
+
+/* Upload a metadata image and expand the per-row arrays on the device.
+ * image (host): written by flide_plan_round for `caps`; dev_meta (device):
+ * layout.dev_words int32 words.  The image is copied into library-owned pinned
+ * staging before the call returns, so the caller may reuse `image` at once.
+ * Errors: FLIDE_E_INVALID_ARG (NULL, header inconsistent with caps), FLIDE_E_HIP. */
+flide_status flide_meta_upload(flide_ctx* ctx, const flide_caps* caps, const int32_t* image, int32_t* dev_meta,
+                               void* stream);
+
+/* ------------------------------------------------------------------------
+ * Token-mixing kernels (every tensor is device memory owned by the caller)
+ * ------------------------------------------------------------------------ */
+
+/* Tree-masked varlen attention, full or sliding window ([ZH] §方法步骤详情:
+ * key y is visible from query x iff j_y = j_x, c_y in {0, c_x}, t_y <= t_x, and
+ * for a window layer t_x - t_y < W).  Rotary embedding at the metadata
+ * positions (rotate-half pairs (i, i + d/2), angle t * theta^(-2i/d), fp64 host
+ * table stored as fp32).  Grouped-query heads: q head h reads kv head
+ * h / (Hq / Hkv).  Scores scaled by 1/sqrt(d); fp32 softmax and accumulation.
+ *  Hq, Hkv, d   heads and head size; Hq % Hkv == 0.  bf16: d == 256 or 128
+ *               (MFMA path); f32: any even d <= 256.
+ *  window       0 = full attention, else W >= 1
+ *  theta        rotary base
+ *  max_pos      exclusive bound on every position of the rounds run (rotary table size)
+ *  cache_rows, cache_slots  shape of the K/V cache (0 if no request resumes)
+ *  deterministic 1 = per-question tiles and a fixed key order (the kernels
+ *               already use a composition-independent order; the flag is
+ *               accepted for interface stability)                              */
+typedef struct {
+  int32_t Hq, Hkv, d, window;
+  double theta;
+  int32_t max_pos;
+  int32_t cache_rows;  /* rows per K/V cache slot (>= the largest m), 0 if no cache */
+  int32_t cache_slots; /* slots of the K/V cache, 0 if no cache                     */
+  int32_t dtype;       /* flide_dtype of q, k, v, caches and o                      */
+  int32_t deterministic;
+} flide_attn_params;
+
+/* Bytes of the workspace flide_fork_attn needs for `caps` (rotated keys). */
+flide_status flide_attn_workspace_bytes(const flide_caps* caps, const flide_attn_params* p, int64_t* bytes);
+
+/*  q        [T_cap, Hq, d]   queries, not yet rotated
+ *  k, v     [T_cap, Hkv, d]  keys (not yet rotated) and values
+ *  k_cache  [slots, cache_rows, Hkv, d] keys of positions 0..m-1, already
+ *           rotated; v_cache the matching values.  Read for requests with m > 0
+ *           from slot ckpt_slot; may be NULL when no request resumes.
+ *  o        [T_cap, Hq, d]   output rows 0..T-1 (tail rows untouched)
+ *  workspace device scratch of flide_attn_workspace_bytes bytes
+ * Errors: FLIDE_E_INVALID_ARG, FLIDE_E_UNSUPPORTED (dims/dtype), FLIDE_E_HIP. */
+flide_status flide_fork_attn(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
+                             const flide_attn_params* p, const void* q, const void* k, const void* v,
+                             const void* k_cache, const void* v_cache, void* o, void* workspace, void* stream);
+
+/* Gated DeltaNet layer, two calls ([ZH] §前置知识 and §方法步骤详情; [KO]
+ * §무엇과 다른가): causal depthwise conv over the raw q|k|v channels (width
+ * conv_k, tap conv_k-1 multiplies the current row, no bias), optional SiLU,
+ * per-head L2 normalisation of q and k (x / sqrt(sum x^2 + 1e-6)), then
+ *     S_t = alpha_t S_{t-1} (I - eta_t k_t k_t^T) + eta_t v_t k_t^T,  o_t = S_t q_t
+ * with an fp32 state S of [dv, dk] per head.
+ *  phase 0 (FLIDE_GDN_TRUNKS): every trunk segment from a zero state and zero
+ *     conv history, or, for m > 0, from state_pool/conv_pool[ckpt_slot]; writes
+ *     S_P to state_pool[out_slot] and the last conv_k-1 raw trunk inputs to
+ *     conv_pool[out_slot].
+ *  phase 1 (FLIDE_GDN_QUESTIONS): every question segment at once, each seeded
+ *     by index from state_pool/conv_pool[its request's out_slot] (no copy);
+ *     the pools are only read.
+ * Parameters: H heads, dk = dv in {32, 64, 128} (bf16) or any <= 128 (f32),
+ * conv_k in 1..4, act 0 = none, 1 = SiLU, chunk = rows per chunk (64).
+ *  x          [T_cap, H*(2dk+dv)] raw inputs, channels q | k | v, head-major
+ *  conv_w     [H*(2dk+dv), conv_k] fp32
+ *  alpha, eta [T_cap, H] fp32
+ *  state_pool [n_slots, H, dv, dk] fp32
+ *  conv_pool  [n_slots, conv_k-1, H*(2dk+dv)] in the dtype of x
+ *  o          [T_cap, H, dv] in the dtype of x (tail rows untouched)
+ * Errors: FLIDE_E_INVALID_ARG, FLIDE_E_UNSUPPORTED, FLIDE_E_HIP.  A slot index
+ * outside [0, n_slots) found on the device sets the device error word.      */
+typedef enum { FLIDE_GDN_TRUNKS = 0, FLIDE_GDN_QUESTIONS = 1 } flide_gdn_phase;
+typedef struct {
+  int32_t H, dk, dv, conv_k;
+  int32_t act;
+  int32_t chunk;
+  int32_t dtype;
+  int32_t deterministic;
+} flide_gdn_params;
+
+flide_status flide_fork_gdn(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
+                            const flide_gdn_params* p, int32_t phase, const void* x, const float* conv_w,
+                            const float* alpha, const float* eta, float* state_pool, void* conv_pool,
+                            int32_t n_slots, void* o, void* stream);
+
+/* Selective readout, Eq. (1) ([KO] §어떻게 동작하나; [ZH] §方法步骤详情 fourth
+ * step): for question i (stream order), h = H[qfin_row[i]] and
+ * p_i(o) = softmax over o in O_i of w_o^T h, logits accumulated in fp32.
+ *  h        [T_cap, hidden] (dtype)       w_opt [n_opt_rows, hidden] (dtype)
+ *  opt_off  [n_qst + 1] int32 CSR offsets; opt_id [opt_off[n_qst]] rows of w_opt
+ *  probs    [opt_off[n_qst]] fp32
+ * Errors: FLIDE_E_INVALID_ARG, FLIDE_E_UNSUPPORTED, FLIDE_E_HIP; an option row
+ * outside [0, n_opt_rows) found on the device sets the device error word.   */
+typedef struct {
+  int32_t hidden;
+  int32_t dtype;
+} flide_readout_params;
+
+flide_status flide_readout(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
+                           const flide_readout_params* p, const void* h, const void* w_opt,
+                           const int32_t* opt_off, const int32_t* opt_id, int32_t n_opt_rows, float* probs,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
+ * Whole rounds: graph buckets per stream capacity ([ZH] §核心方法 and
+ * §方法步骤详情 third step; [KO] §어떻게 쓰나)
+ * ------------------------------------------------------------------------ */
+
+/* Every buffer of one round at one capacity.  Layer 0 is a full-attention
+ * layer; layer 1 (n_attn == 2) an optional sliding-window layer.  The GDN
+ * layer runs phase 0 then phase 1; the readout runs last.  Buffers must stay
+ * alive as long as a graph captured from them.                                */
+typedef struct {
+  flide_caps caps;
+  int32_t* dev_meta;
+  int32_t n_attn;
+  flide_attn_params attn[2];
+  const void* q[2];
+  const void* k[2];
+  const void* v[2];
+  const void* k_cache[2];
+  const void* v_cache[2];
+  void* o_attn[2];
+  void* attn_ws[2];
+  flide_gdn_params gdn;
+  const void* x;
+  const float* conv_w;
+  const float* alpha;
+  const float* eta;
+  float* state_pool;
+  void* conv_pool;
+  int32_t n_slots;
+  void* o_gdn;
+  flide_readout_params ro;
+  const void* h;
+  const void* w_opt;
+  const int32_t* opt_off;
+  const int32_t* opt_id;
+  int32_t n_opt_rows;
+  float* probs;
+} flide_round_bufs;
+
+/* Capture the whole round (metadata expansion, GDN phases 0 and 1, attention
+ * layers, readout) into a HIP graph for capacity bufs->caps.  Launch shapes
+ * depend only on the capacity; kernels read their work from the metadata.
+ * *bucket_id receives the bucket's id.  Errors: FLIDE_E_INVALID_ARG,
+ * FLIDE_E_UNSUPPORTED, FLIDE_E_HIP.                                           */
+flide_status flide_graph_capture(flide_ctx* ctx, const flide_round_bufs* bufs, void* stream, int32_t* bucket_id);
+/* Smallest captured bucket whose capacity holds (T, R, n_q); FLIDE_E_CAPACITY if none. */
+flide_status flide_select_bucket(const flide_ctx* ctx, int32_t T, int32_t R, int32_t n_q, int32_t* bucket_id);
+/* Upload `image` (host, planned for the bucket's caps) into the bucket's
+ * metadata through double-buffered pinned staging, then launch the graph. */
+flide_status flide_graph_replay(flide_ctx* ctx, int32_t bucket_id, const int32_t* image, void* stream);
+/* The same kernel sequence launched one by one (no graph), e.g. for a single
+ * request above the largest capacity ([KO] §어떻게 쓰나).                      */
+flide_status flide_round_eager(flide_ctx* ctx, const flide_round_bufs* bufs, const int32_t* image, void* stream);
+
+/* Synchronise `stream`, read and clear the device error word of dev_meta.
+ * Returns FLIDE_E_DEVICE (with a message) if a kernel flagged bad metadata.  */
+flide_status flide_check_device(flide_ctx* ctx, const flide_caps* caps, int32_t* dev_meta, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLIDE_H */

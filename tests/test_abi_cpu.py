@@ -1,0 +1,149 @@
+"""C ABI checks that need no GPU: exported symbols, the host planner and the split rule.
+
+The planner's metadata must equal the oracle's independent builder bit for bit
+(stream order, (j, c, t) labels, state indices, question-final rows).
+"""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from oracle import layout as olayout
+from tree_forked_hybrid_amd import flide as F
+from workloads import Request, make_round
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flide.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(flide_[a-z_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    lib = F.load_library()
+    declared = _declared_functions()
+    assert len(declared) >= 18
+    out = subprocess.run(["nm", "-D", "--defined-only", F.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(ln.split()[-1] for ln in out.splitlines() if ln.strip())
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(lib, name)
+    # the binding wraps exactly the declared entry points
+    assert sorted(F.exported_names()) == declared
+
+
+def test_status_strings_and_version():
+    lib = F.load_library()
+    for s in range(7):
+        assert lib.flide_status_string(s)
+    assert lib.flide_status_string(99) == b"unknown status"
+    assert "gfx950" in F.flide_version()
+
+
+def _planner_layout(reqs, caps):
+    img = F.flide_plan_round(reqs, caps)
+    return F.decode_image(img, caps)
+
+
+def _assert_same_layout(reqs, caps):
+    got = _planner_layout(reqs, caps)
+    ref = olayout.build_layout(reqs)
+    for key in ("T", "R", "n_seg", "n_qst"):
+        assert got[key] == ref[key], key
+    for key in ("seg_row0", "seg_len", "seg_req", "seg_branch", "seg_pos0", "seg_state", "req_trunk_row0",
+                "req_q_seg0", "qfin_row"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    np.testing.assert_array_equal(got["req_P"], [r.P for r in reqs])
+    np.testing.assert_array_equal(got["req_m"], [r.m for r in reqs])
+    np.testing.assert_array_equal(got["req_nq"], [len(r.q_len) for r in reqs])
+    # the tile list covers every row of every segment exactly once, tiles aligned to segment starts
+    cover = np.zeros(ref["T"], np.int32)
+    for s, r0 in zip(got["tile_seg"], got["tile_row0"]):
+        a = r0 - ref["seg_row0"][s]
+        assert a % 32 == 0 and 0 <= a < ref["seg_len"][s]
+        n = min(32, ref["seg_len"][s] - a)
+        cover[r0:r0 + n] += 1
+    assert (cover == 1).all()
+    return got
+
+
+@pytest.mark.parametrize("config", [0, 1, 2, 4])
+def test_planner_matches_oracle_on_workloads(config):
+    rnd = make_round(config, 0)
+    T = sum((r.P - r.m) + sum(r.q_len) for r in rnd.requests)
+    caps = F.caps_of(T + 5, len(rnd.requests), sum(len(r.q_len) for r in rnd.requests))
+    got = _assert_same_layout(rnd.requests, caps)
+    assert got["max_pos"] == max(r.P + max(r.q_len) for r in rnd.requests)
+
+
+def test_planner_worked_example_tiles():
+    rnd = make_round(0, 0)
+    got = _planner_layout(rnd.requests, F.caps_of(69, 1, 3))
+    # questions (49+ keys) first, then the trunk tile 32..47 (48 keys), then 0..31
+    assert got["tile_row0"].tolist() == [60, 53, 48, 32, 0]
+
+
+_req = st.builds(
+    lambda P, m_frac, qs, slot: (P, min(P, int(P * m_frac)), qs, slot),
+    st.integers(0, 70), st.sampled_from([0.0, 0.0, 0.5, 1.0]),
+    st.lists(st.integers(1, 40), min_size=0, max_size=5), st.integers(0, 3))
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.lists(_req, min_size=1, max_size=6))
+def test_planner_matches_oracle_random(raw):
+    reqs = []
+    for j, (P, m, qs, _) in enumerate(raw):
+        reqs.append(Request(P=P, m=m, q_len=tuple(qs), n_opt=(2,) * len(qs),
+                            ckpt_slot=(100 + j if m > 0 else -1), out_slot=j))
+    T = sum((r.P - r.m) + sum(r.q_len) for r in reqs)
+    caps = F.caps_of(max(T, 1), len(reqs), max(1, sum(len(r.q_len) for r in reqs)))
+    _assert_same_layout(reqs, caps)
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.lists(st.integers(0, 120), min_size=0, max_size=12), st.integers(1, 150))
+def test_split_matches_oracle(rows, t_max):
+    reqs = [Request(P=r, m=0, q_len=(), n_opt=(), out_slot=j) for j, r in enumerate(rows)]
+    assert F.flide_split_round(reqs, t_max) == olayout.split_round(reqs, t_max)
+
+
+@pytest.mark.parametrize("bad", [
+    [Request(P=4, m=5, q_len=(1,), n_opt=(1,), ckpt_slot=0, out_slot=1)],
+    [Request(P=4, m=2, q_len=(1,), n_opt=(1,), ckpt_slot=-1, out_slot=1)],
+    [Request(P=4, m=2, q_len=(1,), n_opt=(1,), ckpt_slot=1, out_slot=1)],
+    [Request(P=4, m=0, q_len=(0,), n_opt=(1,), out_slot=1)],
+    [Request(P=4, m=0, q_len=(1,), n_opt=(1,), out_slot=-1)],
+    [Request(P=4, m=0, q_len=(), n_opt=(), out_slot=1), Request(P=3, m=0, q_len=(), n_opt=(), out_slot=1)],
+    [Request(P=4, m=2, q_len=(), n_opt=(), ckpt_slot=5, out_slot=1),
+     Request(P=3, m=0, q_len=(), n_opt=(), out_slot=5)],
+])
+def test_planner_rejects_invalid_rounds(bad):
+    caps = F.caps_of(64, 4, 4)
+    image = np.full(F.flide_meta_layout_for(caps).host_words, 7, np.int32)
+    with pytest.raises(F.FlideError) as e:
+        F.flide_plan_round(bad, caps, image)
+    assert e.value.status == F.FLIDE_E_INVALID_ARG
+    assert (image == 7).all()  # untouched on error
+
+
+def test_planner_capacity_errors():
+    reqs = [Request(P=40, m=0, q_len=(10, 10), n_opt=(2, 2), out_slot=0)]
+    for caps in (F.caps_of(59, 1, 2), F.caps_of(60, 1, 1)):
+        with pytest.raises(F.FlideError) as e:
+            F.flide_plan_round(reqs, caps)
+        assert e.value.status == F.FLIDE_E_CAPACITY
+    F.flide_plan_round(reqs, F.caps_of(60, 1, 2))
+
+
+def test_layout_rejects_bad_capacity():
+    for caps in (F.caps_of(0, 1, 1), F.caps_of(10, 0, 1), F.caps_of(10, 1, -1)):
+        with pytest.raises(F.FlideError):
+            F.flide_meta_layout_for(caps)

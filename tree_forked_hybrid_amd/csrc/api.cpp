@@ -1,0 +1,511 @@
+// C ABI: context, validation, kernel dispatch and graph buckets.
+//
+// Flat-graph execution (Korean summary §어떻게 쓰나; "Flide: Accelerating
+// Decision Inference with Exact State Forking" §核心方法 and §方法步骤详情,
+// third step): one HIP graph is captured per stream capacity; a round writes
+// its metadata into the bucket's device buffer (one small host-to-device copy
+// from pinned staging) and replays the graph.  Kernels size their work from
+// the metadata, so the launch shapes depend only on the capacity.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "flide_internal.hpp"
+
+using namespace flide;
+
+namespace {
+
+struct RopeTable {
+  double theta;
+  int d;
+  int max_pos;
+  float* dev;
+};
+
+struct Staging {
+  int32_t* host[2] = {nullptr, nullptr};
+  hipEvent_t done[2] = {nullptr, nullptr};
+  int64_t words = 0;
+  int next = 0;
+};
+
+struct Bucket {
+  flide_round_bufs bufs;
+  flide_meta_layout L;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  Staging st;
+};
+
+}  // namespace
+
+struct flide_ctx {
+  int device = 0;
+  std::string err;
+  std::vector<RopeTable> ropes;
+  std::vector<Bucket*> buckets;
+  Staging direct;
+  hipStream_t capture_stream = nullptr;
+};
+
+namespace {
+
+flide_status fail(flide_ctx* ctx, flide_status st, const std::string& msg) {
+  if (ctx) ctx->err = msg;
+  return st;
+}
+
+#define FLIDE_HIP(ctx, call)                                                                          \
+  do {                                                                                                \
+    hipError_t e_ = (call);                                                                           \
+    if (e_ != hipSuccess)                                                                             \
+      return fail(ctx, FLIDE_E_HIP, std::string(#call) + ": " + hipGetErrorString(e_));                \
+  } while (0)
+
+#define FLIDE_TRY(expr)                     \
+  do {                                      \
+    flide_status s_ = (expr);               \
+    if (s_ != FLIDE_OK) return s_;          \
+  } while (0)
+
+flide_status launched(flide_ctx* ctx, int rc, const char* what) {
+  if (rc != 0) return fail(ctx, FLIDE_E_HIP, std::string(what) + ": " + hipGetErrorString(hipError_t(rc)));
+  return FLIDE_OK;
+}
+
+flide_status staging_init(flide_ctx* ctx, Staging& st, int64_t words) {
+  if (st.words >= words) return FLIDE_OK;
+  for (int i = 0; i < 2; ++i) {
+    if (st.done[i]) {
+      FLIDE_HIP(ctx, hipEventSynchronize(st.done[i]));
+    }
+    if (st.host[i]) {
+      FLIDE_HIP(ctx, hipHostFree(st.host[i]));
+      st.host[i] = nullptr;
+    }
+    FLIDE_HIP(ctx, hipHostMalloc((void**)&st.host[i], size_t(words) * sizeof(int32_t), hipHostMallocDefault));
+    if (!st.done[i]) {
+      FLIDE_HIP(ctx, hipEventCreateWithFlags(&st.done[i], hipEventDisableTiming));
+    }
+  }
+  st.words = words;
+  return FLIDE_OK;
+}
+
+void staging_free(Staging& st) {
+  for (int i = 0; i < 2; ++i) {
+    if (st.done[i]) {
+      (void)hipEventSynchronize(st.done[i]);
+      (void)hipEventDestroy(st.done[i]);
+    }
+    if (st.host[i]) (void)hipHostFree(st.host[i]);
+    st.host[i] = nullptr;
+    st.done[i] = nullptr;
+  }
+  st.words = 0;
+}
+
+// Copy `words` of `image` into the next pinned buffer (waiting until its
+// previous copy has left it) and enqueue the H2D copy into `dst`.
+flide_status staging_upload(flide_ctx* ctx, Staging& st, const int32_t* image, int64_t words, int32_t* dst,
+                            hipStream_t stream) {
+  FLIDE_TRY(staging_init(ctx, st, words));
+  const int k = st.next;
+  FLIDE_HIP(ctx, hipEventSynchronize(st.done[k]));
+  std::memcpy(st.host[k], image, size_t(words) * sizeof(int32_t));
+  FLIDE_HIP(ctx, hipMemcpyAsync(dst, st.host[k], size_t(words) * sizeof(int32_t), hipMemcpyHostToDevice, stream));
+  FLIDE_HIP(ctx, hipEventRecord(st.done[k], stream));
+  st.next = k ^ 1;
+  return FLIDE_OK;
+}
+
+flide_status check_image(flide_ctx* ctx, const flide_caps& caps, const flide_meta_layout& L, const int32_t* img) {
+  const int32_t* hdr = img + L.hdr;
+  if (hdr[H_MAGIC] != kMagic) return fail(ctx, FLIDE_E_INVALID_ARG, "metadata image was not written by flide_plan_round");
+  if (hdr[H_T] < 0 || hdr[H_T] > caps.T_cap || hdr[H_R] < 0 || hdr[H_R] > caps.R_cap || hdr[H_NQST] < 0 ||
+      hdr[H_NQST] > caps.Q_cap || hdr[H_NSEG] != hdr[H_R] + hdr[H_NQST] || hdr[H_NTILES] < 0 ||
+      hdr[H_NTILES] > L.tile_cap)
+    return fail(ctx, FLIDE_E_CAPACITY, "metadata image does not fit the capacity");
+  return FLIDE_OK;
+}
+
+// Rotary table [max_pos, d/2, 2] of (cos, sin) for angle t * theta^(-2i/d),
+// evaluated in fp64 on the host and stored as fp32.
+flide_status ensure_rope(flide_ctx* ctx, double theta, int d, int max_pos, RopeArgs* out) {
+  for (auto& t : ctx->ropes) {
+    if (t.theta == theta && t.d == d && t.max_pos >= max_pos) {
+      out->table = t.dev;
+      out->max_pos = t.max_pos;
+      return FLIDE_OK;
+    }
+  }
+  const int half = d / 2;
+  std::vector<float> h(size_t(max_pos) * half * 2);
+  for (int i = 0; i < half; ++i) {
+    const double inv = std::pow(theta, -2.0 * double(i) / double(d));
+    for (int p = 0; p < max_pos; ++p) {
+      const double a = double(p) * inv;
+      h[(size_t(p) * half + i) * 2] = float(std::cos(a));
+      h[(size_t(p) * half + i) * 2 + 1] = float(std::sin(a));
+    }
+  }
+  float* dev = nullptr;
+  FLIDE_HIP(ctx, hipMalloc((void**)&dev, h.size() * sizeof(float)));
+  hipError_t e = hipMemcpy(dev, h.data(), h.size() * sizeof(float), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(dev);
+    return fail(ctx, FLIDE_E_HIP, std::string("hipMemcpy(rope table): ") + hipGetErrorString(e));
+  }
+  ctx->ropes.push_back({theta, d, max_pos, dev});
+  out->table = dev;
+  out->max_pos = max_pos;
+  return FLIDE_OK;
+}
+
+flide_status check_attn(flide_ctx* ctx, const flide_attn_params* p) {
+  if (!p) return fail(ctx, FLIDE_E_INVALID_ARG, "attention params are NULL");
+  if (p->Hq < 1 || p->Hkv < 1 || p->Hq % p->Hkv != 0)
+    return fail(ctx, FLIDE_E_INVALID_ARG, "need Hq, Hkv >= 1 and Hq % Hkv == 0");
+  if (p->d < 8 || p->d > 256 || p->d % 8 != 0) return fail(ctx, FLIDE_E_UNSUPPORTED, "head size must be a multiple of 8 in [8, 256]");
+  if (p->window < 0) return fail(ctx, FLIDE_E_INVALID_ARG, "window must be >= 0");
+  if (p->max_pos < 1 || !(p->theta > 0.0)) return fail(ctx, FLIDE_E_INVALID_ARG, "need max_pos >= 1 and theta > 0");
+  if (p->dtype != FLIDE_F32 && p->dtype != FLIDE_BF16) return fail(ctx, FLIDE_E_UNSUPPORTED, "dtype must be f32 or bf16");
+  if (p->cache_rows < 0 || p->cache_slots < 0) return fail(ctx, FLIDE_E_INVALID_ARG, "cache shape must be >= 0");
+  int64_t table_bytes = int64_t(p->max_pos) * p->d * 4;
+  if (table_bytes > (int64_t(1) << 32)) return fail(ctx, FLIDE_E_UNSUPPORTED, "rotary table above 4 GiB");
+  return FLIDE_OK;
+}
+
+flide_status check_gdn(flide_ctx* ctx, const flide_gdn_params* p, int32_t n_slots) {
+  if (!p) return fail(ctx, FLIDE_E_INVALID_ARG, "GDN params are NULL");
+  auto ok_dim = [](int v) { return v == 16 || v == 32 || v == 64 || v == 128; };
+  if (p->H < 1 || !ok_dim(p->dk) || !ok_dim(p->dv))
+    return fail(ctx, FLIDE_E_UNSUPPORTED, "GDN needs H >= 1 and dk, dv in {16, 32, 64, 128}");
+  if (p->conv_k < 1 || p->conv_k > 4) return fail(ctx, FLIDE_E_UNSUPPORTED, "conv width must be 1..4");
+  if (p->act != 0 && p->act != 1) return fail(ctx, FLIDE_E_INVALID_ARG, "act must be 0 (none) or 1 (SiLU)");
+  if (p->dtype != FLIDE_F32 && p->dtype != FLIDE_BF16) return fail(ctx, FLIDE_E_UNSUPPORTED, "dtype must be f32 or bf16");
+  if (p->chunk != 0 && p->chunk != 64) return fail(ctx, FLIDE_E_UNSUPPORTED, "chunk must be 64 (or 0 for the default)");
+  if (n_slots < 1) return fail(ctx, FLIDE_E_INVALID_ARG, "need at least one pool slot");
+  return FLIDE_OK;
+}
+
+flide_status check_readout(flide_ctx* ctx, const flide_readout_params* p) {
+  if (!p) return fail(ctx, FLIDE_E_INVALID_ARG, "readout params are NULL");
+  if (p->hidden < 8 || p->hidden % 8 != 0 || p->hidden > 8192)
+    return fail(ctx, FLIDE_E_UNSUPPORTED, "hidden must be a multiple of 8 in [8, 8192]");
+  if (p->dtype != FLIDE_F32 && p->dtype != FLIDE_BF16) return fail(ctx, FLIDE_E_UNSUPPORTED, "dtype must be f32 or bf16");
+  return FLIDE_OK;
+}
+
+flide_status view_of(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta, MetaView* mv,
+                     flide_meta_layout* Lout = nullptr) {
+  if (!caps || !dev_meta) return fail(ctx, FLIDE_E_INVALID_ARG, "caps or dev_meta is NULL");
+  flide_meta_layout L;
+  if (compute_layout(*caps, L) != FLIDE_OK) return fail(ctx, FLIDE_E_INVALID_ARG, "invalid capacity");
+  *mv = make_view(const_cast<int32_t*>(dev_meta), L, *caps);
+  if (Lout) *Lout = L;
+  return FLIDE_OK;
+}
+
+flide_status enqueue_attn(flide_ctx* ctx, const MetaView& mv, const flide_attn_params& p, const void* q,
+                          const void* k, const void* v, const void* kc, const void* vc, void* o, void* ws,
+                          hipStream_t stream) {
+  if (!q || !k || !v || !o || !ws) return fail(ctx, FLIDE_E_INVALID_ARG, "attention buffer is NULL");
+  if (p.cache_rows > 0 && (!kc || !vc || p.cache_slots < 1))
+    return fail(ctx, FLIDE_E_INVALID_ARG, "K/V cache shape given without cache buffers");
+  RopeArgs rope;
+  FLIDE_TRY(ensure_rope(ctx, p.theta, p.d, p.max_pos, &rope));
+  FLIDE_TRY(launched(ctx, launch_rope_k(mv, p, rope, k, ws, stream), "rope_k"));
+  FLIDE_TRY(launched(ctx, launch_attn(mv, p, rope, q, ws, v, p.cache_rows > 0 ? kc : nullptr,
+                                      p.cache_rows > 0 ? vc : nullptr, o, stream),
+                     "fork_attn"));
+  return FLIDE_OK;
+}
+
+flide_status enqueue_gdn(flide_ctx* ctx, const MetaView& mv, const flide_gdn_params& p, int phase, const void* x,
+                         const float* conv_w, const float* alpha, const float* eta, float* state_pool,
+                         void* conv_pool, int32_t n_slots, void* o, hipStream_t stream) {
+  if (!x || !conv_w || !alpha || !eta || !state_pool || !o || (p.conv_k > 1 && !conv_pool))
+    return fail(ctx, FLIDE_E_INVALID_ARG, "GDN buffer is NULL");
+  if (phase != 0 && phase != 1) return fail(ctx, FLIDE_E_INVALID_ARG, "phase must be 0 (trunks) or 1 (questions)");
+  return launched(ctx, launch_gdn(mv, p, phase, x, conv_w, alpha, eta, state_pool, conv_pool, n_slots, o, stream),
+                  "fork_gdn");
+}
+
+flide_status enqueue_round(flide_ctx* ctx, const flide_round_bufs* b, hipStream_t stream) {
+  MetaView mv;
+  FLIDE_TRY(view_of(ctx, &b->caps, b->dev_meta, &mv));
+  FLIDE_TRY(launched(ctx, launch_meta_expand(mv, stream), "meta_expand"));
+  FLIDE_TRY(enqueue_gdn(ctx, mv, b->gdn, 0, b->x, b->conv_w, b->alpha, b->eta, b->state_pool, b->conv_pool,
+                        b->n_slots, b->o_gdn, stream));
+  FLIDE_TRY(enqueue_gdn(ctx, mv, b->gdn, 1, b->x, b->conv_w, b->alpha, b->eta, b->state_pool, b->conv_pool,
+                        b->n_slots, b->o_gdn, stream));
+  for (int l = 0; l < b->n_attn; ++l)
+    FLIDE_TRY(enqueue_attn(ctx, mv, b->attn[l], b->q[l], b->k[l], b->v[l], b->k_cache[l], b->v_cache[l],
+                           b->o_attn[l], b->attn_ws[l], stream));
+  if (!b->h || !b->w_opt || !b->opt_off || !b->opt_id || !b->probs)
+    return fail(ctx, FLIDE_E_INVALID_ARG, "readout buffer is NULL");
+  FLIDE_TRY(launched(ctx, launch_readout(mv, b->ro, b->h, b->w_opt, b->opt_off, b->opt_id, b->n_opt_rows,
+                                         b->probs, stream),
+                     "readout"));
+  return FLIDE_OK;
+}
+
+flide_status check_round_bufs(flide_ctx* ctx, const flide_round_bufs* b) {
+  if (!b) return fail(ctx, FLIDE_E_INVALID_ARG, "round buffers are NULL");
+  flide_meta_layout L;
+  if (compute_layout(b->caps, L) != FLIDE_OK) return fail(ctx, FLIDE_E_INVALID_ARG, "invalid capacity");
+  if (!b->dev_meta) return fail(ctx, FLIDE_E_INVALID_ARG, "dev_meta is NULL");
+  if (b->n_attn < 0 || b->n_attn > 2) return fail(ctx, FLIDE_E_INVALID_ARG, "n_attn must be 0, 1 or 2");
+  for (int l = 0; l < b->n_attn; ++l) FLIDE_TRY(check_attn(ctx, &b->attn[l]));
+  FLIDE_TRY(check_gdn(ctx, &b->gdn, b->n_slots));
+  FLIDE_TRY(check_readout(ctx, &b->ro));
+  return FLIDE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+flide_status flide_create(flide_ctx** out, int32_t device) {
+  if (!out) return FLIDE_E_INVALID_ARG;
+  *out = nullptr;
+  try {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return FLIDE_E_HIP;
+    if (hipSetDevice(device) != hipSuccess) return FLIDE_E_HIP;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return FLIDE_E_HIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return FLIDE_E_UNSUPPORTED;
+    flide_ctx* ctx = new flide_ctx();
+    ctx->device = device;
+    if (hipStreamCreateWithFlags(&ctx->capture_stream, hipStreamNonBlocking) != hipSuccess) {
+      delete ctx;
+      return FLIDE_E_HIP;
+    }
+    *out = ctx;
+    return FLIDE_OK;
+  } catch (...) {
+    return FLIDE_E_INTERNAL;
+  }
+}
+
+void flide_destroy(flide_ctx* ctx) {
+  if (!ctx) return;
+  (void)hipSetDevice(ctx->device);
+  (void)hipDeviceSynchronize();
+  for (Bucket* b : ctx->buckets) {
+    if (b->exec) (void)hipGraphExecDestroy(b->exec);
+    if (b->graph) (void)hipGraphDestroy(b->graph);
+    staging_free(b->st);
+    delete b;
+  }
+  staging_free(ctx->direct);
+  for (auto& t : ctx->ropes) (void)hipFree(t.dev);
+  if (ctx->capture_stream) (void)hipStreamDestroy(ctx->capture_stream);
+  delete ctx;
+}
+
+const char* flide_last_error(const flide_ctx* ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+flide_status flide_meta_upload(flide_ctx* ctx, const flide_caps* caps, const int32_t* image, int32_t* dev_meta,
+                               void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    if (!image) return fail(ctx, FLIDE_E_INVALID_ARG, "image is NULL");
+    MetaView mv;
+    flide_meta_layout L;
+    FLIDE_TRY(view_of(ctx, caps, dev_meta, &mv, &L));
+    FLIDE_TRY(check_image(ctx, *caps, L, image));
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    FLIDE_TRY(staging_upload(ctx, ctx->direct, image, L.host_words, dev_meta, (hipStream_t)stream));
+    return launched(ctx, launch_meta_expand(mv, stream), "meta_expand");
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_meta_upload");
+  }
+}
+
+flide_status flide_attn_workspace_bytes(const flide_caps* caps, const flide_attn_params* p, int64_t* bytes) {
+  if (!caps || !p || !bytes) return FLIDE_E_INVALID_ARG;
+  if (caps->T_cap < 1 || p->Hkv < 1 || p->d < 1) return FLIDE_E_INVALID_ARG;
+  const int64_t elem = p->dtype == FLIDE_BF16 ? 2 : 4;
+  *bytes = int64_t(caps->T_cap) * p->Hkv * p->d * elem;
+  return FLIDE_OK;
+}
+
+flide_status flide_fork_attn(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
+                             const flide_attn_params* p, const void* q, const void* k, const void* v,
+                             const void* k_cache, const void* v_cache, void* o, void* workspace, void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    FLIDE_TRY(check_attn(ctx, p));
+    MetaView mv;
+    FLIDE_TRY(view_of(ctx, caps, dev_meta, &mv));
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    return enqueue_attn(ctx, mv, *p, q, k, v, k_cache, v_cache, o, workspace, (hipStream_t)stream);
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_fork_attn");
+  }
+}
+
+flide_status flide_fork_gdn(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
+                            const flide_gdn_params* p, int32_t phase, const void* x, const float* conv_w,
+                            const float* alpha, const float* eta, float* state_pool, void* conv_pool,
+                            int32_t n_slots, void* o, void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    FLIDE_TRY(check_gdn(ctx, p, n_slots));
+    MetaView mv;
+    FLIDE_TRY(view_of(ctx, caps, dev_meta, &mv));
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    return enqueue_gdn(ctx, mv, *p, phase, x, conv_w, alpha, eta, state_pool, conv_pool, n_slots, o,
+                       (hipStream_t)stream);
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_fork_gdn");
+  }
+}
+
+flide_status flide_readout(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
+                           const flide_readout_params* p, const void* h, const void* w_opt,
+                           const int32_t* opt_off, const int32_t* opt_id, int32_t n_opt_rows, float* probs,
+                           void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    FLIDE_TRY(check_readout(ctx, p));
+    if (!h || !w_opt || !opt_off || !opt_id || !probs) return fail(ctx, FLIDE_E_INVALID_ARG, "readout buffer is NULL");
+    MetaView mv;
+    FLIDE_TRY(view_of(ctx, caps, dev_meta, &mv));
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    return launched(ctx, launch_readout(mv, *p, h, w_opt, opt_off, opt_id, n_opt_rows, probs, stream), "readout");
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_readout");
+  }
+}
+
+flide_status flide_graph_capture(flide_ctx* ctx, const flide_round_bufs* bufs, void* stream, int32_t* bucket_id) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  (void)stream;
+  try {
+    if (!bucket_id) return fail(ctx, FLIDE_E_INVALID_ARG, "bucket_id is NULL");
+    FLIDE_TRY(check_round_bufs(ctx, bufs));
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    // rotary tables are built before capture (their upload is not a graph node)
+    for (int l = 0; l < bufs->n_attn; ++l) {
+      RopeArgs r;
+      FLIDE_TRY(ensure_rope(ctx, bufs->attn[l].theta, bufs->attn[l].d, bufs->attn[l].max_pos, &r));
+    }
+    Bucket* b = new Bucket();
+    b->bufs = *bufs;
+    compute_layout(bufs->caps, b->L);
+    hipStream_t cs = ctx->capture_stream;
+    hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) {
+      delete b;
+      return fail(ctx, FLIDE_E_HIP, std::string("hipStreamBeginCapture: ") + hipGetErrorString(e));
+    }
+    flide_status st = enqueue_round(ctx, bufs, cs);
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(cs, &g);
+    if (st != FLIDE_OK || e != hipSuccess) {
+      if (g) (void)hipGraphDestroy(g);
+      delete b;
+      if (st != FLIDE_OK) return st;
+      return fail(ctx, FLIDE_E_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+    }
+    b->graph = g;
+    e = hipGraphInstantiate(&b->exec, g, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+      (void)hipGraphDestroy(g);
+      delete b;
+      return fail(ctx, FLIDE_E_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+    }
+    st = staging_init(ctx, b->st, b->L.host_words);
+    if (st != FLIDE_OK) {
+      (void)hipGraphExecDestroy(b->exec);
+      (void)hipGraphDestroy(g);
+      delete b;
+      return st;
+    }
+    ctx->buckets.push_back(b);
+    *bucket_id = int32_t(ctx->buckets.size() - 1);
+    return FLIDE_OK;
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_graph_capture");
+  }
+}
+
+flide_status flide_select_bucket(const flide_ctx* ctx, int32_t T, int32_t R, int32_t n_q, int32_t* bucket_id) {
+  if (!ctx || !bucket_id) return FLIDE_E_INVALID_ARG;
+  int best = -1;
+  for (size_t i = 0; i < ctx->buckets.size(); ++i) {
+    const flide_caps& c = ctx->buckets[i]->bufs.caps;
+    if (c.T_cap >= T && c.R_cap >= R && c.Q_cap >= n_q) {
+      if (best < 0 || c.T_cap < ctx->buckets[size_t(best)]->bufs.caps.T_cap) best = int(i);
+    }
+  }
+  if (best < 0) return FLIDE_E_CAPACITY;
+  *bucket_id = best;
+  return FLIDE_OK;
+}
+
+flide_status flide_graph_replay(flide_ctx* ctx, int32_t bucket_id, const int32_t* image, void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    if (bucket_id < 0 || size_t(bucket_id) >= ctx->buckets.size())
+      return fail(ctx, FLIDE_E_INVALID_ARG, "no such bucket");
+    if (!image) return fail(ctx, FLIDE_E_INVALID_ARG, "image is NULL");
+    Bucket* b = ctx->buckets[size_t(bucket_id)];
+    FLIDE_TRY(check_image(ctx, b->bufs.caps, b->L, image));
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    FLIDE_TRY(staging_upload(ctx, b->st, image, b->L.host_words, b->bufs.dev_meta, (hipStream_t)stream));
+    FLIDE_HIP(ctx, hipGraphLaunch(b->exec, (hipStream_t)stream));
+    return FLIDE_OK;
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_graph_replay");
+  }
+}
+
+flide_status flide_round_eager(flide_ctx* ctx, const flide_round_bufs* bufs, const int32_t* image, void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    FLIDE_TRY(check_round_bufs(ctx, bufs));
+    if (!image) return fail(ctx, FLIDE_E_INVALID_ARG, "image is NULL");
+    flide_meta_layout L;
+    compute_layout(bufs->caps, L);
+    FLIDE_TRY(check_image(ctx, bufs->caps, L, image));
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    FLIDE_TRY(staging_upload(ctx, ctx->direct, image, L.host_words, bufs->dev_meta, (hipStream_t)stream));
+    return enqueue_round(ctx, bufs, (hipStream_t)stream);
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_round_eager");
+  }
+}
+
+flide_status flide_check_device(flide_ctx* ctx, const flide_caps* caps, int32_t* dev_meta, void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    MetaView mv;
+    FLIDE_TRY(view_of(ctx, caps, dev_meta, &mv));
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    FLIDE_HIP(ctx, hipStreamSynchronize((hipStream_t)stream));
+    int32_t err[4] = {0, 0, 0, 0};
+    FLIDE_HIP(ctx, hipMemcpy(err, mv.dev_error, sizeof(err), hipMemcpyDeviceToHost));
+    if (err[0] == 0) return FLIDE_OK;
+    FLIDE_HIP(ctx, hipMemset(mv.dev_error, 0, sizeof(err)));
+    char msg[160];
+    std::snprintf(msg, sizeof(msg),
+                  "device metadata check failed (bits 0x%x: 1 header, 2 position, 4 slot, 8 option, 16 cache, "
+                  "32 segment)",
+                  unsigned(err[0]));
+    return fail(ctx, FLIDE_E_DEVICE, msg);
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_check_device");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// Internal declarations shared by the host planner, the C ABI and the kernels.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/flide.h"
+
+namespace flide {
+
+// Query rows per attention work tile (rows of one segment; tiles never straddle segments).
+constexpr int kTileRows = 32;
+// Words of the metadata header.
+constexpr int kHdrWords = 64;
+constexpr int32_t kMagic = 0x464C4944;  // 'FLID'
+
+// Header fields.
+enum : int {
+  H_T = 0,
+  H_R = 1,
+  H_NSEG = 2,
+  H_NQST = 3,
+  H_NTILES = 4,
+  H_MAXPOS = 5,
+  H_MAGIC = 15,
+};
+
+// Device error bits.
+enum : int32_t {
+  E_HEADER = 1,     // header inconsistent with the capacity
+  E_POSITION = 2,   // a position outside the rotary table
+  E_SLOT = 4,       // a state slot outside the pool
+  E_OPTION = 8,     // an option row outside w_opt
+  E_CACHE = 16,     // a resume position beyond the K/V cache rows
+  E_SEGMENT = 32,   // a segment/tile entry outside the stream
+};
+
+inline int64_t align_words(int64_t x) { return (x + 63) & ~int64_t(63); }
+
+// Offsets of a metadata image (see flide_meta_layout in flide.h).
+flide_status compute_layout(const flide_caps& caps, flide_meta_layout& L);
+
+// Device pointers into one metadata image, passed by value to kernels.
+struct MetaView {
+  const int32_t* hdr;
+  const int32_t* seg_row0;
+  const int32_t* seg_len;
+  const int32_t* seg_req;
+  const int32_t* seg_branch;
+  const int32_t* seg_pos0;
+  const int32_t* seg_state;
+  const int32_t* req_trunk_row0;
+  const int32_t* req_P;
+  const int32_t* req_m;
+  const int32_t* req_ckpt;
+  const int32_t* req_out;
+  const int32_t* req_q_seg0;
+  const int32_t* req_nq;
+  const int32_t* qfin_row;
+  const int32_t* tile_seg;
+  const int32_t* tile_row0;
+  int32_t* tok_j;
+  int32_t* tok_c;
+  int32_t* tok_t;
+  int32_t* dev_error;
+  int32_t T_cap, R_cap, Q_cap, seg_cap, tile_cap;
+};
+
+inline MetaView make_view(int32_t* base, const flide_meta_layout& L, const flide_caps& c) {
+  MetaView v;
+  v.hdr = base + L.hdr;
+  v.seg_row0 = base + L.seg_row0;
+  v.seg_len = base + L.seg_len;
+  v.seg_req = base + L.seg_req;
+  v.seg_branch = base + L.seg_branch;
+  v.seg_pos0 = base + L.seg_pos0;
+  v.seg_state = base + L.seg_state;
+  v.req_trunk_row0 = base + L.req_trunk_row0;
+  v.req_P = base + L.req_P;
+  v.req_m = base + L.req_m;
+  v.req_ckpt = base + L.req_ckpt;
+  v.req_out = base + L.req_out;
+  v.req_q_seg0 = base + L.req_q_seg0;
+  v.req_nq = base + L.req_nq;
+  v.qfin_row = base + L.qfin_row;
+  v.tile_seg = base + L.tile_seg;
+  v.tile_row0 = base + L.tile_row0;
+  v.tok_j = base + L.tok_j;
+  v.tok_c = base + L.tok_c;
+  v.tok_t = base + L.tok_t;
+  v.dev_error = base + L.dev_error;
+  v.T_cap = c.T_cap;
+  v.R_cap = c.R_cap;
+  v.Q_cap = c.Q_cap;
+  v.seg_cap = L.seg_cap;
+  v.tile_cap = L.tile_cap;
+  return v;
+}
+
+// ---- kernel launchers (defined in the .hip files); all return a hipError_t as int ----
+int launch_meta_expand(const MetaView& mv, void* stream);
+int launch_clear_error(const MetaView& mv, void* stream);
+
+struct RopeArgs {
+  const float* table;  // [max_pos, d/2, 2]: (cos, sin) of every position and pair
+  int32_t max_pos;
+};
+
+int launch_rope_k(const MetaView& mv, const flide_attn_params& p, const RopeArgs& rope, const void* k,
+                  void* k_rot, void* stream);
+int launch_attn(const MetaView& mv, const flide_attn_params& p, const RopeArgs& rope, const void* q,
+                const void* k_rot, const void* v, const void* k_cache, const void* v_cache, void* o,
+                void* stream);
+int launch_gdn(const MetaView& mv, const flide_gdn_params& p, int phase, const void* x, const float* conv_w,
+               const float* alpha, const float* eta, float* state_pool, void* conv_pool, int32_t n_slots,
+               void* o, void* stream);
+int launch_readout(const MetaView& mv, const flide_readout_params& p, const void* h, const void* w_opt,
+                   const int32_t* opt_off, const int32_t* opt_id, int32_t n_opt_rows, float* probs,
+                   void* stream);
+
+}  // namespace flide

@@ -1,0 +1,116 @@
+// Metadata expansion and key rotation.
+//
+// meta_expand turns the uploaded segment table into per-row (j, c, t) labels
+// ("Flide: Accelerating Decision Inference with Exact State Forking"
+// §方法步骤详情: every token carries request, branch and position; question
+// positions continue from P) and marks tail rows (-1, -1, -1) (Korean summary
+// §어떻게 쓰나: padding only at the tail).
+//
+// rope_k rotates every key row once to its metadata position (rotate-half
+// pairs (i, i + d/2), angle t * theta^(-2i/d), host fp64 table stored fp32), so
+// the attention kernel's inner loop reads rotated keys directly.
+#include "device_common.hpp"
+
+namespace flide {
+
+__global__ void __launch_bounds__(256) meta_expand_kernel(MetaView mv) {
+  const int T = mv.hdr[H_T];
+  const int n_seg = mv.hdr[H_NSEG];
+  const bool bad = mv.hdr[H_MAGIC] != kMagic || T < 0 || T > mv.T_cap || n_seg < 0 || n_seg > mv.seg_cap ||
+                   mv.hdr[H_R] < 0 || mv.hdr[H_R] > mv.R_cap || mv.hdr[H_NQST] < 0 ||
+                   mv.hdr[H_NQST] > mv.Q_cap || mv.hdr[H_NTILES] < 0 || mv.hdr[H_NTILES] > mv.tile_cap;
+  const int stride = gridDim.x * blockDim.x;
+  if (bad) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) flag_error(mv.dev_error, E_HEADER);
+    for (int row = blockIdx.x * blockDim.x + threadIdx.x; row < mv.T_cap; row += stride) {
+      mv.tok_j[row] = -1;
+      mv.tok_c[row] = -1;
+      mv.tok_t[row] = -1;
+    }
+    return;
+  }
+  for (int row = blockIdx.x * blockDim.x + threadIdx.x; row < mv.T_cap; row += stride) {
+    int j = -1, c = -1, t = -1;
+    if (row < T && n_seg > 0) {
+      int s = find_segment(mv.seg_row0, n_seg, row);
+      int off = row - mv.seg_row0[s];
+      if (off >= 0 && off < mv.seg_len[s]) {
+        j = mv.seg_req[s];
+        c = mv.seg_branch[s];
+        t = mv.seg_pos0[s] + off;
+      } else if (threadIdx.x == 0) {
+        flag_error(mv.dev_error, E_SEGMENT);
+      }
+    }
+    mv.tok_j[row] = j;
+    mv.tok_c[row] = c;
+    mv.tok_t[row] = t;
+  }
+}
+
+__global__ void clear_error_kernel(int32_t* dev_error) {
+  if (threadIdx.x < 4) dev_error[threadIdx.x] = 0;
+}
+
+int launch_meta_expand(const MetaView& mv, void* stream) {
+  int blocks = (mv.T_cap + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(meta_expand_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, mv);
+  return int(hipGetLastError());
+}
+
+int launch_clear_error(const MetaView& mv, void* stream) {
+  hipLaunchKernelGGL(clear_error_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, mv.dev_error);
+  return int(hipGetLastError());
+}
+
+// One thread rotates 4 consecutive pairs of one (row, kv head).
+template <typename T>
+__global__ void __launch_bounds__(256) rope_k_kernel(MetaView mv, const T* __restrict__ k, T* __restrict__ k_rot,
+                                                     const float* __restrict__ table, int max_pos, int Hkv,
+                                                     int d) {
+  const int T_rows = mv.hdr[H_T];
+  const int half = d >> 1;
+  const int groups = half >> 2;  // 4 pairs per thread
+  const int64_t per_row = int64_t(Hkv) * groups;
+  const int64_t total = int64_t(T_rows) * per_row;
+  for (int64_t w = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; w < total;
+       w += int64_t(gridDim.x) * blockDim.x) {
+    const int row = int(w / per_row);
+    const int rem = int(w - int64_t(row) * per_row);
+    const int h = rem / groups;
+    const int i0 = (rem - h * groups) * 4;
+    const int pos = mv.tok_t[row];
+    const int64_t base = (int64_t(row) * Hkv + h) * d;
+    if (pos < 0 || pos >= max_pos) {
+      if (pos >= max_pos) flag_error(mv.dev_error, E_POSITION);
+      continue;
+    }
+    const float* cs = table + (int64_t(pos) * half + i0) * 2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float c = cs[2 * e], s = cs[2 * e + 1];
+      float x1 = load_f32(k, base + i0 + e);
+      float x2 = load_f32(k, base + i0 + e + half);
+      store_f32(k_rot, base + i0 + e, x1 * c - x2 * s);
+      store_f32(k_rot, base + i0 + e + half, x2 * c + x1 * s);
+    }
+  }
+}
+
+int launch_rope_k(const MetaView& mv, const flide_attn_params& p, const RopeArgs& rope, const void* k,
+                  void* k_rot, void* stream) {
+  int64_t work = int64_t(mv.T_cap) * p.Hkv * (p.d / 8);
+  int blocks = int((work + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  if (p.dtype == FLIDE_BF16)
+    hipLaunchKernelGGL(rope_k_kernel<bf16_t>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, mv,
+                       (const bf16_t*)k, (bf16_t*)k_rot, rope.table, rope.max_pos, p.Hkv, p.d);
+  else
+    hipLaunchKernelGGL(rope_k_kernel<float>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, mv,
+                       (const float*)k, (float*)k_rot, rope.table, rope.max_pos, p.Hkv, p.d);
+  return int(hipGetLastError());
+}
+
+}  // namespace flide

@@ -1,0 +1,274 @@
+// Host planner: flat-stream metadata of a round, the attention work list and the
+// request-boundary split.  Pure host code (runs without a GPU).
+//
+// Stream order and per-row labels follow "Flide: Accelerating Decision Inference
+// with Exact State Forking" §方法步骤详情 (trunks first in request order, then the
+// question segments grouped by request; every row labelled (j, c, t), question
+// positions continuing from P).  Splitting at request boundaries, tail-only
+// padding and the eager path follow the Korean summary §어떻게 쓰나.
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "flide_internal.hpp"
+
+namespace flide {
+
+flide_status compute_layout(const flide_caps& c, flide_meta_layout& L) {
+  if (c.T_cap < 1 || c.R_cap < 1 || c.Q_cap < 0) return FLIDE_E_INVALID_ARG;
+  if (c.T_cap > (1 << 28) || c.R_cap > (1 << 24) || c.Q_cap > (1 << 24)) return FLIDE_E_INVALID_ARG;
+  std::memset(&L, 0, sizeof(L));
+  L.seg_cap = c.R_cap + c.Q_cap;
+  L.tile_rows = kTileRows;
+  L.tile_cap = (c.T_cap + kTileRows - 1) / kTileRows + L.seg_cap;
+  int64_t o = 0;
+  auto take = [&](int64_t n) {
+    int64_t at = o;
+    o = align_words(o + n);
+    return at;
+  };
+  L.hdr = take(kHdrWords);
+  L.seg_row0 = take(L.seg_cap);
+  L.seg_len = take(L.seg_cap);
+  L.seg_req = take(L.seg_cap);
+  L.seg_branch = take(L.seg_cap);
+  L.seg_pos0 = take(L.seg_cap);
+  L.seg_state = take(L.seg_cap);
+  L.req_trunk_row0 = take(c.R_cap);
+  L.req_P = take(c.R_cap);
+  L.req_m = take(c.R_cap);
+  L.req_ckpt = take(c.R_cap);
+  L.req_out = take(c.R_cap);
+  L.req_q_seg0 = take(c.R_cap);
+  L.req_nq = take(c.R_cap);
+  L.qfin_row = take(c.Q_cap > 0 ? c.Q_cap : 1);
+  L.tile_seg = take(L.tile_cap);
+  L.tile_row0 = take(L.tile_cap);
+  L.host_words = o;
+  L.tok_j = take(c.T_cap);
+  L.tok_c = take(c.T_cap);
+  L.tok_t = take(c.T_cap);
+  L.dev_error = take(4);
+  L.dev_words = o;
+  return FLIDE_OK;
+}
+
+static flide_status check_requests(const flide_request* reqs, int32_t R, int64_t* T, int64_t* n_qst) {
+  if (R < 0 || (R > 0 && reqs == nullptr)) return FLIDE_E_INVALID_ARG;
+  int64_t rows = 0, nq = 0;
+  for (int32_t j = 0; j < R; ++j) {
+    const flide_request& r = reqs[j];
+    if (r.P < 0 || r.m < 0 || r.m > r.P || r.n_q < 0) return FLIDE_E_INVALID_ARG;
+    if (r.n_q > 0 && r.q_len == nullptr) return FLIDE_E_INVALID_ARG;
+    if (r.out_slot < 0) return FLIDE_E_INVALID_ARG;
+    if (r.m > 0 && (r.ckpt_slot < 0 || r.ckpt_slot == r.out_slot)) return FLIDE_E_INVALID_ARG;
+    rows += r.P - r.m;
+    for (int32_t i = 0; i < r.n_q; ++i) {
+      if (r.q_len[i] < 1) return FLIDE_E_INVALID_ARG;
+      rows += r.q_len[i];
+    }
+    nq += r.n_q;
+    if (rows > (int64_t(1) << 30)) return FLIDE_E_INVALID_ARG;
+  }
+  // Slots written by the trunk call must be distinct from each other and from
+  // every slot a resumed trunk reads, or two workgroups would race on a slot.
+  std::vector<int32_t> outs, ckpts;
+  for (int32_t j = 0; j < R; ++j) {
+    outs.push_back(reqs[j].out_slot);
+    if (reqs[j].m > 0) ckpts.push_back(reqs[j].ckpt_slot);
+  }
+  std::sort(outs.begin(), outs.end());
+  std::sort(ckpts.begin(), ckpts.end());
+  if (std::adjacent_find(outs.begin(), outs.end()) != outs.end()) return FLIDE_E_INVALID_ARG;
+  for (int32_t o : outs)
+    if (std::binary_search(ckpts.begin(), ckpts.end(), o)) return FLIDE_E_INVALID_ARG;
+  *T = rows;
+  *n_qst = nq;
+  return FLIDE_OK;
+}
+
+}  // namespace flide
+
+using namespace flide;
+
+extern "C" {
+
+const char* flide_status_string(int32_t s) {
+  switch (s) {
+    case FLIDE_OK: return "ok";
+    case FLIDE_E_INVALID_ARG: return "invalid argument";
+    case FLIDE_E_CAPACITY: return "capacity exceeded";
+    case FLIDE_E_UNSUPPORTED: return "unsupported shape or dtype";
+    case FLIDE_E_HIP: return "HIP runtime error";
+    case FLIDE_E_DEVICE: return "device-side metadata check failed";
+    case FLIDE_E_INTERNAL: return "internal error";
+    default: return "unknown status";
+  }
+}
+
+const char* flide_version(void) { return "flide-mi355x 0.1 (gfx950)"; }
+
+flide_status flide_meta_layout_for(const flide_caps* caps, flide_meta_layout* out) {
+  if (!caps || !out) return FLIDE_E_INVALID_ARG;
+  return compute_layout(*caps, *out);
+}
+
+flide_status flide_plan_sizes(const flide_request* reqs, int32_t R, int32_t* T, int32_t* n_seg, int32_t* n_qst) {
+  int64_t t = 0, nq = 0;
+  flide_status st = check_requests(reqs, R, &t, &nq);
+  if (st != FLIDE_OK) return st;
+  if (T) *T = int32_t(t);
+  if (n_seg) *n_seg = int32_t(R + nq);
+  if (n_qst) *n_qst = int32_t(nq);
+  return FLIDE_OK;
+}
+
+flide_status flide_plan_round(const flide_request* reqs, int32_t R, const flide_caps* caps, int32_t* image,
+                              int64_t image_words) {
+  try {
+    if (!caps || !image) return FLIDE_E_INVALID_ARG;
+    flide_meta_layout L;
+    flide_status st = compute_layout(*caps, L);
+    if (st != FLIDE_OK) return st;
+    if (image_words < L.host_words) return FLIDE_E_INVALID_ARG;
+    int64_t T = 0, nq = 0;
+    st = check_requests(reqs, R, &T, &nq);
+    if (st != FLIDE_OK) return st;
+    if (T > caps->T_cap || R > caps->R_cap || nq > caps->Q_cap) return FLIDE_E_CAPACITY;
+
+    std::vector<int32_t> img(size_t(L.host_words), 0);
+    int32_t* hdr = img.data() + L.hdr;
+    int32_t* s_row0 = img.data() + L.seg_row0;
+    int32_t* s_len = img.data() + L.seg_len;
+    int32_t* s_req = img.data() + L.seg_req;
+    int32_t* s_br = img.data() + L.seg_branch;
+    int32_t* s_pos = img.data() + L.seg_pos0;
+    int32_t* s_st = img.data() + L.seg_state;
+    int32_t* r_row0 = img.data() + L.req_trunk_row0;
+    int32_t* r_P = img.data() + L.req_P;
+    int32_t* r_m = img.data() + L.req_m;
+    int32_t* r_ck = img.data() + L.req_ckpt;
+    int32_t* r_out = img.data() + L.req_out;
+    int32_t* r_qs = img.data() + L.req_q_seg0;
+    int32_t* r_nq = img.data() + L.req_nq;
+    int32_t* qfin = img.data() + L.qfin_row;
+
+    int32_t row = 0, seg = 0, max_pos = 0;
+    // trunk segments: one per request, in request order (possibly empty)
+    for (int32_t j = 0; j < R; ++j) {
+      const flide_request& r = reqs[j];
+      r_row0[j] = row;
+      r_P[j] = r.P;
+      r_m[j] = r.m;
+      r_ck[j] = r.m > 0 ? r.ckpt_slot : -1;
+      r_out[j] = r.out_slot;
+      r_nq[j] = r.n_q;
+      s_row0[seg] = row;
+      s_len[seg] = r.P - r.m;
+      s_req[seg] = j;
+      s_br[seg] = 0;
+      s_pos[seg] = r.m;
+      s_st[seg] = r.m > 0 ? r.ckpt_slot : -1;
+      ++seg;
+      row += r.P - r.m;
+      max_pos = std::max(max_pos, r.P);
+    }
+    // question segments, grouped by request; positions continue from P
+    int32_t qi = 0;
+    for (int32_t j = 0; j < R; ++j) {
+      const flide_request& r = reqs[j];
+      r_qs[j] = seg;
+      for (int32_t i = 0; i < r.n_q; ++i) {
+        s_row0[seg] = row;
+        s_len[seg] = r.q_len[i];
+        s_req[seg] = j;
+        s_br[seg] = i + 1;
+        s_pos[seg] = r.P;
+        s_st[seg] = r.out_slot;
+        ++seg;
+        row += r.q_len[i];
+        qfin[qi++] = row - 1;
+        max_pos = std::max(max_pos, r.P + r.q_len[i]);
+      }
+    }
+    // Attention work list: tiles of kTileRows rows aligned to each segment's
+    // start, heaviest first (cost = keys seen by the tile's last row) so that a
+    // fixed grid finishes its long tiles early.  Tiles are independent, so the
+    // order does not change any output bit.
+    struct Tile {
+      int64_t cost;
+      int32_t seg, row0;
+    };
+    std::vector<Tile> tiles;
+    tiles.reserve(size_t(L.tile_cap));
+    for (int32_t s = 0; s < seg; ++s) {
+      const flide_request& r = reqs[s_req[s]];
+      for (int32_t a = 0; a < s_len[s]; a += kTileRows) {
+        int32_t last = std::min(a + kTileRows, s_len[s]);
+        int64_t cost = int64_t(r.m) + last + (s_br[s] > 0 ? int64_t(r.P - r.m) : 0);
+        tiles.push_back({cost, s, s_row0[s] + a});
+      }
+    }
+    if (int64_t(tiles.size()) > L.tile_cap) return FLIDE_E_INTERNAL;
+    std::stable_sort(tiles.begin(), tiles.end(), [](const Tile& x, const Tile& y) { return x.cost > y.cost; });
+    for (size_t i = 0; i < tiles.size(); ++i) {
+      img[size_t(L.tile_seg + int64_t(i))] = tiles[i].seg;
+      img[size_t(L.tile_row0 + int64_t(i))] = tiles[i].row0;
+    }
+    hdr[H_T] = row;
+    hdr[H_R] = R;
+    hdr[H_NSEG] = seg;
+    hdr[H_NQST] = qi;
+    hdr[H_NTILES] = int32_t(tiles.size());
+    hdr[H_MAXPOS] = max_pos;
+    hdr[H_MAGIC] = kMagic;
+    std::memcpy(image, img.data(), size_t(L.host_words) * sizeof(int32_t));
+    return FLIDE_OK;
+  } catch (...) {
+    return FLIDE_E_INTERNAL;
+  }
+}
+
+flide_status flide_split_round(const flide_request* reqs, int32_t R, int32_t T_max, int32_t* sub_first,
+                               int32_t* n_sub, uint8_t* eager) {
+  if (T_max < 1 || !sub_first || !n_sub || (R > 0 && !eager)) return FLIDE_E_INVALID_ARG;
+  int64_t T = 0, nq = 0;
+  flide_status st = check_requests(reqs, R, &T, &nq);
+  if (st != FLIDE_OK) return st;
+  int32_t n = 0;
+  sub_first[0] = 0;
+  int64_t cur_rows = 0;
+  int32_t cur_n = 0;
+  for (int32_t j = 0; j < R; ++j) {
+    const flide_request& r = reqs[j];
+    int64_t rows = r.P - r.m;
+    for (int32_t i = 0; i < r.n_q; ++i) rows += r.q_len[i];
+    if (rows > T_max) {
+      if (cur_n) {
+        eager[n] = 0;
+        sub_first[++n] = j;
+      }
+      eager[n] = 1;
+      sub_first[++n] = j + 1;
+      cur_rows = 0;
+      cur_n = 0;
+      continue;
+    }
+    if (cur_n && cur_rows + rows > T_max) {
+      eager[n] = 0;
+      sub_first[++n] = j;
+      cur_rows = 0;
+      cur_n = 0;
+    }
+    cur_rows += rows;
+    ++cur_n;
+  }
+  if (cur_n) {
+    eager[n] = 0;
+    sub_first[++n] = R;
+  }
+  *n_sub = n;
+  return FLIDE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,237 @@
+"""Device buffers of one round and the calls that run it — marshalling only.
+
+``RoundBuffers`` allocates every tensor of a round at a capacity with torch
+(device memory only), places request payloads at the stream rows a placement
+names (the caller's job in a serving loop: writing the round's rows into the
+capacity buffers before a replay), and hands raw pointers to the C ABI.  All
+computation happens in libflide.so's kernels.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import flide as F
+
+
+def _torch_dtype(dtype: str):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def _flide_dtype(dtype: str) -> int:
+    return F.FLIDE_BF16 if dtype == "bf16" else F.FLIDE_F32
+
+
+@dataclass
+class RoundSpec:
+    """Static shape of the buffers (independent of a particular round)."""
+    shapes: object          # workloads.LayerShapes
+    dtype: str              # "bf16" or "f32"
+    T_cap: int
+    R_cap: int
+    Q_cap: int
+    n_slots: int
+    opt_cap: int            # rows of w_opt / entries of probs
+    cache_rows: int = 0     # K/V cache rows per slot (0: no cache)
+    max_pos: int = 1 << 16
+
+
+class RoundBuffers:
+    def __init__(self, spec: RoundSpec, device: str = "cuda"):
+        self.spec = spec
+        s = spec.shapes
+        dt = _torch_dtype(spec.dtype)
+        self.device = device
+        self.caps = F.caps_of(spec.T_cap, spec.R_cap, spec.Q_cap)
+        self.layout = F.flide_meta_layout_for(self.caps)
+        T = spec.T_cap
+        z = lambda *shape, dtype=dt: torch.zeros(*shape, dtype=dtype, device=device)  # noqa: E731
+        self.dev_meta = z(self.layout.dev_words, dtype=torch.int32)
+        self.n_attn = 2 if s.swa_window > 0 else 1
+        self.q = [z(T, s.Hq, s.d) for _ in range(self.n_attn)]
+        self.k = [z(T, s.Hkv, s.d) for _ in range(self.n_attn)]
+        self.v = [z(T, s.Hkv, s.d) for _ in range(self.n_attn)]
+        self.o_attn = [z(T, s.Hq, s.d) for _ in range(self.n_attn)]
+        self.attn_params = []
+        self.k_cache, self.v_cache, self.ws = [], [], []
+        for layer in range(self.n_attn):
+            p = F.flide_attn_params(s.Hq, s.Hkv, s.d, 0 if layer == 0 else s.swa_window, float(s.theta),
+                                    int(spec.max_pos), int(spec.cache_rows),
+                                    int(spec.n_slots if spec.cache_rows > 0 else 0), _flide_dtype(spec.dtype), 0)
+            self.attn_params.append(p)
+            if spec.cache_rows > 0:
+                self.k_cache.append(z(spec.n_slots, spec.cache_rows, s.Hkv, s.d))
+                self.v_cache.append(z(spec.n_slots, spec.cache_rows, s.Hkv, s.d))
+            else:
+                self.k_cache.append(None)
+                self.v_cache.append(None)
+            nbytes = F.flide_attn_workspace_bytes(self.caps, p)
+            self.ws.append(torch.zeros(nbytes, dtype=torch.uint8, device=device))
+        C = s.channels
+        self.gdn_params = F.flide_gdn_params(s.H, s.dk, s.dv, s.conv_k, 0, 64, _flide_dtype(spec.dtype), 0)
+        self.x = z(T, C)
+        self.conv_w = z(C, s.conv_k, dtype=torch.float32)
+        self.alpha = z(T, s.H, dtype=torch.float32)
+        self.eta = z(T, s.H, dtype=torch.float32)
+        self.state_pool = z(spec.n_slots, s.H, s.dv, s.dk, dtype=torch.float32)
+        self.conv_pool = z(spec.n_slots, max(1, s.conv_k - 1), C)
+        self.o_gdn = z(T, s.H, s.dv)
+        self.ro_params = F.flide_readout_params(s.hidden, _flide_dtype(spec.dtype))
+        self.h = z(T, s.hidden)
+        self.w_opt = z(max(1, spec.opt_cap), s.hidden)
+        self.opt_off = z(spec.Q_cap + 1, dtype=torch.int32)
+        self.opt_id = z(max(1, spec.opt_cap), dtype=torch.int32)
+        self.probs = z(max(1, spec.opt_cap), dtype=torch.float32)
+        self.n_opt_rows = 0
+        self._struct = None
+
+    # ------------------------------------------------------------------ placement
+    def fill(self, rnd, placement: Dict[str, np.ndarray], conv_w: Optional[np.ndarray] = None,
+             clear: bool = True) -> None:
+        """Copy ``rnd``'s payloads to the stream rows named by ``placement``.
+
+        placement: ``req_trunk_row0`` [R], ``req_q_seg0`` [R] and ``seg_row0`` [n_seg]
+        (from the library's plan or an independent builder).
+        """
+        s, spec = rnd.shapes, self.spec
+        dt = _torch_dtype(spec.dtype)
+        T = int(sum((r.P - r.m) + sum(r.q_len) for r in rnd.requests))
+        if T > spec.T_cap:
+            raise ValueError("round does not fit the buffers")
+        names = ["attn_q", "attn_k", "attn_v"] + (["swa_q", "swa_k", "swa_v"] if self.n_attn == 2 else []) + \
+                ["gdn_x", "alpha", "eta", "hidden"]
+        host = {}
+        rows_idx = np.empty(T, np.int64)
+        at = 0
+        for j in range(len(rnd.requests)):
+            segs = rnd.segment_rows(j)
+            s0, n0 = segs[0]
+            r0 = int(placement["req_trunk_row0"][j])
+            rows_idx[at:at + n0] = np.arange(r0, r0 + n0)
+            at += n0
+            q0 = int(placement["req_q_seg0"][j])
+            for i, (_, L) in enumerate(segs[1:]):
+                rr = int(placement["seg_row0"][q0 + i])
+                rows_idx[at:at + L] = np.arange(rr, rr + L)
+                at += L
+        # concatenated request payloads, in request-local order
+        for name in names:
+            parts = [rnd.payload(j)[name] for j in range(len(rnd.requests))]
+            cat = np.concatenate(parts, axis=0) if parts else np.zeros((0,))
+            buf = np.zeros((T,) + cat.shape[1:], np.float32)
+            buf[rows_idx] = cat
+            host[name] = buf
+        tgt = {"attn_q": self.q[0], "attn_k": self.k[0], "attn_v": self.v[0], "gdn_x": self.x,
+               "alpha": self.alpha, "eta": self.eta, "hidden": self.h}
+        if self.n_attn == 2:
+            tgt.update({"swa_q": self.q[1], "swa_k": self.k[1], "swa_v": self.v[1]})
+        for name, t in tgt.items():
+            if clear:
+                t.zero_()
+            t[:T].copy_(torch.from_numpy(host[name]).to(t.dtype))
+        cw = rnd.conv_w() if conv_w is None else conv_w
+        self.conv_w.copy_(torch.from_numpy(np.ascontiguousarray(cw, np.float32)))
+        # options: question order of the stream = request order, then question order
+        blocks, off = [], [0]
+        for j, r in enumerate(rnd.requests):
+            w = rnd.payload(j)["w_opt"]
+            blocks.append(w)
+            for n in r.n_opt:
+                off.append(off[-1] + int(n))
+        n_opt = off[-1]
+        if n_opt > spec.opt_cap:
+            raise ValueError("too many options for the buffers")
+        if n_opt:
+            w_cat = np.concatenate(blocks, axis=0)
+            perm = rnd.option_permutation(n_opt)          # option k lives at row perm[k]
+            w_glob = np.zeros_like(w_cat)
+            w_glob[perm] = w_cat
+            self.w_opt[:n_opt].copy_(torch.from_numpy(w_glob).to(dt))
+            self.opt_id[:n_opt].copy_(torch.from_numpy(perm.astype(np.int32)))
+        self.opt_off[:len(off)].copy_(torch.from_numpy(np.asarray(off, np.int32)))
+        self.n_opt_rows = n_opt
+        self.n_opt = n_opt
+        # checkpoints
+        for j, r in enumerate(rnd.requests):
+            if r.m > 0:
+                pl = rnd.payload(j)
+                self.state_pool[r.ckpt_slot].copy_(torch.from_numpy(pl["ckpt_state"]))
+                self.conv_pool[r.ckpt_slot].copy_(torch.from_numpy(pl["ckpt_window"]).to(dt))
+                for layer, pre in enumerate(["kv", "swa_kv"][:self.n_attn]):
+                    if r.m > spec.cache_rows:
+                        raise ValueError("checkpoint longer than the K/V cache")
+                    self.k_cache[layer][r.ckpt_slot, :r.m].copy_(torch.from_numpy(pl[pre + "_k"]).to(dt))
+                    self.v_cache[layer][r.ckpt_slot, :r.m].copy_(torch.from_numpy(pl[pre + "_v"]).to(dt))
+        self.rows_idx = rows_idx
+        self._struct = None
+
+    # ------------------------------------------------------------------ C structure
+    def round_bufs(self) -> F.flide_round_bufs:
+        if self._struct is not None:
+            return self._struct
+        b = F.flide_round_bufs()
+        b.caps = self.caps
+        b.dev_meta = self.dev_meta.data_ptr()
+        b.n_attn = self.n_attn
+        for l in range(self.n_attn):
+            b.attn[l] = self.attn_params[l]
+            b.q[l] = self.q[l].data_ptr()
+            b.k[l] = self.k[l].data_ptr()
+            b.v[l] = self.v[l].data_ptr()
+            b.k_cache[l] = self.k_cache[l].data_ptr() if self.k_cache[l] is not None else None
+            b.v_cache[l] = self.v_cache[l].data_ptr() if self.v_cache[l] is not None else None
+            b.o_attn[l] = self.o_attn[l].data_ptr()
+            b.attn_ws[l] = self.ws[l].data_ptr()
+        b.gdn = self.gdn_params
+        b.x = self.x.data_ptr()
+        b.conv_w = self.conv_w.data_ptr()
+        b.alpha = self.alpha.data_ptr()
+        b.eta = self.eta.data_ptr()
+        b.state_pool = self.state_pool.data_ptr()
+        b.conv_pool = self.conv_pool.data_ptr()
+        b.n_slots = self.spec.n_slots
+        b.o_gdn = self.o_gdn.data_ptr()
+        b.ro = self.ro_params
+        b.h = self.h.data_ptr()
+        b.w_opt = self.w_opt.data_ptr()
+        b.opt_off = self.opt_off.data_ptr()
+        b.opt_id = self.opt_id.data_ptr()
+        b.n_opt_rows = max(1, self.spec.opt_cap)
+        b.probs = self.probs.data_ptr()
+        self._struct = b
+        return b
+
+    # ------------------------------------------------------------------ direct kernel calls
+    def upload(self, ctx: F.Context, image: np.ndarray, stream=None) -> None:
+        F.flide_meta_upload(ctx, self.caps, image, self.dev_meta, stream)
+
+    def run_layers(self, ctx: F.Context, stream=None) -> None:
+        """GDN call 0, GDN call 1, the attention layer(s) and the readout, one call each."""
+        s = self.spec.shapes
+        for phase in (F.FLIDE_GDN_TRUNKS, F.FLIDE_GDN_QUESTIONS):
+            F.flide_fork_gdn(ctx, self.caps, self.dev_meta, self.gdn_params, phase, self.x, self.conv_w,
+                             self.alpha, self.eta, self.state_pool, self.conv_pool, self.spec.n_slots, self.o_gdn,
+                             stream)
+        for l in range(self.n_attn):
+            F.flide_fork_attn(ctx, self.caps, self.dev_meta, self.attn_params[l], self.q[l], self.k[l], self.v[l],
+                              self.k_cache[l], self.v_cache[l], self.o_attn[l], self.ws[l], stream)
+        F.flide_readout(ctx, self.caps, self.dev_meta, self.ro_params, self.h, self.w_opt, self.opt_off,
+                        self.opt_id, max(1, self.spec.opt_cap), self.probs, stream)
+        del s
+
+
+def spec_for_round(rnd, T_cap: Optional[int] = None, R_cap: Optional[int] = None, Q_cap: Optional[int] = None,
+                   opt_cap: Optional[int] = None) -> RoundSpec:
+    """Buffer shape that holds ``rnd`` (optionally larger capacities)."""
+    T = int(sum((r.P - r.m) + sum(r.q_len) for r in rnd.requests))
+    R = len(rnd.requests)
+    Q = int(sum(len(r.q_len) for r in rnd.requests))
+    n_opt = int(sum(sum(r.n_opt) for r in rnd.requests))
+    slots = [r.out_slot for r in rnd.requests] + [r.ckpt_slot for r in rnd.requests if r.m > 0]
+    max_m = max([r.m for r in rnd.requests] + [0])
+    max_pos = max([r.P + (max(r.q_len) if r.q_len else 0) for r in rnd.requests] + [1])
+    return RoundSpec(rnd.shapes, rnd.dtype, T_cap or max(T, 1), R_cap or max(R, 1), Q_cap if Q_cap is not None else Q,
+                     max(slots + [0]) + 1, opt_cap or max(n_opt, 1), max_m, max_pos)
