@@ -17,7 +17,6 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -112,7 +111,6 @@ def main():
               "(request-sharded multi-GPU rounds are not built); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from tree_forked_hybrid_amd import flide as F
@@ -253,7 +251,6 @@ def main():
     }
     print(json.dumps(rec), flush=True)
     ctx.close()
-    del np, math
 
 
 if __name__ == "__main__":
