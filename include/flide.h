@@ -211,7 +211,9 @@ flide_status flide_attn_workspace_bytes(const flide_caps* caps, const flide_attn
 /*  q        [T_cap, Hq, d]   queries, not yet rotated
  *  k, v     [T_cap, Hkv, d]  keys (not yet rotated) and values
  *  k_cache  [slots, cache_rows, Hkv, d] keys of positions 0..m-1, already
- *           rotated; v_cache the matching values.  Read for requests with m > 0
+ *           rotated.  v_cache [slots, Hkv, d, cache_rows]: the matching values,
+ *           stored transposed (position fastest) so value tiles load as rows.
+ *           cache_rows must be a multiple of 8.  Read for requests with m > 0
  *           from slot ckpt_slot; may be NULL when no request resumes.
  *  o        [T_cap, Hq, d]   output rows 0..T-1 (tail rows untouched)
  *  workspace device scratch of flide_attn_workspace_bytes bytes

@@ -64,3 +64,80 @@ def test_edge_cases(ctx, dtype):
     rnd = custom_round(EDGE, dtype, reqs, base=21)
     bufs, lay = harness.run_gpu(rnd, ctx, "direct")
     harness.check_round(rnd, harness.outputs(bufs), lay, mode="isolated")
+
+
+def _edge_reqs():
+    return [Request(P=150, m=0, q_len=(1, 33, 70), n_opt=(1, 3, 2), out_slot=0),  # several key and query tiles
+            Request(P=0, m=0, q_len=(3,), n_opt=(2,), out_slot=1),
+            Request(P=2, m=0, q_len=(4, 1), n_opt=(2, 5), out_slot=2),
+            Request(P=9, m=0, q_len=(), n_opt=(), out_slot=3),
+            Request(P=104, m=102, q_len=(5, 17), n_opt=(3, 2), ckpt_slot=6, out_slot=4),
+            Request(P=64, m=64, q_len=(2,), n_opt=(2,), ckpt_slot=7, out_slot=5)]
+
+
+@pytest.mark.parametrize("d", [256, 128])
+def test_edge_cases_mfma_path(ctx, d):
+    sh = LayerShapes(H=2, dk=32, dv=32, conv_k=4, Hq=8, Hkv=2, d=d, theta=1e4, hidden=64, swa_window=40)
+    rnd = custom_round(sh, "bf16", _edge_reqs(), base=23)
+    bufs, lay = harness.run_gpu(rnd, ctx, "direct")
+    harness.check_round(rnd, harness.outputs(bufs), lay, mode="isolated")
+
+
+def test_long_document_round_with_sliding_window(ctx):
+    full = make_round(2, 0)
+    j = min(range(len(full.requests)), key=lambda i: full.requests[i].P)
+    rnd = full.subset([j])
+    bufs, lay = harness.run_gpu(rnd, ctx, "direct")
+    r = rnd.requests[0]
+    tn = r.P - r.m
+    rng = np.random.default_rng(0)
+    rows = sorted(set(rng.choice(tn, 96, replace=False).tolist()) | {0, 1, 63, 64, tn - 1})
+    segs = rnd.segment_rows(0)
+    for i in range(4):
+        s, L = segs[1 + i]
+        rows += list(range(s, s + L))
+    harness.check_round(rnd, harness.outputs(bufs), lay, mode="memo", questions=[0, 1, 2, 3],
+                        attn_rows_fn=lambda _j: rows)
+
+
+def test_agent_resume_round(ctx):
+    rnd = make_round(4, 0, requests=[0])
+    bufs, lay = harness.run_gpu(rnd, ctx, "direct")
+    r = rnd.requests[0]
+    tn = r.P - r.m
+    segs = rnd.segment_rows(0)
+    rows = [0, 1, 2, 500, 1023, tn - 1]
+    for i in range(2):
+        s, L = segs[1 + i]
+        rows += [s, s + L // 2, s + L - 1]
+    harness.check_round(rnd, harness.outputs(bufs), lay, mode="memo", questions=[0, 1],
+                        attn_rows_fn=lambda _j: rows)
+
+
+def test_deterministic_round_composition_invariance(ctx):
+    """Outputs of a request are bit-identical alone and inside a round of eight (agent resume workload)."""
+    full = make_round(4, 0)
+    one = full.subset([3])
+    b1, l1 = harness.run_gpu(one, ctx, "graph")
+    g1 = harness.outputs(b1)
+    b8, l8 = harness.run_gpu(full, ctx, "graph")
+    g8 = harness.outputs(b8)
+    rows1 = harness.stream_rows(one, l1, 0)
+    rows8 = harness.stream_rows(full, l8, 3)
+    for key in ("attn_o", "gdn_o"):
+        np.testing.assert_array_equal(g1[key][rows1], g8[key][rows8], err_msg=key)
+    slot = full.requests[3].out_slot
+    np.testing.assert_array_equal(g1["state_pool"][slot], g8["state_pool"][slot])
+    off1, off8 = harness.option_offsets(one), harness.option_offsets(full)
+    q0 = sum(len(r.q_len) for r in full.requests[:3])
+    n = off1[-1]
+    np.testing.assert_array_equal(g1["probs"][:n], g8["probs"][off8[q0]:off8[q0] + n])
+
+
+def test_short_rounds_full_size_graph_bucket(ctx):
+    """The benchmark's launch configuration (whole round, 36864-row bucket, graph replay), sampled parity."""
+    from tree_forked_hybrid_amd.runner import spec_for_round
+    rnd = make_round(1, 0)
+    spec = spec_for_round(rnd, T_cap=36864, R_cap=64, Q_cap=64)
+    bufs, lay = harness.run_gpu(rnd, ctx, "graph", spec=spec)
+    harness.check_round(rnd, harness.outputs(bufs), lay, mode="memo", requests=[0, 31, 63])

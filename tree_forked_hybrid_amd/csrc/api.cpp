@@ -175,7 +175,8 @@ flide_status check_attn(flide_ctx* ctx, const flide_attn_params* p) {
   if (p->window < 0) return fail(ctx, FLIDE_E_INVALID_ARG, "window must be >= 0");
   if (p->max_pos < 1 || !(p->theta > 0.0)) return fail(ctx, FLIDE_E_INVALID_ARG, "need max_pos >= 1 and theta > 0");
   if (p->dtype != FLIDE_F32 && p->dtype != FLIDE_BF16) return fail(ctx, FLIDE_E_UNSUPPORTED, "dtype must be f32 or bf16");
-  if (p->cache_rows < 0 || p->cache_slots < 0) return fail(ctx, FLIDE_E_INVALID_ARG, "cache shape must be >= 0");
+  if (p->cache_rows < 0 || p->cache_slots < 0 || p->cache_rows % 8 != 0)
+    return fail(ctx, FLIDE_E_INVALID_ARG, "cache shape must be >= 0 with cache_rows a multiple of 8");
   int64_t table_bytes = int64_t(p->max_pos) * p->d * 4;
   if (table_bytes > (int64_t(1) << 32)) return fail(ctx, FLIDE_E_UNSUPPORTED, "rotary table above 4 GiB");
   return FLIDE_OK;
@@ -220,11 +221,9 @@ flide_status enqueue_attn(flide_ctx* ctx, const MetaView& mv, const flide_attn_p
     return fail(ctx, FLIDE_E_INVALID_ARG, "K/V cache shape given without cache buffers");
   RopeArgs rope;
   FLIDE_TRY(ensure_rope(ctx, p.theta, p.d, p.max_pos, &rope));
-  FLIDE_TRY(launched(ctx, launch_rope_k(mv, p, rope, k, ws, stream), "rope_k"));
-  FLIDE_TRY(launched(ctx, launch_attn(mv, p, rope, q, ws, v, p.cache_rows > 0 ? kc : nullptr,
-                                      p.cache_rows > 0 ? vc : nullptr, o, stream),
-                     "fork_attn"));
-  return FLIDE_OK;
+  return launched(ctx, launch_attn(mv, p, rope, q, k, v, p.cache_rows > 0 ? kc : nullptr,
+                                   p.cache_rows > 0 ? vc : nullptr, o, ws, stream),
+                  "fork_attn");
 }
 
 flide_status enqueue_gdn(flide_ctx* ctx, const MetaView& mv, const flide_gdn_params& p, int phase, const void* x,
@@ -333,8 +332,7 @@ flide_status flide_meta_upload(flide_ctx* ctx, const flide_caps* caps, const int
 flide_status flide_attn_workspace_bytes(const flide_caps* caps, const flide_attn_params* p, int64_t* bytes) {
   if (!caps || !p || !bytes) return FLIDE_E_INVALID_ARG;
   if (caps->T_cap < 1 || p->Hkv < 1 || p->d < 1) return FLIDE_E_INVALID_ARG;
-  const int64_t elem = p->dtype == FLIDE_BF16 ? 2 : 4;
-  *bytes = int64_t(caps->T_cap) * p->Hkv * p->d * elem;
+  *bytes = attn_workspace_bytes(*caps, *p);
   return FLIDE_OK;
 }
 

@@ -107,9 +107,12 @@ struct RopeArgs {
 
 int launch_rope_k(const MetaView& mv, const flide_attn_params& p, const RopeArgs& rope, const void* k,
                   void* k_rot, void* stream);
-int launch_attn(const MetaView& mv, const flide_attn_params& p, const RopeArgs& rope, const void* q,
-                const void* k_rot, const void* v, const void* k_cache, const void* v_cache, void* o,
-                void* stream);
+// Rotates keys (and, on the MFMA path, transposes values) into `workspace`,
+// then runs the attention kernel.
+int launch_attn(const MetaView& mv, const flide_attn_params& p, const RopeArgs& rope, const void* q, const void* k,
+                const void* v, const void* k_cache, const void* v_cache, void* o, void* workspace, void* stream);
+bool attn_uses_mfma(const flide_attn_params& p);
+int64_t attn_workspace_bytes(const flide_caps& c, const flide_attn_params& p);
 int launch_gdn(const MetaView& mv, const flide_gdn_params& p, int phase, const void* x, const float* conv_w,
                const float* alpha, const float* eta, float* state_pool, void* conv_pool, int32_t n_slots,
                void* o, void* stream);

@@ -63,8 +63,9 @@ class RoundBuffers:
                                     int(spec.n_slots if spec.cache_rows > 0 else 0), _flide_dtype(spec.dtype), 0)
             self.attn_params.append(p)
             if spec.cache_rows > 0:
+                # keys [slot, row, kv head, d]; values transposed [slot, kv head, d, row]
                 self.k_cache.append(z(spec.n_slots, spec.cache_rows, s.Hkv, s.d))
-                self.v_cache.append(z(spec.n_slots, spec.cache_rows, s.Hkv, s.d))
+                self.v_cache.append(z(spec.n_slots, s.Hkv, s.d, spec.cache_rows))
             else:
                 self.k_cache.append(None)
                 self.v_cache.append(None)
@@ -164,7 +165,8 @@ class RoundBuffers:
                     if r.m > spec.cache_rows:
                         raise ValueError("checkpoint longer than the K/V cache")
                     self.k_cache[layer][r.ckpt_slot, :r.m].copy_(torch.from_numpy(pl[pre + "_k"]).to(dt))
-                    self.v_cache[layer][r.ckpt_slot, :r.m].copy_(torch.from_numpy(pl[pre + "_v"]).to(dt))
+                    vv = torch.from_numpy(np.ascontiguousarray(np.transpose(pl[pre + "_v"], (1, 2, 0))))
+                    self.v_cache[layer][r.ckpt_slot, :, :, :r.m].copy_(vv.to(dt))
         self.rows_idx = rows_idx
         self._struct = None
 
@@ -232,6 +234,7 @@ def spec_for_round(rnd, T_cap: Optional[int] = None, R_cap: Optional[int] = None
     n_opt = int(sum(sum(r.n_opt) for r in rnd.requests))
     slots = [r.out_slot for r in rnd.requests] + [r.ckpt_slot for r in rnd.requests if r.m > 0]
     max_m = max([r.m for r in rnd.requests] + [0])
+    max_m = (max_m + 7) // 8 * 8
     max_pos = max([r.P + (max(r.q_len) if r.q_len else 0) for r in rnd.requests] + [1])
     return RoundSpec(rnd.shapes, rnd.dtype, T_cap or max(T, 1), R_cap or max(R, 1), Q_cap if Q_cap is not None else Q,
                      max(slots + [0]) + 1, opt_cap or max(n_opt, 1), max_m, max_pos)

@@ -39,10 +39,13 @@ TENSOR_IDS = {
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    # finite inputs cannot overflow 32 bits here
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    return u.view(np.float32)
 
 
 def _rng(base: int, name: str, *extra: int) -> np.random.Generator:
@@ -170,8 +173,8 @@ class Round:
     # -- global (per-layer) weights ------------------------------------------------
     def conv_w(self) -> np.ndarray:
         s = self.shapes
-        w = _rng(self.base, "conv_w").standard_normal((s.channels, s.conv_k), dtype=np.float32)
-        return (w * np.float32(1.0 / np.sqrt(s.conv_k))).astype(np.float32)
+        w = _rng(self.base, "conv_w").standard_normal((s.channels, s.conv_k))
+        return (w * (1.0 / np.sqrt(s.conv_k))).astype(np.float32)
 
     # -- per-request payloads -------------------------------------------------------
     def _act(self, x: np.ndarray) -> np.ndarray:
@@ -187,10 +190,10 @@ class Round:
         out = {}
 
         def normal(name, shape, scale=1.0):
-            z = _rng(b, name, rid).standard_normal(shape, dtype=np.float32)
+            z = _rng(b, name, rid).standard_normal(shape)
             if scale != 1.0:
-                z *= np.float32(scale)
-            return z
+                z *= scale
+            return z.astype(np.float32)
 
         out["attn_q"] = self._act(normal("attn_q", (n, s.Hq, s.d)))
         out["attn_k"] = self._act(normal("attn_k", (n, s.Hkv, s.d)))
