@@ -141,3 +141,14 @@ def test_short_rounds_full_size_graph_bucket(ctx):
     spec = spec_for_round(rnd, T_cap=36864, R_cap=64, Q_cap=64)
     bufs, lay = harness.run_gpu(rnd, ctx, "graph", spec=spec)
     harness.check_round(rnd, harness.outputs(bufs), lay, mode="memo", requests=[0, 31, 63])
+
+
+@pytest.mark.parametrize("dtype", ["bf16"])
+def test_edge_cases_chunked_gdn(ctx, dtype):
+    """dk = dv = 128 routes the GDN layer to the chunked MFMA kernel: partial chunks, a question longer
+    than one chunk, empty and short trunks, resumes with fewer new rows than the conv width."""
+    sh = LayerShapes(H=2, dk=128, dv=128, conv_k=4, Hq=4, Hkv=1, d=128, theta=1e4, hidden=64, swa_window=40)
+    reqs = _edge_reqs() + [Request(P=300, m=0, q_len=(64, 65), n_opt=(2, 2), out_slot=8)]
+    rnd = custom_round(sh, dtype, reqs, base=29)
+    bufs, lay = harness.run_gpu(rnd, ctx, "direct")
+    harness.check_round(rnd, harness.outputs(bufs), lay, mode="isolated")

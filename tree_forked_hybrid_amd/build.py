@@ -24,6 +24,7 @@ SOURCES = [
     "meta_kernels.hip",
     "attn_kernels.hip",
     "gdn_kernels.hip",
+    "gdn_chunk_kernels.hip",
     "readout_kernels.hip",
 ]
 HEADERS = ["flide_internal.hpp", "device_common.hpp"]

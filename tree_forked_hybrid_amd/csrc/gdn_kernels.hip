@@ -212,7 +212,7 @@ static int dispatch_plain(const MetaView& mv, const flide_gdn_params& p, int pha
   return int(hipErrorInvalidValue);
 }
 
-int launch_gdn(const MetaView& mv, const flide_gdn_params& p, int phase, const void* x, const float* conv_w,
+int launch_gdn_plain(const MetaView& mv, const flide_gdn_params& p, int phase, const void* x, const float* conv_w,
                const float* alpha, const float* eta, float* state_pool, void* conv_pool, int32_t n_slots, void* o,
                void* stream) {
   if (p.dtype == FLIDE_BF16)
