@@ -104,7 +104,10 @@ typedef struct {
  * device.  Segments are ordered trunks first (index j = request j), then
  * questions in stream order.
  *   hdr[0..15]  T, R, n_seg, n_qst, n_tiles, max_pos, 0..., magic
- *   seg_*       [seg_cap]  row0, len, req, branch, pos0, state (slot or -1)
+ *   seg_*       [seg_cap]  row0, len, req, branch, pos0, state (slot or -1),
+ *                          vcol0: column offset of the segment in the transposed
+ *                          value workspace (column = vcol0 + position, so that
+ *                          8-aligned positions land on 16-byte aligned columns)
  *   req_*       [R_cap]    trunk_row0, P, m, ckpt_slot, out_slot, q_seg0, n_q
  *   qfin_row    [Q_cap]    last stream row of every question (stream order)
  *   tile_seg    [tile_cap] attention work list: segment of each tile
@@ -115,7 +118,7 @@ typedef struct {
   int64_t host_words;
   int64_t dev_words;
   int64_t hdr;
-  int64_t seg_row0, seg_len, seg_req, seg_branch, seg_pos0, seg_state;
+  int64_t seg_row0, seg_len, seg_req, seg_branch, seg_pos0, seg_state, seg_vcol0;
   int64_t req_trunk_row0, req_P, req_m, req_ckpt, req_out, req_q_seg0, req_nq;
   int64_t qfin_row;
   int64_t tile_seg, tile_row0;
@@ -205,7 +208,9 @@ typedef struct {
   int32_t deterministic;
 } flide_attn_params;
 
-/* Bytes of the workspace flide_fork_attn needs for `caps` (rotated keys). */
+/* Bytes of the workspace flide_fork_attn needs for `caps` (rotated keys and, on the
+ * bf16 MFMA path, transposed values).  Zero-fill the workspace once when allocating it:
+ * columns between segments are read under a zero mask and must hold finite values. */
 flide_status flide_attn_workspace_bytes(const flide_caps* caps, const flide_attn_params* p, int64_t* bytes);
 
 /*  q        [T_cap, Hq, d]   queries, not yet rotated

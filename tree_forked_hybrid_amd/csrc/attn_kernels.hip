@@ -170,17 +170,23 @@ __device__ __forceinline__ f32x4v mfma16x16x32(u32x4v a, u32x4v b, f32x4v c) {
                                                  0, 0, 0);
 }
 
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+// Two floats to two bf16 (round to nearest even) in one hardware conversion.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
 }
 
-// Rows of the transposed value workspace per (kv head, channel): the stream
-// capacity rounded up, plus room for one aligned over-read.
-__host__ __device__ __forceinline__ int64_t vt_rows(int T_cap) { return ((int64_t(T_cap) + 63) / 64) * 64 + 64; }
+// Columns of the transposed value workspace per (kv head, channel): the stream
+// capacity plus up to 7 alignment columns per segment, rounded up.
+__host__ __device__ __forceinline__ int64_t vt_cols(int T_cap, int seg_cap) {
+  return ((int64_t(T_cap) + 8 * int64_t(seg_cap) + 64 + 63) / 64) * 64;
+}
 
 // Prep pass of the MFMA path: rotate every key row once (rotate-half pairs at
 // the row's metadata position) into k_rot [T_cap, Hkv, D], and write the values
-// transposed into vt [Hkv, D, vt_rows] so value tiles load as contiguous rows.
+// transposed into vt [Hkv, D, vt_cols]; the value of position p of segment s
+// lands in column seg_vcol0[s] + p, so 8-aligned positions are 16-byte aligned.
 template <int D>
 __global__ void __launch_bounds__(256) kv_prep_kernel(MetaView mv, const bf16_t* __restrict__ k,
                                                       const bf16_t* __restrict__ v, bf16_t* __restrict__ k_rot,
@@ -192,11 +198,10 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(MetaView mv, const bf16_t*
   const int r0 = blockIdx.x * ROWS;
   const int g = blockIdx.y;
   const int T = mv.hdr[H_T];
-  if (r0 >= mv.T_cap) return;
+  if (r0 >= T) return;
   const int tid = threadIdx.x;
   constexpr int HALF = D / 2;
   constexpr int GROUPS = HALF / 8;  // 8 pairs per work item
-  // keys: rotate
   for (int it = tid; it < ROWS * GROUPS; it += 256) {
     const int rr = it / GROUPS, i0 = (it % GROUPS) * 8;
     const int row = r0 + rr;
@@ -222,7 +227,7 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(MetaView mv, const bf16_t*
     *reinterpret_cast<u32x4v*>(k_rot + base + i0) = lo;
     *reinterpret_cast<u32x4v*>(k_rot + base + i0 + HALF) = hi;
   }
-  // values: stage rows in LDS, write transposed (rows >= T become zeros)
+  // values: stage the rows in LDS, then write columns (lane = row, so stores coalesce)
   for (int it = tid; it < ROWS * (D / 8); it += 256) {
     const int rr = it / (D / 8), ch = it % (D / 8);
     const int row = r0 + rr;
@@ -235,39 +240,24 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(MetaView mv, const bf16_t*
     dst[3] = val[3];
   }
   __syncthreads();
-  const int64_t VT = vt_rows(mv.T_cap);
-  for (int it = tid; it < D * (ROWS / 8); it += 256) {
-    const int c = it % (ROWS / 8), dd = it / (ROWS / 8);
-    u32x4v out;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t e0 = v_lds[(8 * c + 2 * w) * STR + dd];
-      const uint32_t e1 = v_lds[(8 * c + 2 * w + 1) * STR + dd];
-      out[w] = e0 | (e1 << 16);
-    }
-    *reinterpret_cast<u32x4v*>(vt + (int64_t(g) * D + dd) * VT + r0 + 8 * c) = out;
-  }
+  const int lane = tid & 63, w = tid >> 6;
+  const int row = r0 + lane;
+  if (row >= T) return;
+  const int n_seg = mv.hdr[H_NSEG];
+  const int s = find_segment(mv.seg_row0, n_seg, row);
+  const int64_t col = int64_t(mv.seg_vcol0[s]) + mv.seg_pos0[s] + (row - mv.seg_row0[s]);
+  const int64_t VT = vt_cols(mv.T_cap, mv.seg_cap);
+  bf16_t* dst = vt + int64_t(g) * D * VT + col;
+  for (int dd = w; dd < D; dd += 4) dst[int64_t(dd) * VT] = v_lds[lane * STR + dd];
 }
 
-// 8 consecutive bf16 starting at element `e` of a row whose 16-byte chunks are
-// aligned; `o` = e & 7 is the same for every chunk of a key range.
-__device__ __forceinline__ u32x4v load8_realign(const bf16_t* __restrict__ base, int64_t e, int o) {
-  const bf16_t* a = base + (e - o);
-  const u32x4v w0 = *reinterpret_cast<const u32x4v*>(a);
-  if (o == 0) return w0;
-  const u32x4v w1 = *reinterpret_cast<const u32x4v*>(a + 8);
-  const uint32_t w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-  const int dw = o >> 1;
-  u32x4v r;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    uint32_t lo = w[k], hi = w[k + 1];
-    if (dw == 1) { lo = w[k + 1]; hi = w[k + 2]; }
-    if (dw == 2) { lo = w[k + 2]; hi = w[k + 3]; }
-    if (dw == 3) { lo = w[k + 3]; hi = w[k + 4]; }
-    r[k] = (o & 1) ? __builtin_amdgcn_alignbyte(hi, lo, 2) : lo;
-  }
-  return r;
+typedef __attribute__((address_space(3))) void* lds_vptr_t;
+typedef __attribute__((address_space(1))) void* gbl_vptr_t;
+
+// 16 bytes per lane from global memory straight into LDS: lane i of the wave
+// writes bytes [16 i, 16 i + 16) after `lds_base` (a wave-uniform address).
+__device__ __forceinline__ void async_copy16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_vptr_t)(src), (lds_vptr_t)(lds_base), 16, 0, 0);
 }
 
 // One workgroup = one query tile (32 rows of one segment) x up to 4 q heads of
@@ -275,21 +265,41 @@ __device__ __forceinline__ u32x4v load8_realign(const bf16_t* __restrict__ base,
 // transposed (S^T = K Q^T: keys on MFMA rows, queries on columns) so that each
 // lane holds whole query columns: softmax statistics and the rescale of the
 // output accumulator (O^T = V^T P^T, d on rows) stay lane-local.
-template <int D, int BN>
-__global__ void __launch_bounds__(256) attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q,
-                                                        const bf16_t* __restrict__ k_rot,
-                                                        const bf16_t* __restrict__ vt,
-                                                        const bf16_t* __restrict__ k_cache,
-                                                        const bf16_t* __restrict__ v_cache, bf16_t* __restrict__ o,
-                                                        const float* __restrict__ table, int max_pos, int Hq,
-                                                        int Hkv, int window, int cache_rows, int cache_slots) {
-  constexpr int NC = D / 32;   // 32-wide d chunks of the score contraction
-  constexpr int NDB = D / 16;  // 16-wide d blocks of the output
-  constexpr int NKB = BN / 16; // 16-key blocks per tile
-  constexpr int KSTR = D + 8;  // LDS row stride of the key tile (elements)
-  constexpr int VSTR = BN + 4; // LDS row stride of the transposed value tile (elements)
-  __shared__ __attribute__((aligned(16))) bf16_t k_lds[BN * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16_t v_lds[D * VSTR];
+//
+// Key and value tiles of 32 keys are double-buffered in LDS and filled by
+// direct global-to-LDS copies issued one tile ahead, so memory latency overlaps
+// the MFMA work; 64 KB of LDS per workgroup leaves room for two workgroups per
+// CU.  Both tiles are stored with an XOR swizzle of their 16-byte chunks (key
+// row r: chunk c at slot c ^ ksw(r); value row d: chunk c at slot
+// c ^ ((d >> 2) & 3)), which makes the MFMA operand reads bank-conflict free.
+// Score block kb row r is key 8 (r / 4) + 4 kb + r % 4, so each lane ends up
+// with the probabilities of 8 consecutive keys: exactly the k-slots of its
+// P^T fragment, whose matching V^T fragment is then one 16-byte read.
+//
+// Online softmax in the log2 domain (queries are pre-scaled by log2(e)/sqrt(d)),
+// with a lazily moved running maximum: the output accumulator is rescaled only
+// when a column's maximum grows by more than 8 (a factor of 256), which keeps
+// every exponent <= 2^8 and the result exact up to rounding.
+// Swizzle of the key tile's 16-byte chunks: distinct for the 16 rows one MFMA
+// operand read touches (rows 8a + 4kb + b, a, b in 0..3).
+__device__ __forceinline__ int ksw(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
+
+template <int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_rot,
+                 const bf16_t* __restrict__ vt, const bf16_t* __restrict__ k_cache,
+                 const bf16_t* __restrict__ v_cache, bf16_t* __restrict__ o, const float* __restrict__ table,
+                 int max_pos, int Hq, int Hkv, int window, int cache_rows, int cache_slots) {
+  constexpr int BN = 32;             // keys per tile
+  constexpr int NC = D / 32;         // 32-wide d chunks of the score contraction
+  constexpr int NDB = D / 16;        // 16-wide d blocks of the output
+  constexpr int KROW = D * 2;        // bytes per key row
+  constexpr int KCH = D / 8;         // 16-byte chunks per key row
+  constexpr int VROW = BN * 2;       // bytes per value row (one channel, BN keys)
+  constexpr int TILE_BYTES = BN * D * 2;
+  constexpr int IPW = TILE_BYTES / 1024 / 4;  // copy instructions per wave per tile (per K or V)
+  static_assert(IPW >= 1, "tile split over 4 waves");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * TILE_BYTES];  // K0 K1 V0 V1
 
   const int tile = blockIdx.x;
   if (tile >= mv.hdr[H_NTILES]) return;
@@ -321,20 +331,95 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(MetaView mv, const bf16_
     if (tid == 0) flag_error(mv.dev_error, E_POSITION);
     return;
   }
+  const int64_t VT = vt_cols(mv.T_cap, mv.seg_cap);
+  const int lo_w = window > 0 ? qpos_min - window + 1 : INT_MIN;
 
-  // ---- rotated queries, as MFMA B fragments (query = column) ----
+  // ---- the (up to) three key ranges: positions [lo, hi), key row = p + roff, value column = p + voff ----
+  // (A) checkpoint cache, (B) the request's trunk rows (question tiles only), (C) own rows
+  const int lo0 = max(0, lo_w), hi0 = m > 0 ? min(m, qpos_max + 1) : 0;
+  const int lo1 = max(m, lo_w), hi1 = question ? P : 0;
+  const int lo2 = max(pos0, lo_w), hi2 = qpos_max + 1;
+  const int64_t roff0 = int64_t(ckpt) * cache_rows, roff1 = int64_t(mv.req_trunk_row0[j]) - m,
+                roff2 = int64_t(seg_row0) - pos0;
+  const int64_t voff1 = mv.seg_vcol0[j], voff2 = mv.seg_vcol0[seg];  // trunk segment index = request index
+  const int ts00 = lo0 & ~(BN - 1), ts01 = lo1 & ~(BN - 1), ts02 = lo2 & ~(BN - 1);
+  const int n0 = lo0 < hi0 ? (hi0 - ts00 + BN - 1) / BN : 0;
+  const int n1 = lo1 < hi1 ? (hi1 - ts01 + BN - 1) / BN : 0;
+  const int n2 = lo2 < hi2 ? (hi2 - ts02 + BN - 1) / BN : 0;
+  const int n_tiles = n0 + n1 + n2;
+  struct TileInfo {
+    int src, ts, lo, hi;
+    int64_t roff, voff;
+  };
+  // range and key interval of flat tile index t (all values are uniform across the workgroup)
+  auto tile_info = [&](int t) {
+    TileInfo ti;
+    if (t < n0) {
+      ti = TileInfo{0, ts00 + t * BN, lo0, hi0, roff0, 0};
+    } else if (t < n0 + n1) {
+      ti = TileInfo{1, ts01 + (t - n0) * BN, lo1, hi1, roff1, voff1};
+    } else {
+      ti = TileInfo{2, ts02 + (t - n0 - n1) * BN, lo2, hi2, roff2, voff2};
+    }
+    return ti;
+  };
+  // Lane constants of the copies: wave w issues copy instructions I = w*IPW + ii; lane l of
+  // instruction I fills 16-byte LDS slot 64 I + l.
+  int k_row[IPW], k_off[IPW], v_dd[IPW], v_c[IPW];
+#pragma unroll
+  for (int ii = 0; ii < IPW; ++ii) {
+    const int slot = (w * IPW + ii) * 64 + l;
+    k_row[ii] = slot / KCH;
+    const int kc = (slot % KCH) ^ ksw(k_row[ii]);
+    k_off[ii] = (k_row[ii] * Hkv * D + kc * 8) * 2;  // bytes from the tile's first key row
+    v_dd[ii] = slot / (BN / 8);
+    v_c[ii] = (slot % (BN / 8)) ^ ((v_dd[ii] >> 2) & 3);
+  }
+  auto issue = [&](int t, int buf) {
+    const TileInfo ti = tile_info(t);
+    const int ts = ti.ts, lo = ti.lo, hi = ti.hi;
+    const bool edge = ts < lo || ts + BN > hi;
+    const bf16_t* kbase = (ti.src == 0 ? k_cache : k_rot) + int64_t(kvh) * D;
+    const bf16_t* vbase =
+        ti.src == 0 ? v_cache + (int64_t(ckpt) * Hkv + kvh) * D * cache_rows : vt + int64_t(kvh) * D * VT;
+    const int vstride = ti.src == 0 ? cache_rows : int(VT);
+    unsigned char* kl = lds + buf * TILE_BYTES;
+    unsigned char* vl = lds + (2 + buf) * TILE_BYTES;
+    const unsigned char* ktile = reinterpret_cast<const unsigned char*>(kbase + (int64_t(ts) + ti.roff) * Hkv * D);
+    const unsigned char* vtile = reinterpret_cast<const unsigned char*>(vbase + (int64_t(ts) + ti.voff));
+#pragma unroll
+    for (int ii = 0; ii < IPW; ++ii) {
+      int koff = k_off[ii];
+      int voff = (v_dd[ii] * vstride + 8 * v_c[ii]) * 2;
+      if (edge) {  // masked keys read a valid row / value chunk of the range
+        const int p = ts + k_row[ii];
+        const int pc = p < lo ? lo : (p >= hi ? hi - 1 : p);
+        koff += (pc - p) * Hkv * D * 2;
+        const int p0 = ts + 8 * v_c[ii];
+        const int lo8 = lo & ~7, hi8 = (hi - 1) & ~7;
+        const int p0c = p0 < lo8 ? lo8 : (p0 > hi8 ? hi8 : p0);
+        voff += (p0c - p0) * 2;
+      }
+      async_copy16(ktile + koff, kl + (w * IPW + ii) * 1024);
+      async_copy16(vtile + voff, vl + (w * IPW + ii) * 1024);
+    }
+  };
+
+  if (n_tiles > 0) issue(0, 0);
+
+  // ---- rotated, pre-scaled queries as MFMA B fragments (query = column) ----
+  const float sl2 = 1.4426950408889634f * rsqrtf(float(D));
   u32x4v qf[2][NC];
   int qpos[2];
-  bool qvalid[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int r = qb * 16 + r16;
-    qvalid[qb] = active && r < nrows;
+    const bool qv = active && r < nrows;
     qpos[qb] = qpos_min + r;
 #pragma unroll
     for (int c = 0; c < NC / 2; ++c) {
       u32x4v lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-      if (qvalid[qb]) {
+      if (qv) {
         const int64_t base = (int64_t(x0 + r) * Hq + h) * D + 32 * c + 8 * g4;
         const u32x4v a = *reinterpret_cast<const u32x4v*>(q + base);
         const u32x4v b = *reinterpret_cast<const u32x4v*>(q + base + D / 2);
@@ -344,8 +429,8 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(MetaView mv, const bf16_
           float a0 = __uint_as_float(a[ww] << 16), a1 = __uint_as_float(a[ww] & 0xFFFF0000u);
           float b0 = __uint_as_float(b[ww] << 16), b1 = __uint_as_float(b[ww] & 0xFFFF0000u);
           float c0 = cs[4 * ww], s0 = cs[4 * ww + 1], c1 = cs[4 * ww + 2], s1 = cs[4 * ww + 3];
-          lo[ww] = pack_bf16x2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
-          hi[ww] = pack_bf16x2(b0 * c0 + a0 * s0, b1 * c1 + a1 * s1);
+          lo[ww] = pack_bf16x2((a0 * c0 - b0 * s0) * sl2, (a1 * c1 - b1 * s1) * sl2);
+          hi[ww] = pack_bf16x2((b0 * c0 + a0 * s0) * sl2, (b1 * c1 + a1 * s1) * sl2);
         }
       }
       qf[qb][c] = lo;
@@ -359,156 +444,98 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(MetaView mv, const bf16_
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4v{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  const float sl2 = 1.4426950408889634f * rsqrtf(float(D));
-  const int lo_w = window > 0 ? qpos_min - window + 1 : INT_MIN;
-  const int64_t VT = vt_rows(mv.T_cap);
+  // LDS byte offset of this lane's V^T fragment (channel row r16 of a 16-row block, keys 8 g4 .. +7)
+  const int vfrag = r16 * VROW + ((g4 ^ ((r16 >> 2) & 3)) << 4);
 
-  for (int src = 0; src < 3; ++src) {
-    // positions [lo, hi) of this key range; key row r(p) = p + roff
-    int lo, hi;
-    int64_t roff;
-    const bf16_t* kptr;
-    const bf16_t* vptr;
-    int64_t vstride;
-    if (src == 0) {
-      if (m == 0) continue;
-      lo = max(0, lo_w);
-      hi = min(m, qpos_max + 1);
-      roff = int64_t(ckpt) * cache_rows;
-      kptr = k_cache + int64_t(kvh) * D;
-      vptr = v_cache + (int64_t(ckpt) * Hkv + kvh) * D * cache_rows;
-      vstride = cache_rows;
-    } else if (src == 1) {
-      if (!question) continue;
-      lo = max(m, lo_w);
-      hi = P;
-      roff = int64_t(mv.req_trunk_row0[j]) - m;
-      kptr = k_rot + int64_t(kvh) * D;
-      vptr = vt + int64_t(kvh) * D * VT;
-      vstride = VT;
-    } else {
-      lo = max(pos0, lo_w);
-      hi = qpos_max + 1;
-      roff = int64_t(seg_row0) - pos0;
-      kptr = k_rot + int64_t(kvh) * D;
-      vptr = vt + int64_t(kvh) * D * VT;
-      vstride = VT;
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile t have landed
+    __syncthreads();                // ... and every wave's; buffer buf^1 is free
+    if (t + 1 < n_tiles) issue(t + 1, buf ^ 1);
+    if (!active) continue;
+    const TileInfo cur = tile_info(t);
+    const int ts = cur.ts, lo = cur.lo, hi = cur.hi;
+    const unsigned char* kl = lds + buf * TILE_BYTES;
+    const unsigned char* vl = lds + (2 + buf) * TILE_BYTES;
+
+    // S^T = K Q^T over the 32 keys of the tile (already in log2 units)
+    f32x4v s[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb][0] = f32x4v{0.f, 0.f, 0.f, 0.f};
+      s[kb][1] = f32x4v{0.f, 0.f, 0.f, 0.f};
+      const int krow = 8 * (r16 >> 2) + 4 * kb + (r16 & 3);
+      const unsigned char* kr = kl + krow * KROW;
+      const int ks = ksw(krow);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4v a = *reinterpret_cast<const u32x4v*>(kr + (((4 * c + g4) ^ ks) << 4));
+        s[kb][0] = mfma16x16x32(a, qf[0][c], s[kb][0]);
+        s[kb][1] = mfma16x16x32(a, qf[1][c], s[kb][1]);
+      }
     }
-    if (lo >= hi) continue;
-    const int64_t vro = src == 0 ? 0 : roff;  // value column of position p: p + vro
-    const int valign = int((vro % 8 + 8) % 8);
-    for (int ts = lo - ((lo % BN) + BN) % BN; ts < hi; ts += BN) {
-      __syncthreads();
-      // key tile [BN][D]
-      for (int it = tid; it < BN * (D / 8); it += 256) {
-        const int kk = it / (D / 8), ch = it % (D / 8);
-        const int p = ts + kk;
-        u32x4v val = {0u, 0u, 0u, 0u};
-        if (p >= lo && p < hi)
-          val = *reinterpret_cast<const u32x4v*>(kptr + (int64_t(p) + roff) * (int64_t(Hkv) * D) + ch * 8);
-        *reinterpret_cast<u32x4v*>(k_lds + kk * KSTR + ch * 8) = val;
-      }
-      // transposed value tile [D][BN]
-      for (int it = tid; it < D * (BN / 8); it += 256) {
-        const int c = it % (BN / 8), dd = it / (BN / 8);
-        const int p0 = ts + 8 * c;
-        u32x4v val = {0u, 0u, 0u, 0u};
-        const bf16_t* row = vptr + int64_t(dd) * vstride;
-        if (p0 >= lo && p0 + 7 < hi) {
-          val = load8_realign(row, int64_t(p0) + vro, valign);
-        } else if (p0 + 7 >= lo && p0 < hi) {
-          uint32_t e[8];
+    // mask: key p is visible to query column q iff kmin(q) <= p <= kmax(q)
+    const bool full = ts >= lo && ts + BN <= hi && ts + BN - 1 <= qpos_min &&
+                      (window == 0 || qpos_max - ts < window);
+    u32x4v pf[2];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int p = p0 + i;
-            e[i] = (p >= lo && p < hi) ? uint32_t(row[int64_t(p) + vro]) : 0u;
-          }
-          val = u32x4v{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
-        }
-        u32x2v* dst = reinterpret_cast<u32x2v*>(v_lds + dd * VSTR + 8 * c);
-        dst[0] = u32x2v{val[0], val[1]};
-        dst[1] = u32x2v{val[2], val[3]};
-      }
-      __syncthreads();
-      if (!active) continue;
-
-      // S^T = K Q^T over the tile
-      f32x4v s[NKB][2];
+    for (int qb = 0; qb < 2; ++qb) {
+      if (!full) {
+        const int kmin = window > 0 ? max(lo, qpos[qb] - window + 1) : lo;
+        const int kmax = min(hi - 1, qpos[qb]);
+        const uint32_t span = uint32_t(kmax - kmin);
+        const int pb = ts + 8 * g4 - kmin;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[kb][0] = f32x4v{0.f, 0.f, 0.f, 0.f};
-        s[kb][1] = f32x4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const u32x4v a = *reinterpret_cast<const u32x4v*>(k_lds + (kb * 16 + r16) * KSTR + 32 * c + 8 * g4);
-          s[kb][0] = mfma16x16x32(a, qf[0][c], s[kb][0]);
-          s[kb][1] = mfma16x16x32(a, qf[1][c], s[kb][1]);
-        }
-      }
-      // mask, scale (log2 domain), online softmax per query column
-      const bool full = ts >= lo && ts + BN <= hi && ts + BN - 1 <= qpos_min &&
-                        (window == 0 || qpos_max - ts < window);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int p = ts + kb * 16 + 4 * g4 + i;
-            const bool ok = full || (p >= lo && p < hi && p <= qpos[qb] && (window == 0 || qpos[qb] - p < window));
-            const float v = ok ? s[kb][qb][i] * sl2 : -INFINITY;
-            s[kb][qb][i] = v;
-            mx = fmaxf(mx, v);
+            const bool ok = kmax >= kmin && uint32_t(pb + kb * 4 + i) <= span;
+            s[kb][qb][i] = ok ? s[kb][qb][i] : -INFINITY;
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run[qb], mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float corr = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pv = __builtin_amdgcn_exp2f(s[kb][qb][i] - m_use);
-            s[kb][qb][i] = pv;
-            rs += pv;
-          }
-        rs += __shfl_xor(rs, 16, 64);
-        rs += __shfl_xor(rs, 32, 64);
-        l_run[qb] = l_run[qb] * corr + rs;
-        m_run[qb] = m_new;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), fmaxf(s[0][qb][2], s[0][qb][3])),
+                       fmaxf(fmaxf(s[1][qb][0], s[1][qb][1]), fmaxf(s[1][qb][2], s[1][qb][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // move the running maximum only when it grows by more than 8 (log2 units)
+      const bool grow = mx > m_run[qb] + 8.f;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? fmaxf(m_run[qb], mx) : m_run[qb];
+        const float corr = m_run[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        l_run[qb] *= corr;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) acc[qb][db] *= corr;
+        m_run[qb] = m_new;
       }
-      // O^T += V^T P^T: K-steps of 32 keys = key blocks (2 ks, 2 ks + 1)
+      const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+      float rs = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < NKB / 2; ++ks) {
-        u32x4v pf[2];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const f32x4v a = s[2 * ks][qb], b = s[2 * ks + 1][qb];
-          pf[qb] = u32x4v{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
-                          pack_bf16x2(b[2], b[3])};
+        for (int i = 0; i < 4; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(s[kb][qb][i] - m_use);
+          s[kb][qb][i] = pv;
+          rs += pv;
         }
+      rs += __shfl_xor(rs, 16, 64);
+      rs += __shfl_xor(rs, 32, 64);
+      l_run[qb] += rs;
+      pf[qb] = u32x4v{pack_bf16x2(s[0][qb][0], s[0][qb][1]), pack_bf16x2(s[0][qb][2], s[0][qb][3]),
+                      pack_bf16x2(s[1][qb][0], s[1][qb][1]), pack_bf16x2(s[1][qb][2], s[1][qb][3])};
+    }
+    // O^T += V^T P^T over the tile's 32 keys (lane k-slots 8 g4 .. +7 = keys 8 g4 .. +7)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16_t* vr = v_lds + (db * 16 + r16) * VSTR + 32 * ks + 4 * g4;
-          const u32x2v x0v = *reinterpret_cast<const u32x2v*>(vr);
-          const u32x2v x1v = *reinterpret_cast<const u32x2v*>(vr + 16);
-          const u32x4v a = u32x4v{x0v[0], x0v[1], x1v[0], x1v[1]};
-          acc[0][db] = mfma16x16x32(a, pf[0], acc[0][db]);
-          acc[1][db] = mfma16x16x32(a, pf[1], acc[1][db]);
-        }
-      }
+    for (int db = 0; db < NDB; ++db) {
+      const u32x4v a = *reinterpret_cast<const u32x4v*>(vl + db * 16 * VROW + vfrag);
+      acc[0][db] = mfma16x16x32(a, pf[0], acc[0][db]);
+      acc[1][db] = mfma16x16x32(a, pf[1], acc[1][db]);
     }
   }
 
   if (!active) return;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    if (!qvalid[qb]) continue;
+    if (qb * 16 + r16 >= nrows) continue;
     const float inv = 1.f / l_run[qb];
     bf16_t* dst = o + (int64_t(x0 + qb * 16 + r16) * Hq + h) * D + 4 * g4;
 #pragma unroll
@@ -525,7 +552,11 @@ bool attn_uses_mfma(const flide_attn_params& p) { return p.dtype == FLIDE_BF16 &
 int64_t attn_workspace_bytes(const flide_caps& c, const flide_attn_params& p) {
   const int64_t elem = p.dtype == FLIDE_BF16 ? 2 : 4;
   int64_t bytes = int64_t(c.T_cap) * p.Hkv * p.d * elem;  // rotated keys
-  if (attn_uses_mfma(p)) bytes += int64_t(p.Hkv) * p.d * vt_rows(c.T_cap) * elem;  // transposed values
+  if (attn_uses_mfma(p)) {
+    flide_meta_layout L;
+    compute_layout(c, L);
+    bytes += int64_t(p.Hkv) * p.d * vt_cols(c.T_cap, L.seg_cap) * elem;  // transposed values
+  }
   return bytes;
 }
 
@@ -542,13 +573,13 @@ int launch_attn(const MetaView& mv, const flide_attn_params& p, const RopeArgs& 
     if (p.d == 256) {
       hipLaunchKernelGGL(kv_prep_kernel<256>, pg, dim3(256), 0, st, mv, (const bf16_t*)k, (const bf16_t*)v, k_rot,
                          vt, rope.table, rope.max_pos, p.Hkv);
-      hipLaunchKernelGGL((attn_mfma_kernel<256, 64>), grid, dim3(256), 0, st, mv, (const bf16_t*)q, k_rot, vt,
+      hipLaunchKernelGGL((attn_mfma_kernel<256>), grid, dim3(256), 0, st, mv, (const bf16_t*)q, k_rot, vt,
                          (const bf16_t*)k_cache, (const bf16_t*)v_cache, (bf16_t*)o, rope.table, rope.max_pos, p.Hq,
                          p.Hkv, W, p.cache_rows, p.cache_slots);
     } else {
       hipLaunchKernelGGL(kv_prep_kernel<128>, pg, dim3(256), 0, st, mv, (const bf16_t*)k, (const bf16_t*)v, k_rot,
                          vt, rope.table, rope.max_pos, p.Hkv);
-      hipLaunchKernelGGL((attn_mfma_kernel<128, 64>), grid, dim3(256), 0, st, mv, (const bf16_t*)q, k_rot, vt,
+      hipLaunchKernelGGL((attn_mfma_kernel<128>), grid, dim3(256), 0, st, mv, (const bf16_t*)q, k_rot, vt,
                          (const bf16_t*)k_cache, (const bf16_t*)v_cache, (bf16_t*)o, rope.table, rope.max_pos, p.Hq,
                          p.Hkv, W, p.cache_rows, p.cache_slots);
     }

@@ -48,6 +48,7 @@ struct MetaView {
   const int32_t* seg_branch;
   const int32_t* seg_pos0;
   const int32_t* seg_state;
+  const int32_t* seg_vcol0;
   const int32_t* req_trunk_row0;
   const int32_t* req_P;
   const int32_t* req_m;
@@ -74,6 +75,7 @@ inline MetaView make_view(int32_t* base, const flide_meta_layout& L, const flide
   v.seg_branch = base + L.seg_branch;
   v.seg_pos0 = base + L.seg_pos0;
   v.seg_state = base + L.seg_state;
+  v.seg_vcol0 = base + L.seg_vcol0;
   v.req_trunk_row0 = base + L.req_trunk_row0;
   v.req_P = base + L.req_P;
   v.req_m = base + L.req_m;

@@ -34,6 +34,7 @@ flide_status compute_layout(const flide_caps& c, flide_meta_layout& L) {
   L.seg_branch = take(L.seg_cap);
   L.seg_pos0 = take(L.seg_cap);
   L.seg_state = take(L.seg_cap);
+  L.seg_vcol0 = take(L.seg_cap);
   L.req_trunk_row0 = take(c.R_cap);
   L.req_P = take(c.R_cap);
   L.req_m = take(c.R_cap);
@@ -152,6 +153,7 @@ flide_status flide_plan_round(const flide_request* reqs, int32_t R, const flide_
     int32_t* r_qs = img.data() + L.req_q_seg0;
     int32_t* r_nq = img.data() + L.req_nq;
     int32_t* qfin = img.data() + L.qfin_row;
+    int32_t* s_vc = img.data() + L.seg_vcol0;
 
     int32_t row = 0, seg = 0, max_pos = 0;
     // trunk segments: one per request, in request order (possibly empty)
@@ -189,6 +191,18 @@ flide_status flide_plan_round(const flide_request* reqs, int32_t R, const flide_
         row += r.q_len[i];
         qfin[qi++] = row - 1;
         max_pos = std::max(max_pos, r.P + r.q_len[i]);
+      }
+    }
+    // Columns of the transposed value workspace: every segment starts at the
+    // first free column congruent to its first position modulo 8, so value tiles
+    // aligned in position space are 16-byte aligned in memory.
+    {
+      int64_t vend = 0;
+      for (int32_t s = 0; s < seg; ++s) {
+        const int64_t pos0 = s_pos[s];
+        const int64_t vstart = vend + (((pos0 - vend) % 8) + 8) % 8;
+        s_vc[s] = int32_t(vstart - pos0);
+        vend = vstart + s_len[s];
       }
     }
     // Attention work list: tiles of kTileRows rows aligned to each segment's

@@ -45,7 +45,7 @@ class flide_caps(C.Structure):
 class flide_meta_layout(C.Structure):
     _fields_ = [(n, C.c_int64) for n in (
         "host_words", "dev_words", "hdr", "seg_row0", "seg_len", "seg_req", "seg_branch", "seg_pos0",
-        "seg_state", "req_trunk_row0", "req_P", "req_m", "req_ckpt", "req_out", "req_q_seg0", "req_nq",
+        "seg_state", "seg_vcol0", "req_trunk_row0", "req_P", "req_m", "req_ckpt", "req_out", "req_q_seg0", "req_nq",
         "qfin_row", "tile_seg", "tile_row0", "tok_j", "tok_c", "tok_t", "dev_error")] + \
         [("seg_cap", C.c_int32), ("tile_cap", C.c_int32), ("tile_rows", C.c_int32), ("reserved", C.c_int32)]
 
@@ -119,6 +119,12 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    # torch bundles its own HIP runtime; when torch is installed, load it first so
+    # that libflide.so binds to the same runtime instance (one runtime per process).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m tree_forked_hybrid_amd.build` "
                           "(the HIP library is required; there is no fallback path)")
@@ -235,7 +241,7 @@ def decode_image(image: np.ndarray, caps: flide_caps) -> dict:
     hdr = image[L.hdr:L.hdr + 16]
     T, R, n_seg, n_qst, n_tiles = (int(v) for v in hdr[:5])
     out = {"T": T, "R": R, "n_seg": n_seg, "n_qst": n_qst, "n_tiles": n_tiles, "max_pos": int(hdr[5])}
-    for name in ("seg_row0", "seg_len", "seg_req", "seg_branch", "seg_pos0", "seg_state"):
+    for name in ("seg_row0", "seg_len", "seg_req", "seg_branch", "seg_pos0", "seg_state", "seg_vcol0"):
         off = getattr(L, name)
         out[name] = image[off:off + n_seg].copy()
     for name in ("req_trunk_row0", "req_P", "req_m", "req_ckpt", "req_out", "req_q_seg0", "req_nq"):
