@@ -13,14 +13,23 @@
 // chunks of a segment.  Chunks start at multiples of 64 rows from the segment
 // start, so a segment's arithmetic never depends on the rest of the round.
 //
-// Workgroup = (segment, head), 8 waves.  Wave w owns value channels
-// [16w, 16w + 16) and the matching 16 rows of S, which stay in registers for
-// the whole segment in the layout the next chunk's MFMA needs as its B operand.
-// Everything that depends on those channels (K S0^T, Q S0^T, the solve, O and
-// the state update) is wave-local; only the channel-independent pieces (the
-// normalised q/k tiles, A, Gamma (.) QK^T and the 16x16 diagonal inverses of
-// I + A) are shared through LDS.  MFMA operands are fp16 (q, k are unit
-// vectors; the other operands are O(1)), accumulation and the state are fp32.
+// Workgroup = (segment, head), 8 waves, two workgroups per CU.  Wave w owns
+// value channels [16w, 16w + 16) and the matching 16 rows of S, which stay in
+// registers for the whole segment in the layout the next chunk's MFMA needs as
+// its B operand.  Everything that depends on those channels (the values' conv,
+// K S0^T, Q S0^T, the solve, O and the state update) is wave-local; only the
+// channel-independent pieces (the normalised q/k tiles, A, Gamma (.) QK^T and
+// the 16x16 diagonal inverses of I + A) are shared through LDS.  MFMA operands
+// are fp16 (q, k are unit vectors; the other operands are O(1)); accumulation,
+// the inverses and the state are fp32.
+//
+// Per chunk: (1) conv + L2 norm of q and k, one thread per (row quad, 8
+// channels), the row norm summed over 16 lanes with DPP; values convolved by
+// their owner wave straight into the solve's register layout; (2) Gram blocks
+// A = KK^T and QK^T (the latter as hi*hi + hi*lo + lo*hi), K S0^T and Q S0^T,
+// while one wave inverts the diagonal blocks of I + A in fp32; (3) A, P and
+// K^T are written over the q/k lo tiles; (4) blocked forward substitution,
+// outputs and the state update.
 #include "device_common.hpp"
 
 namespace flide {
@@ -34,14 +43,14 @@ namespace {
 typedef _Float16 h4v __attribute__((ext_vector_type(4)));
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
-constexpr int CK = 64;        // chunk rows
-constexpr int DK = 128;       // key size
-constexpr int DV = 128;       // value size (8 waves x 16 channels)
-constexpr int NT = 512;       // threads
-constexpr int QS = DK + 8;    // row stride (halves) of the q/k tiles [t][dk]
-constexpr int TS = CK + 4;    // row stride (halves) of k^T [dk][t] and of A, P [t][s]
-constexpr int DS = 16 + 4;    // row stride (halves) of the diagonal inverses
+constexpr int CK = 64;   // chunk rows
+constexpr int DK = 128;  // key size
+constexpr int DV = 128;  // value size (8 waves x 16 channels)
+constexpr int NT = 512;  // threads
+constexpr int RAW_ROW = 3 * 128 * 2;                      // bytes of one raw row of a head: q | k | v channels
+constexpr int RAW_COPIES = ((CK + 3) * RAW_ROW + 1023) / 1024;  // 1 KB direct-to-LDS copies per chunk tile
 
 __device__ __forceinline__ f4v mma16(h4v a, h4v b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
 __device__ __forceinline__ f4v mma32(h8v a, h8v b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
@@ -51,22 +60,107 @@ __device__ __forceinline__ h8v cat8(h4v a, h4v b) { return h8v{a[0], a[1], a[2],
 __device__ __forceinline__ h4v lds4(const _Float16* p) { return *reinterpret_cast<const h4v*>(p); }
 __device__ __forceinline__ h8v lds8(const _Float16* p) { return *reinterpret_cast<const h8v*>(p); }
 
+// Element offsets (in halves) inside the swizzled LDS tiles.  A [64][128] q/k
+// tile keeps 16-byte chunk c of row t at chunk slot c ^ (t & 15); a [rows][64]
+// tile (A, P, K^T) keeps chunk c of row r at c ^ ((r >> 1) & 7).  Both make the
+// MFMA operand reads (16 rows x 16 or 8 bytes) bank-conflict free.
+__device__ __forceinline__ int qk_off(int t, int c) { return t * DK + ((((c >> 3) ^ (t & 15))) << 3) + (c & 7); }
+__device__ __forceinline__ int sq_off(int r, int c) { return r * CK + ((((c >> 3) ^ ((r >> 1) & 7))) << 3) + (c & 7); }
+
+// sum over the 16 lanes of a DPP row (butterfly: quad swaps, half-row and row mirrors)
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+  return v;
+}
+
 struct ChunkLds {
-  _Float16 q[CK * QS];   // normalised q, fp16 (hi part)
-  _Float16 k[CK * QS];   // normalised k, fp16 (hi part)
-  _Float16 ql[CK * QS];  // q - hi, fp16 (lo part)
-  _Float16 kl[CK * QS];  // k - hi, fp16 (lo part)
-  float v[CK * DV];      // conv'd values [t][channel]
-  _Float16 kt[DK * TS];
-  _Float16 a[CK * TS];   // -A (strictly lower blocks)
-  _Float16 p[CK * TS];   // Gamma (.) QK^T (lower blocks, diagonal included)
-  _Float16 tinv[4 * 16 * DS];
-  float a32[4][16][17];  // diagonal blocks of A in fp32 for the inverse
+  // raw rows c0 - 3 .. c0 + 63 of the head's q, k and v channels (bf16), loaded one chunk ahead
+  unsigned char raw[RAW_COPIES * 1024];
+  _Float16 qh[CK * DK];  // normalised q, fp16 (hi part)
+  _Float16 kh[CK * DK];  // normalised k, fp16 (hi part)
+  _Float16 ql[CK * DK];  // q - hi (lo part); after the Gram products: K^T [dk][t]
+  _Float16 kl[CK * DK];  // k - hi (lo part); after the Gram products: -A [t][s] then P [t][s]
+  float a32[4][16 * 16 + 4];  // diagonal blocks of A in fp32 [t][s] (rows of 16; blocks padded to spread banks)
+  _Float16 tinv[4][16][16];
+  float cw[2][8][16][4];  // q/k conv taps [section][channel % 8][channel / 8][tap], right-aligned (tap 3 = current row)
   float g[CK];
   float eta[CK];
-  float cw[3 * 128][4];   // conv taps of the head's q, k and v channels (right-aligned: tap 3 = current row)
+  float alpha_in[CK];  // alpha and eta of the chunk's rows, loaded one chunk ahead (0 past the segment)
+  float eta_in[CK];
   float glast;
 };
+
+// lower-triangular 16-row block index -> (row block, column block)
+template <int B>
+struct Tri {
+  static constexpr int ti = B >= 6 ? 3 : (B >= 3 ? 2 : (B >= 1 ? 1 : 0));
+  static constexpr int si = B - ti * (ti + 1) / 2;
+};
+
+// Gram block B, transposed: the lane holds row t = 16 ti + r16, columns s = 16 si + 4 g4 + i.
+// P blocks (Q K^T) use hi*hi + lo*hi + hi*lo: q.k of unit vectors can be far smaller than its
+// fp16 rounding error; A blocks (K K^T) use hi*hi.
+template <int B, bool IS_A>
+__device__ __forceinline__ f4v gram_block(const ChunkLds& L, const int (&gq)[4]) {
+  constexpr int rs = 16 * Tri<B>::si * DK, rt = 16 * Tri<B>::ti * DK;
+  f4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const h8v ks_ = lds8(L.kh + rs + gq[c]);
+    if (IS_A) {
+      acc = mma32(ks_, lds8(L.kh + rt + gq[c]), acc);
+    } else {
+      const h8v qt_ = lds8(L.qh + rt + gq[c]);
+      acc = mma32(ks_, qt_, acc);
+      acc = mma32(lds8(L.kl + rs + gq[c]), qt_, acc);
+      acc = mma32(ks_, lds8(L.ql + rt + gq[c]), acc);
+    }
+  }
+  return acc;
+}
+
+// decayed, masked Gram block -> fp16 rows of -A (s < t) or P (s <= t)
+template <int B, bool IS_A>
+__device__ __forceinline__ void gram_store(ChunkLds& L, f4v acc, int r16, int g4, const int (&sql)[4]) {
+  constexpr int ti = Tri<B>::ti, si = Tri<B>::si;
+  const int t = 16 * ti + r16;
+  const float gt = L.g[t], et = L.eta[t];
+  h4v out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = 16 * si + 4 * g4 + i;
+    const float dec = __expf(gt - L.g[s]);
+    out[i] = IS_A ? (_Float16)(s < t ? -(et * dec * acc[i]) : 0.f) : (_Float16)(s <= t ? dec * acc[i] : 0.f);
+  }
+  _Float16* base = IS_A ? L.kl : L.kl + CK * CK;
+  *reinterpret_cast<h4v*>(base + 16 * ti * CK + sql[si]) = out;
+}
+
+// Direct-to-LDS copies for the chunk starting at segment row cc: raw rows cc - 3 .. cc + 63 of the
+// head's q, k and v channels (rows outside the segment read as zero), and (wave 0) alpha, eta of rows
+// cc .. cc + 63.  head_b = byte offset of the head's q channels in a raw row, sect_b = bytes between
+// the q, k and v sections, rowb = bytes per raw row, hstride = bytes between rows of alpha / eta.
+__device__ __forceinline__ void issue_chunk_loads(ChunkLds& L, __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t ar,
+                                                  __amdgpu_buffer_rsrc_t er, int cc, int w, int l, int rowb,
+                                                  int head_b, int sect_b, int hstride) {
+  for (int cp = w; cp < RAW_COPIES; cp += NT / 64) {
+    const int byte = cp * 1024 + 16 * l;
+    const int row = byte / RAW_ROW, col = byte - row * RAW_ROW;
+    const int chb = (col >> 8) * sect_b + head_b + (col & 255);
+    const int voff = row < CK + 3 ? (cc - 3 + row) * rowb + chb : 0x7FFFFFF0;  // past the tile: zero fill
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(L.raw + cp * 1024), 16, voff,
+                                             0, 0, 0);
+  }
+  if (w == 0) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (__attribute__((address_space(3))) void*)L.alpha_in, 4,
+                                             (cc + l) * hstride, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (__attribute__((address_space(3))) void*)L.eta_in, 4,
+                                             (cc + l) * hstride, 0, 0, 0);
+  }
+}
 
 }  // namespace
 
@@ -101,19 +195,15 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
   const int qch = h * DK, kch = H * DK + h * DK, vch = 2 * H * DK + h * DV;
   const int ncol = 16 * w + r16;  // this lane's value channel / state row
 
-  // raw inputs of channels (ch, ch+1) at segment-local row u as one dword of two bf16
-  // (u < 0: conv history; u >= len or before the history: zero).  Branch-free so that
-  // a lane's row loads issue back to back.
-  auto pair = [&](int u, int ch) -> uint32_t {
-    const bool in_x = u >= 0 && u < len;
-    const bool in_h = u < 0 && u >= -(K - 1) && hist != nullptr;
-    const bf16_t* ptr = in_x ? x + int64_t(row0 + u) * C + ch
-                             : (in_h ? hist + int64_t(K - 1 + u) * C + ch : x + int64_t(row0) * C + ch);
-    const uint32_t val = *reinterpret_cast<const uint32_t*>(ptr);
-    return (in_x || in_h) ? val : 0u;
-  };
-  auto lo_f = [](uint32_t v2) { return __uint_as_float(v2 << 16); };
-  auto hi_f = [](uint32_t v2) { return __uint_as_float(v2 & 0xFFFF0000u); };
+  // Raw inputs through buffer resources: the segment's rows [0, len) and the conv history window
+  // (K - 1 rows before the segment).  A row outside either reads as zero (out-of-range buffer
+  // loads return 0; a negative byte offset wraps past the end), which is the conv's zero padding.
+  const int rowb = int(C) * 2;  // bytes per raw row
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(x + int64_t(row0) * C), 0, len * rowb, 0x00020000);
+  const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(hist != nullptr ? hist : x), 0, hist != nullptr ? (K - 1) * rowb : 0, 0x00020000);
+  const int hoff = (K - 1) * rowb;  // byte offset of segment row 0 in the history window's row numbering
 
   // state rows [16w, 16w+16) x dk, lane holds S[ncol][16 mb + 4 g4 + i]
   f4v S[8];
@@ -125,87 +215,86 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) S[mb] = f4v{0.f, 0.f, 0.f, 0.f};
   }
-  // conv lanes: pass 1 waves 0-3 -> q, 4-7 -> k; pass 2 waves 0-3 -> v; lane = channel pair,
-  // wave % 4 = row quarter of the chunk
-  const bool is_k = w >= 4;
-  const int pair_ch = (is_k ? kch : qch) + 2 * l;
-  const int vpair_ch = vch + 2 * l;
-  const int quarter = w & 3;
-  for (int it = tid; it < 3 * 128 * 4; it += NT) {
+  // q/k conv threads: waves 0-3 -> q, 4-7 -> k; row quad rq (rows 4 rq .. 4 rq + 3), channels 8 r16 .. 8 r16 + 7
+  const int sec = w >> 2, rq = (w & 3) * 4 + g4, p8 = 8 * r16;
+  const int qk_ch = (sec ? kch : qch) + p8;
+  for (int it = tid; it < 2 * DK * 4; it += NT) {
     const int ci = it >> 2, tap = it & 3;
-    const int ch = ci < DK ? qch + ci : (ci < 2 * DK ? kch + ci - DK : vch + ci - 2 * DK);
+    const int sc = ci / DK, cc = ci % DK;
     const int tau = tap - (4 - K);
-    L.cw[ci][tap] = tau >= 0 ? conv_w[int64_t(ch) * K + tau] : 0.f;
+    L.cw[sc][cc & 7][cc >> 3][tap] = tau >= 0 ? conv_w[int64_t((sc ? kch : qch) + cc) * K + tau] : 0.f;
   }
-  const int cwq = (is_k ? DK : 0) + 2 * l;  // row of this lane's first q/k channel in L.cw
-  const int cwv = 2 * DK + 2 * l;           // row of this lane's first v channel in L.cw
+  float vw[4];  // this lane's value-channel taps, right-aligned
+#pragma unroll
+  for (int tap = 0; tap < 4; ++tap) {
+    const int tau = tap - (4 - K);
+    vw[tap] = tau >= 0 ? conv_w[int64_t(vch + ncol) * K + tau] : 0.f;
+  }
+  // lane offsets (halves) into the swizzled tiles, for rows 16 x + r16 (add 16 x * row length):
+  // q/k tile, 16-byte operand chunk 4 c + g4
+  int gq[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) gq[c] = r16 * DK + ((((4 * c + g4) ^ r16)) << 3);
+  // q/k tile, 8-byte operands at columns 32 c + 16 hh + 4 g4
+  int kq[4][2];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) kq[c][hh] = r16 * DK + ((((4 * c + 2 * hh + (g4 >> 1)) ^ r16)) << 3) + 4 * (g4 & 1);
+  // [rows][64] tiles, 8-byte operands at columns 16 jb + 4 g4
+  int sql[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) sql[jb] = r16 * CK + ((((2 * jb + (g4 >> 1)) ^ ((r16 >> 1) & 7))) << 3) + 4 * (g4 & 1);
+
+  // The copies of the next chunk are issued once the current chunk's conv is done with the tile; the
+  // first chunk's history rows are patched in at its top.
+  const __amdgpu_buffer_rsrc_t ar =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(alpha + int64_t(row0) * H + h), 0, len > 0 ? ((len - 1) * H + 1) * 4 : 0,
+                                        0x00020000);
+  const __amdgpu_buffer_rsrc_t er =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(eta + int64_t(row0) * H + h), 0, len > 0 ? ((len - 1) * H + 1) * 4 : 0,
+                                        0x00020000);
+  const int head_b = h * DK * 2, sect_b = H * DK * 2;
+  if (len > 0) issue_chunk_loads(L, xr, ar, er, 0, w, l, rowb, head_b, sect_b, H * 4);
+
+  _Float16* const am = L.kl;           // -A [t][s] (strictly lower blocks), after the Gram products
+  _Float16* const pm = L.kl + CK * CK;  // P [t][s] (lower blocks)
+  _Float16* const kt = L.ql;           // K^T [dk][t]
 
   for (int c0 = 0; c0 < len; c0 += CK) {
     const int n = min(CK, len - c0);
-    __syncthreads();  // previous chunk's readers are done with the LDS tiles
-    // ---- conv + L2 norm of q and k -> fp16 hi/lo tiles (pass 1) ----
-    const int t0 = 16 * quarter;
-    for (int half = 0; half < 2; ++half) {
-      const int tb = t0 + 8 * half;
-      uint32_t rr[11];
-#pragma unroll
-      for (int i = 0; i < 11; ++i) rr[i] = pair(c0 + tb - 3 + i, pair_ch);
-      const float4 wa = *reinterpret_cast<const float4*>(L.cw[cwq]);
-      const float4 wb = *reinterpret_cast<const float4*>(L.cw[cwq + 1]);
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const int t = tb + tt;
-        float ya = wa.x * lo_f(rr[tt]) + wa.y * lo_f(rr[tt + 1]) + wa.z * lo_f(rr[tt + 2]) + wa.w * lo_f(rr[tt + 3]);
-        float yb = wb.x * hi_f(rr[tt]) + wb.y * hi_f(rr[tt + 1]) + wb.z * hi_f(rr[tt + 2]) + wb.w * hi_f(rr[tt + 3]);
-        if (act == 1) {
-          ya = ya / (1.f + __expf(-ya));
-          yb = yb / (1.f + __expf(-yb));
-        }
-        const float ss = wave_sum(ya * ya + yb * yb);
-        const float inv = t < n ? rsqrtf(ss + 1e-6f) : 0.f;
-        const float na = ya * inv, nb = yb * inv;
-        const _Float16 ha = (_Float16)na, hb = (_Float16)nb;
-        const _Float16 la = (_Float16)(na - (float)ha), lb = (_Float16)(nb - (float)hb);
-        _Float16* dst = (is_k ? L.k : L.q) + t * QS + 2 * l;
-        _Float16* dsl = (is_k ? L.kl : L.ql) + t * QS + 2 * l;
-        dst[0] = ha;
-        dst[1] = hb;
-        dsl[0] = la;
-        dsl[1] = lb;
-        if (is_k) {
-          L.kt[(2 * l) * TS + t] = ha;
-          L.kt[(2 * l + 1) * TS + t] = hb;
-        }
+    // Lane indices recomputed per chunk from an opaque copy: the per-lane LDS addresses derived from
+    // them below are cheap to rebuild, and keeping them out of the loop preheader keeps them out of
+    // registers across the whole segment.
+    int tid_v = tid;
+    asm volatile("" : "+v"(tid_v));
+    const int l = tid_v & 63, r16 = l & 15, g4 = l >> 4;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's raw-tile copies have landed
+    __syncthreads();                // ... and every wave's; the previous chunk is done with the LDS tiles
+    if (c0 == 0 && hist != nullptr) {
+      // rows -3 .. -1 of the first chunk: the conv history window (K - 1 rows; older rows stay zero)
+      if (tid_v < 3 * RAW_ROW / 16) {
+        const int row = tid_v / (RAW_ROW / 16), col = (tid_v % (RAW_ROW / 16)) * 16;
+        const int chb = (col >> 8) * sect_b + head_b + (col & 255);
+        *reinterpret_cast<u4v*>(L.raw + row * RAW_ROW + col) =
+            __builtin_amdgcn_raw_buffer_load_b128(hr, (row - 3) * rowb + hoff + chb, 0, 0);
       }
+      __syncthreads();
     }
-    // ---- pass 2: values (waves 0-3); decay and step sizes (wave 4) ----
-    if (w < 4) {
-     for (int half = 0; half < 2; ++half) {
-      const int tb = t0 + 8 * half;
-      uint32_t rr[11];
+    uint32_t vraw[4][7];  // bf16 bits of this lane's value channel at tile rows 16 rb + 4 g4 + i
 #pragma unroll
-      for (int i = 0; i < 11; ++i) rr[i] = pair(c0 + tb - 3 + i, vpair_ch);
-      const float4 wa = *reinterpret_cast<const float4*>(L.cw[cwv]);
-      const float4 wb = *reinterpret_cast<const float4*>(L.cw[cwv + 1]);
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const int t = tb + tt;
-        float ya = wa.x * lo_f(rr[tt]) + wa.y * lo_f(rr[tt + 1]) + wa.z * lo_f(rr[tt + 2]) + wa.w * lo_f(rr[tt + 3]);
-        float yb = wb.x * hi_f(rr[tt]) + wb.y * hi_f(rr[tt + 1]) + wb.z * hi_f(rr[tt + 2]) + wb.w * hi_f(rr[tt + 3]);
-        if (act == 1) {
-          ya = ya / (1.f + __expf(-ya));
-          yb = yb / (1.f + __expf(-yb));
-        }
-        L.v[t * DV + 2 * l] = t < n ? ya : 0.f;
-        L.v[t * DV + 2 * l + 1] = t < n ? yb : 0.f;
-      }
-     }
-    } else if (w == 4) {
+      for (int i = 0; i < 7; ++i)
+        vraw[rb][i] = *reinterpret_cast<const unsigned short*>(L.raw + (16 * rb + 4 * g4 + i) * RAW_ROW + 512 + 2 * ncol);
+    u4v raw[7];  // this thread's q/k row window (8 channels) at tile rows 4 rq + i
+#pragma unroll
+    for (int i = 0; i < 7; ++i) raw[i] = *reinterpret_cast<const u4v*>(L.raw + (4 * rq + i) * RAW_ROW + sec * 256 + 2 * p8);
+    if (w == 0) {
       // g = inclusive prefix sum of log alpha over the chunk
       const int t = l;
-      const float a = t < n ? alpha[int64_t(row0 + c0 + t) * H + h] : 1.f;
-      const float e = t < n ? eta[int64_t(row0 + c0 + t) * H + h] : 0.f;
-      float gsum = __logf(a);
+      const float e = t < n ? L.eta_in[t] : 0.f;
+      float gsum = t < n ? __logf(L.alpha_in[t]) : 0.f;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float up = __shfl_up(gsum, off, 64);
@@ -215,93 +304,157 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
       L.eta[t] = e;
       if (t == n - 1) L.glast = gsum;
     }
-    __syncthreads();
-    // ---- shared products: A = eta_t e^{g_t-g_s} k_t.k_s (s < t), P = e^{g_t-g_s} q_t.k_s (s <= t) ----
-    for (int task = w; task < 20; task += 8) {
-      const bool isq = task >= 10;
-      int blk = isq ? task - 10 : task;  // lower-triangular block index -> (ti, si)
-      int ti = 0;
-      while (blk > ti) {
-        blk -= ti + 1;
-        ++ti;
+    // ---- values of this lane's channel at rows 16 rb + 4 g4 + i (the solve's layout) ----
+    f4v vv[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        auto xv = [&](int k) { return __uint_as_float(vraw[rb][k] << 16); };
+        float acc = vw[0] * xv(i) + vw[1] * xv(i + 1) + vw[2] * xv(i + 2) + vw[3] * xv(i + 3);
+        if (act == 1) acc = acc / (1.f + __expf(-acc));
+        vv[rb][i] = acc;
       }
-      const int si = blk;
-      const int oa = (16 * ti + r16) * QS + 8 * g4, ob = (16 * si + r16) * QS + 8 * g4;
-      f4v acc = {0.f, 0.f, 0.f, 0.f};
-      if (isq) {
-        // q.k of unit vectors can be far smaller than its rounding error in fp16: hi*hi + hi*lo + lo*hi
+    // ---- conv + L2 norm of q and k -> fp16 hi/lo tiles ----
+    {
+      _Float16* th = sec ? L.kh : L.qh;
+      _Float16* tl = sec ? L.kl : L.ql;
+#pragma unroll
+      for (int jr = 0; jr < 4; ++jr) {
+        const int t = 4 * rq + jr;
+        float y[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float4 wt = *reinterpret_cast<const float4*>(L.cw[sec][c][r16]);
+          const int hw = c >> 1;
+          auto xv = [&](int i) {
+            const uint32_t wv = raw[i][hw];
+            return (c & 1) ? __uint_as_float(wv & 0xFFFF0000u) : __uint_as_float(wv << 16);
+          };
+          float acc = wt.x * xv(jr) + wt.y * xv(jr + 1) + wt.z * xv(jr + 2) + wt.w * xv(jr + 3);
+          if (act == 1) acc = acc / (1.f + __expf(-acc));
+          y[c] = acc;
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) ss += y[c] * y[c];
+        ss = row16_sum(ss);
+        const float inv = t < n ? rsqrtf(ss + 1e-6f) : 0.f;
+        h8v hv, lv;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float nv = y[c] * inv;
+          const _Float16 hi = (_Float16)nv;
+          hv[c] = hi;
+          lv[c] = (_Float16)(nv - (float)hi);
+        }
+        const int wo = t * DK + ((r16 ^ (4 * g4 + jr)) << 3);
+        *reinterpret_cast<h8v*>(th + wo) = hv;
+        *reinterpret_cast<h8v*>(tl + wo) = lv;
+      }
+    }
+    __syncthreads();
+    if (c0 + CK < len) issue_chunk_loads(L, xr, ar, er, c0 + CK, w, l, rowb, head_b, sect_b, H * 4);
+    // ---- Gram blocks, held in registers until every wave is done with the lo tiles.  Waves 0-6 take
+    // the P blocks and the strictly lower A blocks; wave 7 the diagonal A blocks and their inverses ----
+    f4v gres[3];
+    switch (w) {
+      case 0: gres[0] = gram_block<0, false>(L, gq); gres[1] = gram_block<7, false>(L, gq); break;
+      case 1: gres[0] = gram_block<1, false>(L, gq); gres[1] = gram_block<8, false>(L, gq); break;
+      case 2: gres[0] = gram_block<2, false>(L, gq); gres[1] = gram_block<9, false>(L, gq); break;
+      case 3: gres[0] = gram_block<3, false>(L, gq); gres[1] = gram_block<1, true>(L, gq);
+              gres[2] = gram_block<3, true>(L, gq); break;
+      case 4: gres[0] = gram_block<4, false>(L, gq); gres[1] = gram_block<4, true>(L, gq);
+              gres[2] = gram_block<6, true>(L, gq); break;
+      case 5: gres[0] = gram_block<5, false>(L, gq); gres[1] = gram_block<7, true>(L, gq); break;
+      case 6: gres[0] = gram_block<6, false>(L, gq); gres[1] = gram_block<8, true>(L, gq); break;
+      default: break;
+    }
+    if (w == 7) {
+      // diagonal blocks of A in fp32 ...
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        f4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const h8v qh = lds8(L.q + oa + 32 * c), kh = lds8(L.k + ob + 32 * c);
-          acc = mma32(qh, kh, acc);
-          acc = mma32(qh, lds8(L.kl + ob + 32 * c), acc);
-          acc = mma32(lds8(L.ql + oa + 32 * c), kh, acc);
+          const h8v kb = lds8(L.kh + 16 * b * DK + gq[c]);
+          acc = mma32(kb, kb, acc);
         }
-      } else {
+        const int t = 16 * b + r16;
+        const float gt = L.g[t], et = L.eta[t];
+        f4v av;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc = mma32(lds8(L.k + oa + 32 * c), lds8(L.k + ob + 32 * c), acc);
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * b + 4 * g4 + i;
+          av[i] = s < t ? et * __expf(gt - L.g[s]) * acc[i] : 0.f;
+        }
+        *reinterpret_cast<f4v*>(&L.a32[b][r16 * 16 + 4 * g4]) = av;
       }
-      const int s = 16 * si + r16;
-      const float gs = L.g[s];
+    }
+    // ---- K S0^T and Q S0^T for this wave's channels, and the solve's right-hand side ----
+    h8v sf[4];  // S as the B operand (k-slots permuted to match the register layout)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sf[c] = cat8(to_h4(S[2 * c]), to_h4(S[2 * c + 1]));
+    f4v qs[4], rhs[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      f4v ks = {0.f, 0.f, 0.f, 0.f};
+      qs[rb] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        ks = mma32(cat8(lds4(L.kh + 16 * rb * DK + kq[c][0]), lds4(L.kh + 16 * rb * DK + kq[c][1])), sf[c], ks);
+        qs[rb] = mma32(cat8(lds4(L.qh + 16 * rb * DK + kq[c][0]), lds4(L.qh + 16 * rb * DK + kq[c][1])), sf[c], qs[rb]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = 16 * ti + 4 * g4 + i;
-        const float dec = __expf(L.g[t] - gs);
-        if (isq) {
-          L.p[t * TS + s] = (_Float16)(s <= t ? dec * acc[i] : 0.f);
-        } else {
-          const float av = s < t ? L.eta[t] * dec * acc[i] : 0.f;
-          L.a[t * TS + s] = (_Float16)(-av);
-          if (ti == si) L.a32[ti][4 * g4 + i][r16] = av;
+        const int tr = 16 * rb + 4 * g4 + i;
+        rhs[rb][i] = L.eta[tr] * (vv[rb][i] - __expf(L.g[tr]) * ks[i]);
+      }
+    }
+    __syncthreads();  // every wave is done with the lo tiles; the diagonal blocks of A are in LDS
+    // ---- -A, P and K^T over the lo tiles; the diagonal inverses ----
+    if (w == 7) {
+      // T_bb = (I + A_bb)^{-1} by forward substitution, lane = 16 b + column
+      const int b = g4, col = r16;
+      float tc[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float acc[4] = {r == col ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j4 = 0; j4 < (r + 3) / 4; ++j4) {
+          const f4v a4 = *reinterpret_cast<const f4v*>(&L.a32[b][r * 16 + 4 * j4]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * j4 + i < r) acc[i] -= a4[i] * tc[4 * j4 + i];
         }
+        tc[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        if ((r & 3) == 3) asm volatile("" ::: "memory");  // bound how far the row reads are hoisted
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) L.tinv[b][r][col] = (_Float16)tc[r];
+    }
+    switch (w) {
+      case 0: gram_store<0, false>(L, gres[0], r16, g4, sql); gram_store<7, false>(L, gres[1], r16, g4, sql); break;
+      case 1: gram_store<1, false>(L, gres[0], r16, g4, sql); gram_store<8, false>(L, gres[1], r16, g4, sql); break;
+      case 2: gram_store<2, false>(L, gres[0], r16, g4, sql); gram_store<9, false>(L, gres[1], r16, g4, sql); break;
+      case 3: gram_store<3, false>(L, gres[0], r16, g4, sql); gram_store<1, true>(L, gres[1], r16, g4, sql);
+              gram_store<3, true>(L, gres[2], r16, g4, sql); break;
+      case 4: gram_store<4, false>(L, gres[0], r16, g4, sql); gram_store<4, true>(L, gres[1], r16, g4, sql);
+              gram_store<6, true>(L, gres[2], r16, g4, sql); break;
+      case 5: gram_store<5, false>(L, gres[0], r16, g4, sql); gram_store<7, true>(L, gres[1], r16, g4, sql); break;
+      case 6: gram_store<6, false>(L, gres[0], r16, g4, sql); gram_store<8, true>(L, gres[1], r16, g4, sql); break;
+      default: break;
+    }
+    {
+      const int dk = tid_v & 127, tq = tid_v >> 7;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int t0 = 16 * tq + 4 * jj;
+        const h4v v = {L.kh[qk_off(t0, dk)], L.kh[qk_off(t0 + 1, dk)], L.kh[qk_off(t0 + 2, dk)], L.kh[qk_off(t0 + 3, dk)]};
+        *reinterpret_cast<h4v*>(kt + sq_off(dk, t0)) = v;
       }
     }
     __syncthreads();
-    // ---- diagonal inverses T_bb = (I + A_bb)^{-1} by forward substitution (waves 0-3) ----
-    if (w < 4) {
-      const int b = w, col = r16, part = g4;
-      float tv[4] = {0.f, 0.f, 0.f, 0.f};  // T[part + 4k][col]
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int jj = part + 4 * kk;
-          if (jj < r) acc += L.a32[b][r][jj] * tv[kk];
-        }
-        acc += __shfl_xor(acc, 16, 64);
-        acc += __shfl_xor(acc, 32, 64);
-        const float trc = (r == col ? 1.f : 0.f) - acc;
-        if ((r & 3) == part) tv[r >> 2] = trc;
-        if (part == 0) L.tinv[(b * 16 + r) * DS + col] = (_Float16)trc;
-      }
-    }
-    // ---- wave-local, channel-dependent work part 1 (no dependency on the inverses) ----
-    h8v sf[4];  // S as the B operand of K S^T / Q S^T (k-slots permuted to match the register layout)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) sf[c] = cat8(to_h4(S[2 * c]), to_h4(S[2 * c + 1]));
-    f4v ks[4], qs[4], rhs[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      ks[rb] = f4v{0.f, 0.f, 0.f, 0.f};
-      qs[rb] = f4v{0.f, 0.f, 0.f, 0.f};
-      const _Float16* kr = L.k + (16 * rb + r16) * QS + 4 * g4;
-      const _Float16* qr = L.q + (16 * rb + r16) * QS + 4 * g4;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        ks[rb] = mma32(cat8(lds4(kr + 32 * c), lds4(kr + 32 * c + 16)), sf[c], ks[rb]);
-        qs[rb] = mma32(cat8(lds4(qr + 32 * c), lds4(qr + 32 * c + 16)), sf[c], qs[rb]);
-      }
-      // values of this lane's channel (conv) and the right-hand side
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * rb + 4 * g4 + i;
-        const float vv = L.v[t * DV + ncol];
-        const float e = L.eta[t];
-        rhs[rb][i] = e * (vv - __expf(L.g[t]) * ks[rb][i]);
-      }
-    }
-    __syncthreads();  // diagonal inverses ready
     // ---- blocked forward substitution U = (I + A)^{-1} RHS ----
     h4v uh[4];
     f4v u[4];
@@ -309,8 +462,8 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
     for (int rb = 0; rb < 4; ++rb) {
       f4v acc = rhs[rb];
 #pragma unroll
-      for (int jb = 0; jb < rb; ++jb) acc = mma16(lds4(L.a + (16 * rb + r16) * TS + 16 * jb + 4 * g4), uh[jb], acc);
-      u[rb] = mma16(lds4(L.tinv + (rb * 16 + r16) * DS + 4 * g4), to_h4(acc), f4v{0.f, 0.f, 0.f, 0.f});
+      for (int jb = 0; jb < rb; ++jb) acc = mma16(lds4(am + 16 * rb * CK + sql[jb]), uh[jb], acc);
+      u[rb] = mma16(lds4(&L.tinv[rb][r16][4 * g4]), to_h4(acc), f4v{0.f, 0.f, 0.f, 0.f});
       uh[rb] = to_h4(u[rb]);
     }
     // ---- outputs O = e^g Q S0^T + P U ----
@@ -320,7 +473,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = __expf(L.g[16 * rb + 4 * g4 + i]) * qs[rb][i];
 #pragma unroll
-      for (int jb = 0; jb <= rb; ++jb) acc = mma16(lds4(L.p + (16 * rb + r16) * TS + 16 * jb + 4 * g4), uh[jb], acc);
+      for (int jb = 0; jb <= rb; ++jb) acc = mma16(lds4(pm + 16 * rb * CK + sql[jb]), uh[jb], acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * rb + 4 * g4 + i;
@@ -345,7 +498,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
     for (int mb = 0; mb < 8; ++mb) {
       f4v acc = S[mb] * egl;
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) acc = mma16(lds4(L.kt + (16 * mb + r16) * TS + 16 * rb + 4 * g4), ud[rb], acc);
+      for (int rb = 0; rb < 4; ++rb) acc = mma16(lds4(kt + 16 * mb * CK + sql[rb]), ud[rb], acc);
       S[mb] = acc;
     }
   }
@@ -376,7 +529,9 @@ bool gdn_uses_chunk(const flide_gdn_params& p) { return p.dtype == FLIDE_BF16 &&
 int launch_gdn(const MetaView& mv, const flide_gdn_params& p, int phase, const void* x, const float* conv_w,
                const float* alpha, const float* eta, float* state_pool, void* conv_pool, int32_t n_slots, void* o,
                void* stream) {
-  if (!gdn_uses_chunk(p))
+  // the chunk kernel addresses a segment's raw rows with 32-bit buffer offsets
+  const bool offsets_fit = int64_t(mv.T_cap + CK) * p.H * (2 * DK + DV) * 2 < (int64_t(1) << 31);
+  if (!gdn_uses_chunk(p) || !offsets_fit)
     return launch_gdn_plain(mv, p, phase, x, conv_w, alpha, eta, state_pool, conv_pool, n_slots, o, stream);
   dim3 grid(phase == 0 ? mv.R_cap : (mv.Q_cap > 0 ? mv.Q_cap : 1), p.H);
   hipLaunchKernelGGL(gdn_chunk_kernel, grid, dim3(NT), 0, (hipStream_t)stream, mv, phase, p.H, p.conv_k, p.act,
