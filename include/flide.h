@@ -112,6 +112,8 @@ typedef struct {
  *   qfin_row    [Q_cap]    last stream row of every question (stream order)
  *   tile_seg    [tile_cap] attention work list: segment of each tile
  *   tile_row0   [tile_cap]                      first stream row of each tile
+ *   gdn_order   [seg_cap]  GDN work list: trunk segments, then question segments,
+ *                          each by length, longest first (ties in stream order)
  *   tok_j/c/t   [T_cap]    per-row metadata (device only)
  *   dev_error   [4]        device error word (device only)                     */
 typedef struct {
@@ -122,6 +124,7 @@ typedef struct {
   int64_t req_trunk_row0, req_P, req_m, req_ckpt, req_out, req_q_seg0, req_nq;
   int64_t qfin_row;
   int64_t tile_seg, tile_row0;
+  int64_t gdn_order;
   int64_t tok_j, tok_c, tok_t;
   int64_t dev_error;
   int32_t seg_cap;

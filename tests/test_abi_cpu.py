@@ -71,6 +71,15 @@ def _assert_same_layout(reqs, caps):
         n = min(32, ref["seg_len"][s] - a)
         cover[r0:r0 + n] += 1
     assert (cover == 1).all()
+    # the GDN work list: trunks then questions, each a permutation ordered by length (longest first,
+    # ties in stream order)
+    R, n_seg = ref["R"], ref["n_seg"]
+    order = got["gdn_order"]
+    for lo, hi in ((0, R), (R, n_seg)):
+        part = order[lo:hi]
+        np.testing.assert_array_equal(np.sort(part), np.arange(lo, hi))
+        keys = [(-int(ref["seg_len"][s]), int(s)) for s in part]
+        assert keys == sorted(keys)
     return got
 
 

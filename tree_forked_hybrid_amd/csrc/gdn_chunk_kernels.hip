@@ -76,22 +76,31 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Targets of the direct-to-LDS copies, kept apart from the tiles so that the compiler can tell that
+// no tile access touches them while copies are in flight.
+struct ChunkIn {
+  unsigned char raw[RAW_COPIES * 1024];  // raw rows c0 - 3 .. c0 + 63 of the head's q, k and v channels (bf16)
+  float alpha[CK];                       // alpha and eta of the chunk's rows (0 past the segment)
+  float eta[CK];
+};
+
 struct ChunkLds {
-  // raw rows c0 - 3 .. c0 + 63 of the head's q, k and v channels (bf16), loaded one chunk ahead
-  unsigned char raw[RAW_COPIES * 1024];
   _Float16 qh[CK * DK];  // normalised q, fp16 (hi part)
   _Float16 kh[CK * DK];  // normalised k, fp16 (hi part)
   _Float16 ql[CK * DK];  // q - hi (lo part); after the Gram products: K^T [dk][t]
   _Float16 kl[CK * DK];  // k - hi (lo part); after the Gram products: -A [t][s] then P [t][s]
-  float a32[4][16 * 16 + 4];  // diagonal blocks of A in fp32 [t][s] (rows of 16; blocks padded to spread banks)
   _Float16 tinv[4][16][16];
   float cw[2][8][16][4];  // q/k conv taps [section][channel % 8][channel / 8][tap], right-aligned (tap 3 = current row)
   float g[CK];
   float eta[CK];
-  float alpha_in[CK];  // alpha and eta of the chunk's rows, loaded one chunk ahead (0 past the segment)
-  float eta_in[CK];
   float glast;
 };
+
+// Workgroup barrier that orders LDS only: unlike __syncthreads() it does not wait for this wave's
+// outstanding global loads, so the next chunk's direct-to-LDS copies stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.f + __expf(-v)); }
 
 // lower-triangular 16-row block index -> (row block, column block)
 template <int B>
@@ -139,26 +148,81 @@ __device__ __forceinline__ void gram_store(ChunkLds& L, f4v acc, int r16, int g4
   *reinterpret_cast<h4v*>(base + 16 * ti * CK + sql[si]) = out;
 }
 
+// One direct-to-LDS buffer load per lane of `bytes` (4 or 16) into the wave-uniform LDS address dst
+// (lane i fills dst + bytes * i).  Written as inline asm so that the compiler does not track it: it
+// would otherwise make every later LDS access it cannot tell apart from dst wait for the copy, while
+// the kernel waits for the copies explicitly, one chunk later.  M0 is written here and used by
+// nothing else in this kernel; the nops cover the SGPR-write and M0-write hazards.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 in the clobber list is intended
+template <int BYTES>
+__device__ __forceinline__ void lds_copy(__amdgpu_buffer_rsrc_t r, void* dst, int voff) {
+  const unsigned a = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)dst);
+  if (BYTES == 16)
+    asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :: "v"(voff), "s"(a), "s"(r) : "memory", "m0");
+  else
+    asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 1\n\tbuffer_load_dword %0, %2, 0 offen lds"
+                 :: "v"(voff), "s"(a), "s"(r) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Direct-to-LDS copies for the chunk starting at segment row cc: raw rows cc - 3 .. cc + 63 of the
 // head's q, k and v channels (rows outside the segment read as zero), and (wave 0) alpha, eta of rows
 // cc .. cc + 63.  head_b = byte offset of the head's q channels in a raw row, sect_b = bytes between
 // the q, k and v sections, rowb = bytes per raw row, hstride = bytes between rows of alpha / eta.
-__device__ __forceinline__ void issue_chunk_loads(ChunkLds& L, __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t ar,
+__device__ __forceinline__ void issue_chunk_loads(ChunkIn& I, __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t ar,
                                                   __amdgpu_buffer_rsrc_t er, int cc, int w, int l, int rowb,
                                                   int head_b, int sect_b, int hstride) {
+  if (w == 0) {
+    lds_copy<4>(ar, I.alpha, (cc + l) * hstride);
+    lds_copy<4>(er, I.eta, (cc + l) * hstride);
+  }
   for (int cp = w; cp < RAW_COPIES; cp += NT / 64) {
     const int byte = cp * 1024 + 16 * l;
     const int row = byte / RAW_ROW, col = byte - row * RAW_ROW;
     const int chb = (col >> 8) * sect_b + head_b + (col & 255);
     const int voff = row < CK + 3 ? (cc - 3 + row) * rowb + chb : 0x7FFFFFF0;  // past the tile: zero fill
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(L.raw + cp * 1024), 16, voff,
-                                             0, 0, 0);
+    lds_copy<16>(xr, I.raw + cp * 1024, voff);
   }
-  if (w == 0) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (__attribute__((address_space(3))) void*)L.alpha_in, 4,
-                                             (cc + l) * hstride, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (__attribute__((address_space(3))) void*)L.eta_in, 4,
-                                             (cc + l) * hstride, 0, 0, 0);
+}
+
+// Diagonal block b of A (fp32, from the hi tiles) and T_bb = (I + A_bb)^{-1} by forward
+// substitution, one column per lane (lanes 16 .. 63 repeat lanes 0 .. 15).  A_bb[r][j] lives in
+// lane r + 16 (j / 4), register j % 4, and reaches every lane through a lane shuffle; none of these
+// loads waits on the running column, so they issue ahead of the substitution chain.
+template <int B>
+__device__ __forceinline__ void diag_inverse(ChunkLds& L, const int (&gq)[4], int r16, int g4) {
+  f4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const h8v kb = lds8(L.kh + 16 * B * DK + gq[c]);
+    acc = mma32(kb, kb, acc);
+  }
+  const int t = 16 * B + r16;
+  const float gt = L.g[t], et = L.eta[t];
+  float av[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = 16 * B + 4 * g4 + i;
+    av[i] = s < t ? et * __expf(gt - L.g[s]) * acc[i] : 0.f;
+  }
+  const int col = r16;
+  float tc[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float part[4] = {r == col ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < r; ++jj) {
+      const float a = __shfl(av[jj & 3], r + 16 * (jj >> 2), 64);
+      part[jj & 3] -= a * tc[jj];
+    }
+    tc[r] = (part[0] + part[1]) + (part[2] + part[3]);
+  }
+  if (g4 == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) L.tinv[B][r][col] = (_Float16)tc[r];
   }
 }
 
@@ -171,15 +235,18 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
                                                        bf16_t* __restrict__ conv_pool, int n_slots,
                                                        bf16_t* __restrict__ o) {
   __shared__ ChunkLds L;
-  const int item = blockIdx.x, h = blockIdx.y;
+  __shared__ ChunkIn I;
+  // workgroups are dispatched in linear order: rank = position in the longest-first work list
+  const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+  const int item = lin / H, h = lin % H;
   const int R = mv.hdr[H_R];
   int seg;
   if (phase == 0) {
     if (item >= R) return;
-    seg = item;
+    seg = mv.gdn_order[item];
   } else {
     if (item >= mv.hdr[H_NQST]) return;
-    seg = R + item;
+    seg = mv.gdn_order[R + item];
   }
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g4 = l >> 4;
   const int64_t C = int64_t(H) * (2 * DK + DV);
@@ -217,7 +284,6 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
   }
   // q/k conv threads: waves 0-3 -> q, 4-7 -> k; row quad rq (rows 4 rq .. 4 rq + 3), channels 8 r16 .. 8 r16 + 7
   const int sec = w >> 2, rq = (w & 3) * 4 + g4, p8 = 8 * r16;
-  const int qk_ch = (sec ? kch : qch) + p8;
   for (int it = tid; it < 2 * DK * 4; it += NT) {
     const int ci = it >> 2, tap = it & 3;
     const int sc = ci / DK, cc = ci % DK;
@@ -255,7 +321,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
       __builtin_amdgcn_make_buffer_rsrc((void*)(eta + int64_t(row0) * H + h), 0, len > 0 ? ((len - 1) * H + 1) * 4 : 0,
                                         0x00020000);
   const int head_b = h * DK * 2, sect_b = H * DK * 2;
-  if (len > 0) issue_chunk_loads(L, xr, ar, er, 0, w, l, rowb, head_b, sect_b, H * 4);
+  if (len > 0) issue_chunk_loads(I, xr, ar, er, 0, w, l, rowb, head_b, sect_b, H * 4);
 
   _Float16* const am = L.kl;           // -A [t][s] (strictly lower blocks), after the Gram products
   _Float16* const pm = L.kl + CK * CK;  // P [t][s] (lower blocks)
@@ -269,32 +335,32 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
     int tid_v = tid;
     asm volatile("" : "+v"(tid_v));
     const int l = tid_v & 63, r16 = l & 15, g4 = l >> 4;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's raw-tile copies have landed
-    __syncthreads();                // ... and every wave's; the previous chunk is done with the LDS tiles
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
+    lds_barrier();                  // ... and every wave's; the previous chunk is done with the LDS tiles
     if (c0 == 0 && hist != nullptr) {
       // rows -3 .. -1 of the first chunk: the conv history window (K - 1 rows; older rows stay zero)
       if (tid_v < 3 * RAW_ROW / 16) {
         const int row = tid_v / (RAW_ROW / 16), col = (tid_v % (RAW_ROW / 16)) * 16;
         const int chb = (col >> 8) * sect_b + head_b + (col & 255);
-        *reinterpret_cast<u4v*>(L.raw + row * RAW_ROW + col) =
+        *reinterpret_cast<u4v*>(I.raw + row * RAW_ROW + col) =
             __builtin_amdgcn_raw_buffer_load_b128(hr, (row - 3) * rowb + hoff + chb, 0, 0);
       }
-      __syncthreads();
+      lds_barrier();
     }
     uint32_t vraw[4][7];  // bf16 bits of this lane's value channel at tile rows 16 rb + 4 g4 + i
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int i = 0; i < 7; ++i)
-        vraw[rb][i] = *reinterpret_cast<const unsigned short*>(L.raw + (16 * rb + 4 * g4 + i) * RAW_ROW + 512 + 2 * ncol);
+        vraw[rb][i] = *reinterpret_cast<const unsigned short*>(I.raw + (16 * rb + 4 * g4 + i) * RAW_ROW + 512 + 2 * ncol);
     u4v raw[7];  // this thread's q/k row window (8 channels) at tile rows 4 rq + i
 #pragma unroll
-    for (int i = 0; i < 7; ++i) raw[i] = *reinterpret_cast<const u4v*>(L.raw + (4 * rq + i) * RAW_ROW + sec * 256 + 2 * p8);
+    for (int i = 0; i < 7; ++i) raw[i] = *reinterpret_cast<const u4v*>(I.raw + (4 * rq + i) * RAW_ROW + sec * 256 + 2 * p8);
     if (w == 0) {
       // g = inclusive prefix sum of log alpha over the chunk
       const int t = l;
-      const float e = t < n ? L.eta_in[t] : 0.f;
-      float gsum = t < n ? __logf(L.alpha_in[t]) : 0.f;
+      const float e = t < n ? I.eta[t] : 0.f;
+      float gsum = t < n ? __logf(I.alpha[t]) : 0.f;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float up = __shfl_up(gsum, off, 64);
@@ -312,27 +378,30 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
       for (int i = 0; i < 4; ++i) {
         auto xv = [&](int k) { return __uint_as_float(vraw[rb][k] << 16); };
         float acc = vw[0] * xv(i) + vw[1] * xv(i + 1) + vw[2] * xv(i + 2) + vw[3] * xv(i + 3);
-        if (act == 1) acc = acc / (1.f + __expf(-acc));
+        if (act == 1) acc = silu(acc);
         vv[rb][i] = acc;
       }
     // ---- conv + L2 norm of q and k -> fp16 hi/lo tiles ----
     {
       _Float16* th = sec ? L.kh : L.qh;
       _Float16* tl = sec ? L.kl : L.ql;
+      float4 wt4[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) wt4[c] = *reinterpret_cast<const float4*>(L.cw[sec][c][r16]);
 #pragma unroll
       for (int jr = 0; jr < 4; ++jr) {
         const int t = 4 * rq + jr;
         float y[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          const float4 wt = *reinterpret_cast<const float4*>(L.cw[sec][c][r16]);
+          const float4 wt = wt4[c];
           const int hw = c >> 1;
           auto xv = [&](int i) {
             const uint32_t wv = raw[i][hw];
             return (c & 1) ? __uint_as_float(wv & 0xFFFF0000u) : __uint_as_float(wv << 16);
           };
           float acc = wt.x * xv(jr) + wt.y * xv(jr + 1) + wt.z * xv(jr + 2) + wt.w * xv(jr + 3);
-          if (act == 1) acc = acc / (1.f + __expf(-acc));
+          if (act == 1) acc = silu(acc);
           y[c] = acc;
         }
         float ss = 0.f;
@@ -353,43 +422,22 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
         *reinterpret_cast<h8v*>(tl + wo) = lv;
       }
     }
-    __syncthreads();
-    if (c0 + CK < len) issue_chunk_loads(L, xr, ar, er, c0 + CK, w, l, rowb, head_b, sect_b, H * 4);
+    lds_barrier();
+    if (c0 + CK < len) issue_chunk_loads(I, xr, ar, er, c0 + CK, w, l, rowb, head_b, sect_b, H * 4);
     // ---- Gram blocks, held in registers until every wave is done with the lo tiles.  Waves 0-6 take
     // the P blocks and the strictly lower A blocks; wave 7 the diagonal A blocks and their inverses ----
     f4v gres[3];
     switch (w) {
-      case 0: gres[0] = gram_block<0, false>(L, gq); gres[1] = gram_block<7, false>(L, gq); break;
-      case 1: gres[0] = gram_block<1, false>(L, gq); gres[1] = gram_block<8, false>(L, gq); break;
-      case 2: gres[0] = gram_block<2, false>(L, gq); gres[1] = gram_block<9, false>(L, gq); break;
-      case 3: gres[0] = gram_block<3, false>(L, gq); gres[1] = gram_block<1, true>(L, gq);
-              gres[2] = gram_block<3, true>(L, gq); break;
-      case 4: gres[0] = gram_block<4, false>(L, gq); gres[1] = gram_block<4, true>(L, gq);
-              gres[2] = gram_block<6, true>(L, gq); break;
-      case 5: gres[0] = gram_block<5, false>(L, gq); gres[1] = gram_block<7, true>(L, gq); break;
-      case 6: gres[0] = gram_block<6, false>(L, gq); gres[1] = gram_block<8, true>(L, gq); break;
-      default: break;
-    }
-    if (w == 7) {
-      // diagonal blocks of A in fp32 ...
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        f4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const h8v kb = lds8(L.kh + 16 * b * DK + gq[c]);
-          acc = mma32(kb, kb, acc);
-        }
-        const int t = 16 * b + r16;
-        const float gt = L.g[t], et = L.eta[t];
-        f4v av;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = 16 * b + 4 * g4 + i;
-          av[i] = s < t ? et * __expf(gt - L.g[s]) * acc[i] : 0.f;
-        }
-        *reinterpret_cast<f4v*>(&L.a32[b][r16 * 16 + 4 * g4]) = av;
-      }
+      case 0: gres[0] = gram_block<0, false>(L, gq); gres[1] = gram_block<4, false>(L, gq); break;
+      case 1: gres[0] = gram_block<1, false>(L, gq); gres[1] = gram_block<5, false>(L, gq); break;
+      case 2: gres[0] = gram_block<2, false>(L, gq); gres[1] = gram_block<6, false>(L, gq); break;
+      case 3: gres[0] = gram_block<3, false>(L, gq); gres[1] = gram_block<7, false>(L, gq); break;
+      case 4: gres[0] = gram_block<8, false>(L, gq); diag_inverse<0>(L, gq, r16, g4); break;
+      case 5: gres[0] = gram_block<9, false>(L, gq); diag_inverse<1>(L, gq, r16, g4); break;
+      case 6: gres[0] = gram_block<1, true>(L, gq); gres[1] = gram_block<3, true>(L, gq);
+              gres[2] = gram_block<4, true>(L, gq); diag_inverse<2>(L, gq, r16, g4); break;
+      default: gres[0] = gram_block<6, true>(L, gq); gres[1] = gram_block<7, true>(L, gq);
+               gres[2] = gram_block<8, true>(L, gq); diag_inverse<3>(L, gq, r16, g4); break;
     }
     // ---- K S0^T and Q S0^T for this wave's channels, and the solve's right-hand side ----
     h8v sf[4];  // S as the B operand (k-slots permuted to match the register layout)
@@ -411,39 +459,19 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
         rhs[rb][i] = L.eta[tr] * (vv[rb][i] - __expf(L.g[tr]) * ks[i]);
       }
     }
-    __syncthreads();  // every wave is done with the lo tiles; the diagonal blocks of A are in LDS
-    // ---- -A, P and K^T over the lo tiles; the diagonal inverses ----
-    if (w == 7) {
-      // T_bb = (I + A_bb)^{-1} by forward substitution, lane = 16 b + column
-      const int b = g4, col = r16;
-      float tc[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc[4] = {r == col ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j4 = 0; j4 < (r + 3) / 4; ++j4) {
-          const f4v a4 = *reinterpret_cast<const f4v*>(&L.a32[b][r * 16 + 4 * j4]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (4 * j4 + i < r) acc[i] -= a4[i] * tc[4 * j4 + i];
-        }
-        tc[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        if ((r & 3) == 3) asm volatile("" ::: "memory");  // bound how far the row reads are hoisted
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) L.tinv[b][r][col] = (_Float16)tc[r];
-    }
+    lds_barrier();  // every wave is done with the lo tiles; the diagonal inverses are in LDS
+    // ---- -A, P and K^T over the lo tiles ----
     switch (w) {
-      case 0: gram_store<0, false>(L, gres[0], r16, g4, sql); gram_store<7, false>(L, gres[1], r16, g4, sql); break;
-      case 1: gram_store<1, false>(L, gres[0], r16, g4, sql); gram_store<8, false>(L, gres[1], r16, g4, sql); break;
-      case 2: gram_store<2, false>(L, gres[0], r16, g4, sql); gram_store<9, false>(L, gres[1], r16, g4, sql); break;
-      case 3: gram_store<3, false>(L, gres[0], r16, g4, sql); gram_store<1, true>(L, gres[1], r16, g4, sql);
-              gram_store<3, true>(L, gres[2], r16, g4, sql); break;
-      case 4: gram_store<4, false>(L, gres[0], r16, g4, sql); gram_store<4, true>(L, gres[1], r16, g4, sql);
-              gram_store<6, true>(L, gres[2], r16, g4, sql); break;
-      case 5: gram_store<5, false>(L, gres[0], r16, g4, sql); gram_store<7, true>(L, gres[1], r16, g4, sql); break;
-      case 6: gram_store<6, false>(L, gres[0], r16, g4, sql); gram_store<8, true>(L, gres[1], r16, g4, sql); break;
-      default: break;
+      case 0: gram_store<0, false>(L, gres[0], r16, g4, sql); gram_store<4, false>(L, gres[1], r16, g4, sql); break;
+      case 1: gram_store<1, false>(L, gres[0], r16, g4, sql); gram_store<5, false>(L, gres[1], r16, g4, sql); break;
+      case 2: gram_store<2, false>(L, gres[0], r16, g4, sql); gram_store<6, false>(L, gres[1], r16, g4, sql); break;
+      case 3: gram_store<3, false>(L, gres[0], r16, g4, sql); gram_store<7, false>(L, gres[1], r16, g4, sql); break;
+      case 4: gram_store<8, false>(L, gres[0], r16, g4, sql); break;
+      case 5: gram_store<9, false>(L, gres[0], r16, g4, sql); break;
+      case 6: gram_store<1, true>(L, gres[0], r16, g4, sql); gram_store<3, true>(L, gres[1], r16, g4, sql);
+              gram_store<4, true>(L, gres[2], r16, g4, sql); break;
+      default: gram_store<6, true>(L, gres[0], r16, g4, sql); gram_store<7, true>(L, gres[1], r16, g4, sql);
+               gram_store<8, true>(L, gres[2], r16, g4, sql); break;
     }
     {
       const int dk = tid_v & 127, tq = tid_v >> 7;
@@ -454,7 +482,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
         *reinterpret_cast<h4v*>(kt + sq_off(dk, t0)) = v;
       }
     }
-    __syncthreads();
+    lds_barrier();
     // ---- blocked forward substitution U = (I + A)^{-1} RHS ----
     h4v uh[4];
     f4v u[4];

@@ -45,6 +45,7 @@ flide_status compute_layout(const flide_caps& c, flide_meta_layout& L) {
   L.qfin_row = take(c.Q_cap > 0 ? c.Q_cap : 1);
   L.tile_seg = take(L.tile_cap);
   L.tile_row0 = take(L.tile_cap);
+  L.gdn_order = take(L.seg_cap);
   L.host_words = o;
   L.tok_j = take(c.T_cap);
   L.tok_c = take(c.T_cap);
@@ -228,6 +229,16 @@ flide_status flide_plan_round(const flide_request* reqs, int32_t R, const flide_
     for (size_t i = 0; i < tiles.size(); ++i) {
       img[size_t(L.tile_seg + int64_t(i))] = tiles[i].seg;
       img[size_t(L.tile_row0 + int64_t(i))] = tiles[i].row0;
+    }
+    // GDN work list: trunk segments, then question segments, each longest first (ties in stream
+    // order), so that the chains that take longest start first.  Segments are independent, so the
+    // order does not change any output bit.
+    {
+      int32_t* ord = img.data() + L.gdn_order;
+      for (int32_t s = 0; s < seg; ++s) ord[s] = s;
+      auto longer = [&](int32_t x, int32_t y) { return s_len[x] > s_len[y]; };
+      std::stable_sort(ord, ord + R, longer);
+      std::stable_sort(ord + R, ord + seg, longer);
     }
     hdr[H_T] = row;
     hdr[H_R] = R;
