@@ -188,10 +188,41 @@ __device__ __forceinline__ void issue_chunk_loads(ChunkIn& I, __amdgpu_buffer_rs
   }
 }
 
-// Diagonal block b of A (fp32, from the hi tiles) and T_bb = (I + A_bb)^{-1} by forward
-// substitution, one column per lane (lanes 16 .. 63 repeat lanes 0 .. 15).  A_bb[r][j] lives in
-// lane r + 16 (j / 4), register j % 4, and reaches every lane through a lane shuffle; none of these
-// loads waits on the running column, so they issue ahead of the substitution chain.
+// sum over the four 16-lane rows of the wave (v_permlane16_swap / v_permlane32_swap pair each lane
+// with the same lane of the partner row; adding both halves of each swap gives the pair sum)
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Row R of the substitution (the DPP broadcast lane must be a constant), then the next row.
+template <int R>
+struct InvRow {
+  static __device__ __forceinline__ void run(const float (&av)[4], float (&tq)[4], int g4, int col) {
+    float part[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(av[i]), 0x150 + R, 0xF, 0xF, false));
+      part[i] = (4 * g4 + i < R) ? a * tq[i] : 0.f;  // A[R][4 g4 + i] T[4 g4 + i][col]
+    }
+    const float tot = rows4_sum((part[0] + part[1]) + (part[2] + part[3]));
+    const float v = (R == col ? 1.f : 0.f) - tot;
+    if (g4 == (R >> 2)) tq[R & 3] = v;
+    InvRow<R + 1>::run(av, tq, g4, col);
+  }
+};
+template <>
+struct InvRow<16> {
+  static __device__ __forceinline__ void run(const float (&)[4], float (&)[4], int, int) {}
+};
+
+// Diagonal block B of A (fp32, from the hi tiles) and T_BB = (I + A_BB)^{-1} by forward
+// substitution.  Lane (r16, g4) first holds A[r16][4 g4 + i]; for the substitution it owns column
+// c = r16 and rows 4 g4 .. 4 g4 + 3 of T.  Row r of A reaches the lanes with a DPP row broadcast
+// of lane r of every 16-lane row, each row of lanes sums its four products, and the four partial
+// sums are combined across rows with lane swaps; nothing goes through LDS until T is stored.
 template <int B>
 __device__ __forceinline__ void diag_inverse(ChunkLds& L, const int (&gq)[4], int r16, int g4) {
   f4v acc = {0.f, 0.f, 0.f, 0.f};
@@ -209,21 +240,10 @@ __device__ __forceinline__ void diag_inverse(ChunkLds& L, const int (&gq)[4], in
     av[i] = s < t ? et * __expf(gt - L.g[s]) * acc[i] : 0.f;
   }
   const int col = r16;
-  float tc[16];
+  float tq[4] = {0.f, 0.f, 0.f, 0.f};  // T[4 g4 + i][col]
+  InvRow<0>::run(av, tq, g4, col);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float part[4] = {r == col ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int jj = 0; jj < r; ++jj) {
-      const float a = __shfl(av[jj & 3], r + 16 * (jj >> 2), 64);
-      part[jj & 3] -= a * tc[jj];
-    }
-    tc[r] = (part[0] + part[1]) + (part[2] + part[3]);
-  }
-  if (g4 == 0) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) L.tinv[B][r][col] = (_Float16)tc[r];
-  }
+  for (int i = 0; i < 4; ++i) L.tinv[B][4 * g4 + i][col] = (_Float16)tq[i];
 }
 
 }  // namespace
