@@ -16,6 +16,7 @@ Prints one JSON line.  ``value`` is stream tokens per second of whole rounds
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -28,6 +29,42 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # fp32 matrix
+COPY_BYTES = 256 << 20         # size of the reference copy of the counter pass
+
+
+# Kernel sources behind each timed entry point (their hash pins the HBM counter figures).
+KERNEL_SOURCES = {
+    "fork_gdn_trunks": ["gdn_chunk_kernels.hip"], "fork_gdn_questions": ["gdn_chunk_kernels.hip"],
+    "attn_prepare": ["attn_kernels.hip"], "attn_core": ["attn_kernels.hip"],
+    "attn_prepare_swa": ["attn_kernels.hip"], "attn_core_swa": ["attn_kernels.hip"],
+    "readout": ["readout_kernels.hip"],
+}
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters_short_rounds.md")
+
+
+def source_digest(name: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[name] + ["device_common.hpp", "flide_internal.hpp"]:
+        with open(os.path.join(ROOT, "tree_forked_hybrid_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name: str):
+    """HBM bytes per launch of `name` from the committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE,
+    scaled by the reference copy), or None when there is none or the kernel source changed since."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    with open(COUNTERS_FILE) as fh:
+        for line in fh:
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) >= 5 and cells[0] == name:
+                try:
+                    return float(cells[4]) if cells[1] == source_digest(name) else None
+                except ValueError:
+                    return None
+    return None
 
 
 def _round_up(x: int, m: int) -> int:
@@ -56,7 +93,9 @@ def algorithmic_work(rnd):
         flops = 4.0 * s.d * s.Hq * pr
         cached = sum(min(r.m, W) if W > 0 else r.m for r in rnd.requests)
         byts = T * (2 * s.Hq + 2 * s.Hkv) * s.d * b + cached * 2 * s.Hkv * s.d * b
-        attn[name] = {"flops": flops, "bytes": byts, "pairs": pr}
+        attn[name] = {"flops": flops, "bytes": byts, "pairs": pr,
+                      # rotary K and transposed V: read k, v and write both once
+                      "prep_bytes": 4 * T * s.Hkv * s.d * b}
     C = s.channels
     per_row = s.H * ((2 * s.dk + s.dv) * b + 8 + s.dv * b)
     state = 4 * s.H * s.dv * s.dk
@@ -105,6 +144,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-requests", type=int, default=6, help="requests of the oracle CPU sample (0: skip)")
     ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--counters", action="store_true",
+                    help="counter pass: one launch of every kernel plus a 256 MiB device copy (for rocprofv3 --pmc "
+                         "FETCH_SIZE / WRITE_SIZE and the copy-kernel scale factor); prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the ForkAttention round runs on a single MI355X "
@@ -142,6 +184,11 @@ def main():
         step()
     torch.cuda.synchronize()
     F.flide_check_device(ctx, caps, bufs.dev_meta)
+    # A serving loop keeps the collector out of the round's critical path: the setup heap is frozen
+    # and collection is paused while rounds are timed (a full collection costs tens of ms here).
+    gc.collect()
+    gc.freeze()
+    gc.disable()
     lat = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -150,6 +197,7 @@ def main():
         torch.cuda.synchronize()
         lat.append(time.perf_counter() - s0)
     t1 = time.perf_counter()
+    gc.enable()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     F.flide_check_device(ctx, caps, bufs.dev_meta)
 
@@ -168,29 +216,48 @@ def main():
         torch.cuda.synchronize()
         kernels[name] = ev[0].elapsed_time(ev[1]) * 1e3 / args.kernel_reps  # us
 
+    st = torch.cuda.current_stream()  # events and kernels on one stream
     gp = bufs.gdn_params
+    launches = {}
     for phase, name in ((0, "fork_gdn_trunks"), (1, "fork_gdn_questions")):
-        timed(name, lambda ph=phase: F.flide_fork_gdn(ctx, caps, bufs.dev_meta, gp, ph, bufs.x, bufs.conv_w,
-                                                      bufs.alpha, bufs.eta, bufs.state_pool, bufs.conv_pool,
-                                                      spec.n_slots, bufs.o_gdn))
+        launches[name] = lambda ph=phase: F.flide_fork_gdn(ctx, caps, bufs.dev_meta, gp, ph, bufs.x, bufs.conv_w,
+                                                           bufs.alpha, bufs.eta, bufs.state_pool, bufs.conv_pool,
+                                                           spec.n_slots, bufs.o_gdn, stream=st)
     for l in range(bufs.n_attn):
-        nm = "fork_attn" if l == 0 else "fork_attn_swa"
-        timed(nm, lambda l=l: F.flide_fork_attn(ctx, caps, bufs.dev_meta, bufs.attn_params[l], bufs.q[l], bufs.k[l],
-                                                bufs.v[l], bufs.k_cache[l], bufs.v_cache[l], bufs.o_attn[l],
-                                                bufs.ws[l]))
-    timed("readout", lambda: F.flide_readout(ctx, caps, bufs.dev_meta, bufs.ro_params, bufs.h, bufs.w_opt,
-                                             bufs.opt_off, bufs.opt_id, max(1, spec.opt_cap), bufs.probs))
+        sfx = "" if l == 0 else "_swa"
+        launches["attn_prepare" + sfx] = lambda l=l: F.flide_attn_prepare(
+            ctx, caps, bufs.dev_meta, bufs.attn_params[l], bufs.k[l], bufs.v[l], bufs.ws[l], stream=st)
+        launches["attn_core" + sfx] = lambda l=l: F.flide_attn_core(
+            ctx, caps, bufs.dev_meta, bufs.attn_params[l], bufs.q[l], bufs.v[l], bufs.k_cache[l], bufs.v_cache[l],
+            bufs.o_attn[l], bufs.ws[l], stream=st)
+    launches["readout"] = lambda: F.flide_readout(ctx, caps, bufs.dev_meta, bufs.ro_params, bufs.h, bufs.w_opt,
+                                                  bufs.opt_off, bufs.opt_id, max(1, spec.opt_cap), bufs.probs,
+                                                  stream=st)
+    if args.counters:
+        for fn in launches.values():
+            fn()
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)  # reference copy of known size: scales FETCH_SIZE / WRITE_SIZE
+        torch.cuda.synchronize()
+        print(f"counter pass done: {len(launches)} kernels, copy {COPY_BYTES} bytes", flush=True)
+        ctx.close()
+        return
+    for name, fn in launches.items():
+        timed(name, fn)
     torch.cuda.synchronize()
 
     work = algorithmic_work(rnd)
     rows = {
         "fork_gdn_trunks": ("hbm", work["gdn0"], None),
         "fork_gdn_questions": ("hbm", work["gdn1"], None),
-        "fork_attn": ("mfma", work["attn"]["attn"]["bytes"], work["attn"]["attn"]["flops"]),
+        "attn_prepare": ("hbm", work["attn"]["attn"]["prep_bytes"], None),
+        "attn_core": ("mfma", work["attn"]["attn"]["bytes"], work["attn"]["attn"]["flops"]),
         "readout": ("hbm", work["readout"], None),
     }
     if "swa" in work["attn"]:
-        rows["fork_attn_swa"] = ("mfma", work["attn"]["swa"]["bytes"], work["attn"]["swa"]["flops"])
+        rows["attn_prepare_swa"] = ("hbm", work["attn"]["swa"]["prep_bytes"], None)
+        rows["attn_core_swa"] = ("mfma", work["attn"]["swa"]["bytes"], work["attn"]["swa"]["flops"])
     per_kernel = {}
     for name, us in kernels.items():
         bound, byts, flops = rows[name]
@@ -212,11 +279,11 @@ def main():
     if bound == "mfma":
         ach = flops / (us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom}
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom), "kernel": dom}
     else:
         ach = byts / (us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom}
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(dom), "kernel": dom}
 
     cpu = None
     if args.cpu_requests > 0:
@@ -243,7 +310,7 @@ def main():
                              "p90": round(lat_ms[(9 * len(lat_ms)) // 10], 4)},
         "per_layer_tokens_per_s": {
             "gdn": round(T / ((kernels["fork_gdn_trunks"] + kernels["fork_gdn_questions"]) * 1e-6), 1),
-            "attn": round(T / (kernels["fork_attn"] * 1e-6), 1),
+            "attn": round(T / ((kernels["attn_prepare"] + kernels["attn_core"]) * 1e-6), 1),
         },
         "kernels": per_kernel,
         "roofline": roof,

@@ -262,6 +262,23 @@ typedef struct {
   int32_t deterministic;
 } flide_gdn_params;
 
+/* The two halves of flide_fork_attn, for callers that schedule them apart;
+ * flide_fork_attn is flide_attn_prepare followed by flide_attn_core on one stream.
+ * flide_attn_prepare: rotary embedding of k at the metadata positions (the
+ *   rotation of [ZH] §方法步骤详情) into `workspace`, and on the bf16 MFMA path the
+ *   transposed copy of v (per segment, value columns starting 8-aligned).
+ * flide_attn_core: the masked attention of q against the prepared workspace and
+ *   the K/V cache.  v is read only on the f32 path (the MFMA path reads the
+ *   transposed copy).  The workspace must hold what flide_attn_prepare wrote for
+ *   the same metadata, params and k, v.
+ * Arguments, layouts and errors as flide_fork_attn. */
+flide_status flide_attn_prepare(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
+                                const flide_attn_params* p, const void* k, const void* v, void* workspace,
+                                void* stream);
+flide_status flide_attn_core(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
+                             const flide_attn_params* p, const void* q, const void* v, const void* k_cache,
+                             const void* v_cache, void* o, const void* workspace, void* stream);
+
 flide_status flide_fork_gdn(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
                             const flide_gdn_params* p, int32_t phase, const void* x, const float* conv_w,
                             const float* alpha, const float* eta, float* state_pool, void* conv_pool,

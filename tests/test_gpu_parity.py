@@ -50,6 +50,26 @@ def test_short_rounds_bf16_subset(ctx):
     harness.check_round(rnd, harness.outputs(bufs), lay, mode="memo")
 
 
+@pytest.mark.parametrize("config", [1, 0])
+def test_attention_prepare_then_core_equals_fork_attn(ctx, config):
+    """flide_attn_prepare + flide_attn_core reproduce flide_fork_attn bit for bit (bf16 MFMA and f32 paths)."""
+    import torch
+    from tree_forked_hybrid_amd import flide as F
+    rnd = make_round(config, 0, requests=range(min(6, len(make_round(config, 0).requests))))
+    bufs, _ = harness.run_gpu(rnd, ctx, "direct")
+    for l in range(bufs.n_attn):
+        ref = bufs.o_attn[l].clone()
+        out = torch.zeros_like(ref)
+        ws = torch.zeros_like(bufs.ws[l])
+        p = bufs.attn_params[l]
+        F.flide_attn_prepare(ctx, bufs.caps, bufs.dev_meta, p, bufs.k[l], bufs.v[l], ws)
+        F.flide_attn_core(ctx, bufs.caps, bufs.dev_meta, p, bufs.q[l], bufs.v[l], bufs.k_cache[l], bufs.v_cache[l],
+                          out, ws)
+        torch.cuda.synchronize()
+        T = sum((r.P - r.m) + sum(r.q_len) for r in rnd.requests)
+        assert torch.equal(out[:T], ref[:T])
+
+
 EDGE = LayerShapes(H=2, dk=32, dv=32, conv_k=4, Hq=4, Hkv=2, d=64, theta=1e4, hidden=64, swa_window=5)
 
 

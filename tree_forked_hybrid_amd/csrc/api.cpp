@@ -213,17 +213,33 @@ flide_status view_of(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_
   return FLIDE_OK;
 }
 
-flide_status enqueue_attn(flide_ctx* ctx, const MetaView& mv, const flide_attn_params& p, const void* q,
-                          const void* k, const void* v, const void* kc, const void* vc, void* o, void* ws,
-                          hipStream_t stream) {
-  if (!q || !k || !v || !o || !ws) return fail(ctx, FLIDE_E_INVALID_ARG, "attention buffer is NULL");
+flide_status enqueue_attn_prepare(flide_ctx* ctx, const MetaView& mv, const flide_attn_params& p, const void* k,
+                                  const void* v, void* ws, hipStream_t stream) {
+  if (!k || !v || !ws) return fail(ctx, FLIDE_E_INVALID_ARG, "attention buffer is NULL");
+  RopeArgs rope;
+  FLIDE_TRY(ensure_rope(ctx, p.theta, p.d, p.max_pos, &rope));
+  return launched(ctx, launch_attn_prepare(mv, p, rope, k, v, ws, stream), "attn_prepare");
+}
+
+flide_status enqueue_attn_core(flide_ctx* ctx, const MetaView& mv, const flide_attn_params& p, const void* q,
+                               const void* v, const void* kc, const void* vc, void* o, const void* ws,
+                               hipStream_t stream) {
+  if (!q || !v || !o || !ws) return fail(ctx, FLIDE_E_INVALID_ARG, "attention buffer is NULL");
   if (p.cache_rows > 0 && (!kc || !vc || p.cache_slots < 1))
     return fail(ctx, FLIDE_E_INVALID_ARG, "K/V cache shape given without cache buffers");
   RopeArgs rope;
   FLIDE_TRY(ensure_rope(ctx, p.theta, p.d, p.max_pos, &rope));
-  return launched(ctx, launch_attn(mv, p, rope, q, k, v, p.cache_rows > 0 ? kc : nullptr,
-                                   p.cache_rows > 0 ? vc : nullptr, o, ws, stream),
-                  "fork_attn");
+  return launched(ctx, launch_attn_core(mv, p, rope, q, v, p.cache_rows > 0 ? kc : nullptr,
+                                        p.cache_rows > 0 ? vc : nullptr, o, ws, stream),
+                  "attn_core");
+}
+
+flide_status enqueue_attn(flide_ctx* ctx, const MetaView& mv, const flide_attn_params& p, const void* q,
+                          const void* k, const void* v, const void* kc, const void* vc, void* o, void* ws,
+                          hipStream_t stream) {
+  if (!q || !o) return fail(ctx, FLIDE_E_INVALID_ARG, "attention buffer is NULL");
+  FLIDE_TRY(enqueue_attn_prepare(ctx, mv, p, k, v, ws, stream));
+  return enqueue_attn_core(ctx, mv, p, q, v, kc, vc, o, ws, stream);
 }
 
 flide_status enqueue_gdn(flide_ctx* ctx, const MetaView& mv, const flide_gdn_params& p, int phase, const void* x,
@@ -348,6 +364,36 @@ flide_status flide_fork_attn(flide_ctx* ctx, const flide_caps* caps, const int32
     return enqueue_attn(ctx, mv, *p, q, k, v, k_cache, v_cache, o, workspace, (hipStream_t)stream);
   } catch (...) {
     return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_fork_attn");
+  }
+}
+
+flide_status flide_attn_prepare(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
+                                const flide_attn_params* p, const void* k, const void* v, void* workspace,
+                                void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    FLIDE_TRY(check_attn(ctx, p));
+    MetaView mv;
+    FLIDE_TRY(view_of(ctx, caps, dev_meta, &mv));
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    return enqueue_attn_prepare(ctx, mv, *p, k, v, workspace, (hipStream_t)stream);
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_attn_prepare");
+  }
+}
+
+flide_status flide_attn_core(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
+                             const flide_attn_params* p, const void* q, const void* v, const void* k_cache,
+                             const void* v_cache, void* o, const void* workspace, void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    FLIDE_TRY(check_attn(ctx, p));
+    MetaView mv;
+    FLIDE_TRY(view_of(ctx, caps, dev_meta, &mv));
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    return enqueue_attn_core(ctx, mv, *p, q, v, k_cache, v_cache, o, workspace, (hipStream_t)stream);
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_attn_core");
   }
 }
 

@@ -560,33 +560,43 @@ int64_t attn_workspace_bytes(const flide_caps& c, const flide_attn_params& p) {
   return bytes;
 }
 
-int launch_attn(const MetaView& mv, const flide_attn_params& p, const RopeArgs& rope, const void* q, const void* k,
-                const void* v, const void* k_cache, const void* v_cache, void* o, void* workspace, void* stream) {
-  hipStream_t st = (hipStream_t)stream;
-  const int W = p.window;
+int launch_attn_prepare(const MetaView& mv, const flide_attn_params& p, const RopeArgs& rope, const void* k,
+                        const void* v, void* workspace, void* stream) {
   if (attn_uses_mfma(p)) {
     bf16_t* k_rot = (bf16_t*)workspace;
     bf16_t* vt = k_rot + int64_t(mv.T_cap) * p.Hkv * p.d;
     dim3 pg((mv.T_cap + 63) / 64, p.Hkv);
+    if (p.d == 256)
+      hipLaunchKernelGGL(kv_prep_kernel<256>, pg, dim3(256), 0, (hipStream_t)stream, mv, (const bf16_t*)k,
+                         (const bf16_t*)v, k_rot, vt, rope.table, rope.max_pos, p.Hkv);
+    else
+      hipLaunchKernelGGL(kv_prep_kernel<128>, pg, dim3(256), 0, (hipStream_t)stream, mv, (const bf16_t*)k,
+                         (const bf16_t*)v, k_rot, vt, rope.table, rope.max_pos, p.Hkv);
+    return int(hipGetLastError());
+  }
+  return launch_rope_k(mv, p, rope, k, workspace, stream);
+}
+
+int launch_attn_core(const MetaView& mv, const flide_attn_params& p, const RopeArgs& rope, const void* q,
+                     const void* v, const void* k_cache, const void* v_cache, void* o, const void* workspace,
+                     void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const int W = p.window;
+  if (attn_uses_mfma(p)) {
+    const bf16_t* k_rot = (const bf16_t*)workspace;
+    const bf16_t* vt = k_rot + int64_t(mv.T_cap) * p.Hkv * p.d;
     const int G = p.Hq / p.Hkv;
     dim3 grid(mv.tile_cap, p.Hkv * ((G + 3) / 4));
-    if (p.d == 256) {
-      hipLaunchKernelGGL(kv_prep_kernel<256>, pg, dim3(256), 0, st, mv, (const bf16_t*)k, (const bf16_t*)v, k_rot,
-                         vt, rope.table, rope.max_pos, p.Hkv);
+    if (p.d == 256)
       hipLaunchKernelGGL((attn_mfma_kernel<256>), grid, dim3(256), 0, st, mv, (const bf16_t*)q, k_rot, vt,
                          (const bf16_t*)k_cache, (const bf16_t*)v_cache, (bf16_t*)o, rope.table, rope.max_pos, p.Hq,
                          p.Hkv, W, p.cache_rows, p.cache_slots);
-    } else {
-      hipLaunchKernelGGL(kv_prep_kernel<128>, pg, dim3(256), 0, st, mv, (const bf16_t*)k, (const bf16_t*)v, k_rot,
-                         vt, rope.table, rope.max_pos, p.Hkv);
+    else
       hipLaunchKernelGGL((attn_mfma_kernel<128>), grid, dim3(256), 0, st, mv, (const bf16_t*)q, k_rot, vt,
                          (const bf16_t*)k_cache, (const bf16_t*)v_cache, (bf16_t*)o, rope.table, rope.max_pos, p.Hq,
                          p.Hkv, W, p.cache_rows, p.cache_slots);
-    }
     return int(hipGetLastError());
   }
-  int rc = launch_rope_k(mv, p, rope, k, workspace, stream);
-  if (rc != 0) return rc;
   dim3 grid(mv.tile_cap, p.Hq);
   if (p.dtype == FLIDE_BF16) {
     hipLaunchKernelGGL(attn_plain_kernel<bf16_t>, grid, dim3(256), 0, st, mv, (const bf16_t*)q,

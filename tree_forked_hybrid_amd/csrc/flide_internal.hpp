@@ -111,10 +111,13 @@ struct RopeArgs {
 
 int launch_rope_k(const MetaView& mv, const flide_attn_params& p, const RopeArgs& rope, const void* k,
                   void* k_rot, void* stream);
-// Rotates keys (and, on the MFMA path, transposes values) into `workspace`,
-// then runs the attention kernel.
-int launch_attn(const MetaView& mv, const flide_attn_params& p, const RopeArgs& rope, const void* q, const void* k,
-                const void* v, const void* k_cache, const void* v_cache, void* o, void* workspace, void* stream);
+// Rotates keys (and, on the MFMA path, transposes values) into `workspace`.
+int launch_attn_prepare(const MetaView& mv, const flide_attn_params& p, const RopeArgs& rope, const void* k,
+                        const void* v, void* workspace, void* stream);
+// The masked attention over a prepared workspace (the f32 path reads values from v).
+int launch_attn_core(const MetaView& mv, const flide_attn_params& p, const RopeArgs& rope, const void* q,
+                     const void* v, const void* k_cache, const void* v_cache, void* o, const void* workspace,
+                     void* stream);
 bool attn_uses_mfma(const flide_attn_params& p);
 int64_t attn_workspace_bytes(const flide_caps& c, const flide_attn_params& p);
 int launch_gdn(const MetaView& mv, const flide_gdn_params& p, int phase, const void* x, const float* conv_w,

@@ -100,6 +100,10 @@ _SIGNATURES = {
                                              C.POINTER(C.c_int64)]),
     "flide_fork_attn": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.POINTER(flide_attn_params), _VP, _VP, _VP,
                                   _VP, _VP, _VP, _VP, _VP]),
+    "flide_attn_prepare": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.POINTER(flide_attn_params), _VP, _VP, _VP,
+                                     _VP]),
+    "flide_attn_core": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.POINTER(flide_attn_params), _VP, _VP, _VP, _VP,
+                                  _VP, _VP, _VP]),
     "flide_fork_gdn": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.POINTER(flide_gdn_params), C.c_int32, _VP,
                                  _VP, _VP, _VP, _VP, _VP, C.c_int32, _VP, _VP]),
     "flide_readout": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.POINTER(flide_readout_params), _VP, _VP, _VP,
@@ -304,6 +308,19 @@ def flide_fork_attn(ctx: Context, caps: flide_caps, dev_meta, p: flide_attn_para
     _check(load_library().flide_fork_attn(ctx.handle, C.byref(caps), _ptr(dev_meta), C.byref(p), _ptr(q), _ptr(k),
                                           _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(workspace),
                                           _stream(stream)), "flide_fork_attn", ctx.handle)
+
+
+def flide_attn_prepare(ctx: Context, caps: flide_caps, dev_meta, p: flide_attn_params, k, v, workspace,
+                       stream=None) -> None:
+    _check(load_library().flide_attn_prepare(ctx.handle, C.byref(caps), _ptr(dev_meta), C.byref(p), _ptr(k), _ptr(v),
+                                             _ptr(workspace), _stream(stream)), "flide_attn_prepare", ctx.handle)
+
+
+def flide_attn_core(ctx: Context, caps: flide_caps, dev_meta, p: flide_attn_params, q, v, k_cache, v_cache, o,
+                    workspace, stream=None) -> None:
+    _check(load_library().flide_attn_core(ctx.handle, C.byref(caps), _ptr(dev_meta), C.byref(p), _ptr(q), _ptr(v),
+                                          _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(workspace), _stream(stream)),
+           "flide_attn_core", ctx.handle)
 
 
 def flide_fork_gdn(ctx: Context, caps: flide_caps, dev_meta, p: flide_gdn_params, phase: int, x, conv_w, alpha,
