@@ -39,6 +39,7 @@ __global__ void __launch_bounds__(256) attn_plain_kernel(MetaView mv, const T* _
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int s = mv.tile_seg[tile];
+  if (s == -1) return;  // unused position of the work list
   if (s < 0 || s >= mv.hdr[H_NSEG]) {
     if (threadIdx.x == 0) flag_error(mv.dev_error, E_SEGMENT);
     return;
@@ -301,16 +302,21 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   static_assert(IPW >= 1, "tile split over 4 waves");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * TILE_BYTES];  // K0 K1 V0 V1
 
-  const int tile = blockIdx.x;
-  if (tile >= mv.hdr[H_NTILES]) return;
+  // Workgroup i runs on XCD i mod 8: XCD c takes the work-list positions c, c + 8, ... (the planner
+  // puts each group of tiles that share keys on one of them), every head group of a position in turn.
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g4 = l >> 4;
   const int G = Hq / Hkv;
   const int HG = (G + 3) / 4;
-  const int kvh = blockIdx.y / HG, hl = (blockIdx.y % HG) * 4 + w;
+  const int HY = Hkv * HG;
+  const int i8 = blockIdx.x / kXcdClasses;
+  const int tile = kXcdClasses * (i8 / HY) + int(blockIdx.x % kXcdClasses), yy = i8 % HY;
+  if (tile >= mv.hdr[H_NTILES]) return;
+  const int kvh = yy / HG, hl = (yy % HG) * 4 + w;
   const bool active = hl < G;
   const int h = kvh * G + hl;
 
   const int seg = mv.tile_seg[tile];
+  if (seg == -1) return;  // unused position of the work list
   if (seg < 0 || seg >= mv.hdr[H_NSEG]) {
     if (tid == 0) flag_error(mv.dev_error, E_SEGMENT);
     return;
@@ -586,7 +592,7 @@ int launch_attn_core(const MetaView& mv, const flide_attn_params& p, const RopeA
     const bf16_t* k_rot = (const bf16_t*)workspace;
     const bf16_t* vt = k_rot + int64_t(mv.T_cap) * p.Hkv * p.d;
     const int G = p.Hq / p.Hkv;
-    dim3 grid(mv.tile_cap, p.Hkv * ((G + 3) / 4));
+    dim3 grid(mv.tile_cap * p.Hkv * ((G + 3) / 4));  // tile_cap is a multiple of kXcdClasses
     if (p.d == 256)
       hipLaunchKernelGGL((attn_mfma_kernel<256>), grid, dim3(256), 0, st, mv, (const bf16_t*)q, k_rot, vt,
                          (const bf16_t*)k_cache, (const bf16_t*)v_cache, (bf16_t*)o, rope.table, rope.max_pos, p.Hq,

@@ -9,6 +9,8 @@ namespace flide {
 
 // Query rows per attention work tile (rows of one segment; tiles never straddle segments).
 constexpr int kTileRows = 32;
+// XCDs of the chip: workgroup i of a grid runs on XCD i mod kXcdClasses.
+constexpr int kXcdClasses = 8;
 // Words of the metadata header.
 constexpr int kHdrWords = 64;
 constexpr int32_t kMagic = 0x464C4944;  // 'FLID'

@@ -248,7 +248,9 @@ __device__ __forceinline__ void diag_inverse(ChunkLds& L, const int (&gq)[4], in
 
 }  // namespace
 
-__global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, int H, int K, int act,
+// PHASE 0: trunk segments (writes each request's state and conv window); PHASE 1: question segments.
+template <int PHASE>
+__global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K, int act,
                                                        const bf16_t* __restrict__ x, const float* __restrict__ conv_w,
                                                        const float* __restrict__ alpha,
                                                        const float* __restrict__ eta, float* __restrict__ state_pool,
@@ -261,7 +263,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
   const int item = lin / H, h = lin % H;
   const int R = mv.hdr[H_R];
   int seg;
-  if (phase == 0) {
+  if (PHASE == 0) {
     if (item >= R) return;
     seg = mv.gdn_order[item];
   } else {
@@ -273,8 +275,8 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
   const int j = mv.seg_req[seg];
   const int row0 = mv.seg_row0[seg], len = mv.seg_len[seg];
   const int in_slot = mv.seg_state[seg];
-  const int out_slot = phase == 0 ? mv.req_out[j] : -1;
-  if (in_slot >= n_slots || out_slot >= n_slots || (phase == 1 && in_slot < 0)) {
+  const int out_slot = PHASE == 0 ? mv.req_out[j] : -1;
+  if (in_slot >= n_slots || out_slot >= n_slots || (PHASE == 1 && in_slot < 0)) {
     if (tid == 0) flag_error(mv.dev_error, E_SLOT);
     return;
   }
@@ -551,7 +553,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int phase, i
     }
   }
 
-  if (phase == 0) {
+  if (PHASE == 0) {
     float* dst = state_pool + ((int64_t(out_slot) * H + h) * DV + ncol) * DK;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<f4v*>(dst + 16 * mb + 4 * g4) = S[mb];
@@ -582,7 +584,8 @@ int launch_gdn(const MetaView& mv, const flide_gdn_params& p, int phase, const v
   if (!gdn_uses_chunk(p) || !offsets_fit)
     return launch_gdn_plain(mv, p, phase, x, conv_w, alpha, eta, state_pool, conv_pool, n_slots, o, stream);
   dim3 grid(phase == 0 ? mv.R_cap : (mv.Q_cap > 0 ? mv.Q_cap : 1), p.H);
-  hipLaunchKernelGGL(gdn_chunk_kernel, grid, dim3(NT), 0, (hipStream_t)stream, mv, phase, p.H, p.conv_k, p.act,
+  hipLaunchKernelGGL(phase == 0 ? gdn_chunk_kernel<0> : gdn_chunk_kernel<1>, grid, dim3(NT), 0, (hipStream_t)stream,
+                     mv, p.H, p.conv_k, p.act,
                      (const bf16_t*)x, conv_w, alpha, eta, state_pool, (bf16_t*)conv_pool, n_slots, (bf16_t*)o);
   return int(hipGetLastError());
 }

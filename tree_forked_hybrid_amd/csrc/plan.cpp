@@ -20,7 +20,7 @@ flide_status compute_layout(const flide_caps& c, flide_meta_layout& L) {
   std::memset(&L, 0, sizeof(L));
   L.seg_cap = c.R_cap + c.Q_cap;
   L.tile_rows = kTileRows;
-  L.tile_cap = (c.T_cap + kTileRows - 1) / kTileRows + L.seg_cap;
+  L.tile_cap = ((c.T_cap + kTileRows - 1) / kTileRows + L.seg_cap + kXcdClasses - 1) / kXcdClasses * kXcdClasses;
   int64_t o = 0;
   auto take = [&](int64_t n) {
     int64_t at = o;
@@ -206,29 +206,93 @@ flide_status flide_plan_round(const flide_request* reqs, int32_t R, const flide_
         vend = vstart + s_len[s];
       }
     }
-    // Attention work list: tiles of kTileRows rows aligned to each segment's
-    // start, heaviest first (cost = keys seen by the tile's last row) so that a
-    // fixed grid finishes its long tiles early.  Tiles are independent, so the
-    // order does not change any output bit.
-    struct Tile {
-      int64_t cost;
-      int32_t seg, row0;
-    };
-    std::vector<Tile> tiles;
-    tiles.reserve(size_t(L.tile_cap));
-    for (int32_t s = 0; s < seg; ++s) {
-      const flide_request& r = reqs[s_req[s]];
-      for (int32_t a = 0; a < s_len[s]; a += kTileRows) {
-        int32_t last = std::min(a + kTileRows, s_len[s]);
-        int64_t cost = int64_t(r.m) + last + (s_br[s] > 0 ? int64_t(r.P - r.m) : 0);
-        tiles.push_back({cost, s, s_row0[s] + a});
+    int32_t n_tiles = 0;
+    // Attention work list, indexed by the kernel's tile position x.  Tiles of kTileRows rows aligned to
+    // each segment's start; cost = keys seen by the tile's last row.  A request's tiles (trunk by
+    // position, then its questions, which read the trunk's keys) are cut into contiguous groups of at
+    // most about 1/16 of the round's cost; the groups go, heaviest first, to the least loaded of
+    // kXcdClasses classes, and class c's tiles take positions c, c + 8, c + 16, ... group by group
+    // (heaviest tile first within a group).  The kernel runs position x on XCD x mod 8, so a group's
+    // key and value tiles are read into one L2, one or two groups at a time.  Unused positions hold
+    // segment -1.  Tiles are independent, so the order does not change
+    // any output bit.
+    {
+      struct Tile {
+        int64_t cost;
+        int32_t seg, row0;
+      };
+      std::vector<std::vector<Tile>> per_req(static_cast<size_t>(R));
+      int64_t total = 0, n_all = 0;
+      auto add_segment = [&](int32_t s, std::vector<Tile>& out) {
+        const flide_request& r = reqs[s_req[s]];
+        for (int32_t a = 0; a < s_len[s]; a += kTileRows) {
+          const int32_t last = std::min(a + kTileRows, s_len[s]);
+          const int64_t cost = int64_t(r.m) + last + (s_br[s] > 0 ? int64_t(r.P - r.m) : 0);
+          out.push_back({cost, s, s_row0[s] + a});
+          total += cost;
+          ++n_all;
+        }
+      };
+      for (int32_t j = 0; j < R; ++j) {
+        add_segment(j, per_req[size_t(j)]);
+        for (int32_t i = 0; i < reqs[j].n_q; ++i) add_segment(r_qs[j] + i, per_req[size_t(j)]);
       }
-    }
-    if (int64_t(tiles.size()) > L.tile_cap) return FLIDE_E_INTERNAL;
-    std::stable_sort(tiles.begin(), tiles.end(), [](const Tile& x, const Tile& y) { return x.cost > y.cost; });
-    for (size_t i = 0; i < tiles.size(); ++i) {
-      img[size_t(L.tile_seg + int64_t(i))] = tiles[i].seg;
-      img[size_t(L.tile_row0 + int64_t(i))] = tiles[i].row0;
+      if (n_all > L.tile_cap) return FLIDE_E_INTERNAL;
+      const int64_t target = std::max<int64_t>(1, (total + 15) / 16);
+      struct Group {
+        int64_t cost;
+        std::vector<Tile> tiles;
+      };
+      std::vector<Group> groups;
+      for (auto& rt : per_req) {
+        Group cur{0, {}};
+        for (const Tile& t : rt) {
+          cur.tiles.push_back(t);
+          cur.cost += t.cost;
+          if (cur.cost >= target) {
+            groups.push_back(std::move(cur));
+            cur = Group{0, {}};
+          }
+        }
+        if (!cur.tiles.empty()) groups.push_back(std::move(cur));
+      }
+      std::stable_sort(groups.begin(), groups.end(), [](const Group& x, const Group& y) { return x.cost > y.cost; });
+      std::vector<Tile> cls[kXcdClasses];
+      int64_t load[kXcdClasses] = {};
+      for (const Group& g : groups) {
+        int c = 0;
+        for (int k = 1; k < kXcdClasses; ++k)
+          if (load[k] < load[c]) c = k;
+        load[c] += g.cost;
+        std::vector<Tile> gt = g.tiles;
+        std::stable_sort(gt.begin(), gt.end(), [](const Tile& x, const Tile& y) { return x.cost > y.cost; });
+        cls[c].insert(cls[c].end(), gt.begin(), gt.end());
+      }
+      size_t maxlen = 0;
+      for (auto& v : cls) maxlen = std::max(maxlen, v.size());
+      int32_t* t_seg = img.data() + L.tile_seg;
+      int32_t* t_row = img.data() + L.tile_row0;
+      if (int64_t(maxlen) * kXcdClasses <= L.tile_cap) {
+        n_tiles = int32_t(maxlen) * kXcdClasses;
+        for (int32_t x = 0; x < n_tiles; ++x) {
+          t_seg[x] = -1;
+          t_row[x] = 0;
+        }
+        for (int c = 0; c < kXcdClasses; ++c)
+          for (size_t k = 0; k < cls[c].size(); ++k) {
+            t_seg[k * kXcdClasses + size_t(c)] = cls[c][k].seg;
+            t_row[k * kXcdClasses + size_t(c)] = cls[c][k].row0;
+          }
+      } else {  // unbalanced classes: one list, heaviest first, without XCD affinity
+        std::vector<Tile> all;
+        for (auto& v : cls) all.insert(all.end(), v.begin(), v.end());
+        std::stable_sort(all.begin(), all.end(), [](const Tile& x, const Tile& y) { return x.cost > y.cost; });
+        n_tiles = int32_t(all.size());
+        for (int32_t x = 0; x < n_tiles; ++x) {
+          t_seg[x] = all[size_t(x)].seg;
+          t_row[x] = all[size_t(x)].row0;
+        }
+      }
     }
     // GDN work list: trunk segments, then question segments, each longest first (ties in stream
     // order), so that the chains that take longest start first.  Segments are independent, so the
@@ -244,7 +308,7 @@ flide_status flide_plan_round(const flide_request* reqs, int32_t R, const flide_
     hdr[H_R] = R;
     hdr[H_NSEG] = seg;
     hdr[H_NQST] = qi;
-    hdr[H_NTILES] = int32_t(tiles.size());
+    hdr[H_NTILES] = n_tiles;
     hdr[H_MAXPOS] = max_pos;
     hdr[H_MAGIC] = kMagic;
     std::memcpy(image, img.data(), size_t(L.host_words) * sizeof(int32_t));
