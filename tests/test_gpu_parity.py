@@ -44,6 +44,31 @@ def test_graph_and_eager_equal_direct_bitwise(ctx, mode):
         np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
 
 
+def test_graph_replays_with_eager_work_between(ctx):
+    """One captured graph, replayed four times with the program's own eager work (output clears, other
+    torch kernels) and synchronizations in between; every replay equals the eager round bit for bit."""
+    import torch
+    from tree_forked_hybrid_amd import flide as F
+    rnd = make_round(1, 0, requests=range(5))
+    be, _ = harness.run_gpu(rnd, ctx, "eager")
+    ref = harness.outputs(be)
+    bg, _ = harness.run_gpu(rnd, ctx, "direct")
+    img = F.flide_plan_round(rnd.requests, bg.caps)
+    bid = F.flide_graph_capture(ctx, bg.round_bufs())
+    scratch = torch.randn(1024, 1024, device="cuda")
+    for rep in range(4):
+        for t in [bg.o_gdn, bg.probs, bg.state_pool] + list(bg.o_attn):
+            t.zero_()
+        scratch = torch.tanh(scratch @ scratch.T * 1e-3)  # unrelated eager work on the device
+        torch.cuda.synchronize()
+        F.flide_graph_replay(ctx, bid, img)
+        torch.cuda.synchronize()
+        got = harness.outputs(bg)
+        for k in ref:
+            np.testing.assert_array_equal(got[k], ref[k], err_msg=f"replay {rep}: {k}")
+    F.flide_check_device(ctx, bg.caps, bg.dev_meta)
+
+
 def test_short_rounds_bf16_subset(ctx):
     rnd = make_round(1, 0, requests=range(6))
     bufs, lay = harness.run_gpu(rnd, ctx, "direct")
@@ -172,3 +197,28 @@ def test_edge_cases_chunked_gdn(ctx, dtype):
     rnd = custom_round(sh, dtype, reqs, base=29)
     bufs, lay = harness.run_gpu(rnd, ctx, "direct")
     harness.check_round(rnd, harness.outputs(bufs), lay, mode="isolated")
+
+
+def test_split_round_graph_buckets_and_eager(ctx):
+    """A round larger than one capacity: split at request boundaries, sub-rounds replayed in one
+    captured bucket of T_max rows, and a request longer than T_max run eagerly in its own buffers."""
+    from tree_forked_hybrid_amd import flide as F
+    from tree_forked_hybrid_amd.runner import RoundBuffers, spec_for_round
+    sh = LayerShapes(H=2, dk=128, dv=128, conv_k=4, Hq=4, Hkv=1, d=128, theta=1e4, hidden=64, swa_window=40)
+    reqs = [Request(P=100, m=0, q_len=(20, 9), n_opt=(2, 3), out_slot=0),
+            Request(P=260, m=0, q_len=(40,), n_opt=(4,), out_slot=1),
+            Request(P=700, m=0, q_len=(30, 12), n_opt=(2, 2), out_slot=2),
+            Request(P=150, m=0, q_len=(16,), n_opt=(3,), out_slot=3),
+            Request(P=200, m=0, q_len=(8, 8, 8), n_opt=(2, 2, 2), out_slot=4)]
+    t_max = 512
+    rnd = custom_round(sh, "bf16", reqs, base=41, t_max=t_max)
+    first, eager = F.flide_split_round(rnd.requests, t_max)
+    assert eager.count(True) == 1 and len(eager) >= 3
+    bucket = RoundBuffers(spec_for_round(rnd, T_cap=t_max, R_cap=len(reqs), Q_cap=8))
+    for i, is_eager in enumerate(eager):
+        sub = rnd.subset(list(range(first[i], first[i + 1])))
+        if is_eager:
+            bufs, lay = harness.run_gpu(sub, ctx, "eager")
+        else:
+            bufs, lay = harness.run_gpu(sub, ctx, "graph", bufs=bucket)
+        harness.check_round(sub, harness.outputs(bufs), lay, mode="memo")

@@ -501,8 +501,7 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
       }
       float mx = fmaxf(fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), fmaxf(s[0][qb][2], s[0][qb][3])),
                        fmaxf(fmaxf(s[1][qb][0], s[1][qb][1]), fmaxf(s[1][qb][2], s[1][qb][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = rows4_max(mx);
       // move the running maximum only when it grows by more than 8 (log2 units)
       const bool grow = mx > m_run[qb] + 8.f;
       if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -523,8 +522,7 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
           s[kb][qb][i] = pv;
           rs += pv;
         }
-      rs += __shfl_xor(rs, 16, 64);
-      rs += __shfl_xor(rs, 32, 64);
+      rs = rows4_sum(rs);
       l_run[qb] += rs;
       pf[qb] = u32x4v{pack_bf16x2(s[0][qb][0], s[0][qb][1]), pack_bf16x2(s[0][qb][2], s[0][qb][3]),
                       pack_bf16x2(s[1][qb][0], s[1][qb][1]), pack_bf16x2(s[1][qb][2], s[1][qb][3])};

@@ -41,6 +41,23 @@ __device__ __forceinline__ void store_f32<bf16_t>(bf16_t* p, int64_t i, float v)
   p[i] = f32_to_bf16(v);
 }
 
+// Sum / max over the four 16-lane rows of a wave (lane l with lanes l ^ 16, l ^ 32, l ^ 48) on the
+// VALU: v_permlane16_swap / v_permlane32_swap pair each lane with the same lane of the partner row,
+// and combining both halves of a swap gives the pair result.  Same pairing as a shuffle butterfly
+// (xor 16, then xor 32), so the results match it bit for bit.
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -188,15 +188,6 @@ __device__ __forceinline__ void issue_chunk_loads(ChunkIn& I, __amdgpu_buffer_rs
   }
 }
 
-// sum over the four 16-lane rows of the wave (v_permlane16_swap / v_permlane32_swap pair each lane
-// with the same lane of the partner row; adding both halves of each swap gives the pair sum)
-__device__ __forceinline__ float rows4_sum(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // Row R of the substitution (the DPP broadcast lane must be a constant), then the next row.
 template <int R>
 struct InvRow {
