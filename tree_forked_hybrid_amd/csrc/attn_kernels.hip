@@ -171,12 +171,7 @@ __device__ __forceinline__ f32x4v mfma16x16x32(u32x4v a, u32x4v b, f32x4v c) {
                                                  0, 0, 0);
 }
 
-typedef float f32x2v __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 // Two floats to two bf16 (round to nearest even) in one hardware conversion.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
-}
 
 // Columns of the transposed value workspace per (kv head, channel): the stream
 // capacity plus up to 7 alignment columns per segment, rounded up.

@@ -13,6 +13,14 @@ typedef uint16_t bf16_t;  // raw bfloat16 bits
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
 // Round to nearest even (inputs here are finite).
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Two floats to two bf16 (round to nearest even, v_cvt_pk_bf16_f32); lo in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
+}
+
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);

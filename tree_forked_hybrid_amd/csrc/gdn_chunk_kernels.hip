@@ -91,9 +91,11 @@ struct ChunkLds {
   _Float16 kl[CK * DK];  // k - hi (lo part); after the Gram products: -A [t][s] then P [t][s]
   _Float16 tinv[4][16][16];
   float cw[2][8][16][4];  // q/k conv taps [section][channel % 8][channel / 8][tap], right-aligned (tap 3 = current row)
-  float g[CK];
-  float eta[CK];
-  float glast;
+  alignas(16) float g[CK];    // g_t = sum of log alpha over the chunk's rows up to t
+  alignas(16) float eta[CK];  // eta_t (0 past the chunk)
+  alignas(16) float eg[CK];   // e^{g_t}
+  alignas(16) float egn[CK];  // e^{g_n - g_t} (0 past the chunk)
+  float egl;                  // e^{g_n}
 };
 
 // Workgroup barrier that orders LDS only: unlike __syncthreads() it does not wait for this wave's
@@ -334,6 +336,10 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
       __builtin_amdgcn_make_buffer_rsrc((void*)(eta + int64_t(row0) * H + h), 0, len > 0 ? ((len - 1) * H + 1) * 4 : 0,
                                         0x00020000);
   const int head_b = h * DK * 2, sect_b = H * DK * 2;
+  // outputs of the segment's rows [0, len): stores past the segment fall outside the resource
+  const int rowo = H * DV * 2;  // bytes per output row
+  const __amdgpu_buffer_rsrc_t orr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(o + int64_t(row0) * H * DV), 0, len * rowo, 0x00020000);
   if (len > 0) issue_chunk_loads(I, xr, ar, er, 0, w, l, rowb, head_b, sect_b, H * 4);
 
   _Float16* const am = L.kl;           // -A [t][s] (strictly lower blocks), after the Gram products
@@ -379,9 +385,12 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
         const float up = __shfl_up(gsum, off, 64);
         if (t >= off) gsum += up;
       }
+      const float gn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gsum), n - 1));
       L.g[t] = gsum;
       L.eta[t] = e;
-      if (t == n - 1) L.glast = gsum;
+      L.eg[t] = __expf(gsum);
+      L.egn[t] = t < n ? __expf(gn - gsum) : 0.f;
+      if (t == 0) L.egl = __expf(gn);
     }
     // ---- values of this lane's channel at rows 16 rb + 4 g4 + i (the solve's layout) ----
     f4v vv[4];
@@ -466,11 +475,10 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
         ks = mma32(cat8(lds4(L.kh + 16 * rb * DK + kq[c][0]), lds4(L.kh + 16 * rb * DK + kq[c][1])), sf[c], ks);
         qs[rb] = mma32(cat8(lds4(L.qh + 16 * rb * DK + kq[c][0]), lds4(L.qh + 16 * rb * DK + kq[c][1])), sf[c], qs[rb]);
       }
+      const f4v eg4 = *reinterpret_cast<const f4v*>(&L.eg[16 * rb + 4 * g4]);
+      const f4v eta4 = *reinterpret_cast<const f4v*>(&L.eta[16 * rb + 4 * g4]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tr = 16 * rb + 4 * g4 + i;
-        rhs[rb][i] = L.eta[tr] * (vv[rb][i] - __expf(L.g[tr]) * ks[i]);
-      }
+      for (int i = 0; i < 4; ++i) rhs[rb][i] = eta4[i] * (vv[rb][i] - eg4[i] * ks[i]);
     }
     lds_barrier();  // every wave is done with the lo tiles; the diagonal inverses are in LDS
     // ---- -A, P and K^T over the lo tiles ----
@@ -510,31 +518,30 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
     // ---- outputs O = e^g Q S0^T + P U ----
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      f4v acc;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = __expf(L.g[16 * rb + 4 * g4 + i]) * qs[rb][i];
+      f4v acc = *reinterpret_cast<const f4v*>(&L.eg[16 * rb + 4 * g4]) * qs[rb];
 #pragma unroll
       for (int jb = 0; jb <= rb; ++jb) acc = mma16(lds4(pm + 16 * rb * CK + sql[jb]), uh[jb], acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * rb + 4 * g4 + i;
-        if (t < n) o[(int64_t(row0 + c0 + t) * H + h) * DV + ncol] = f32_to_bf16(acc[i]);
-      }
+      const uint32_t p01 = pack_bf16x2(acc[0], acc[1]), p23 = pack_bf16x2(acc[2], acc[3]);
+      const int ob = (c0 + 16 * rb + 4 * g4) * rowo + (h * DV + ncol) * 2;  // row 16 rb + 4 g4 of this chunk
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)p01, orr, ob, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(p01 >> 16), orr, ob + rowo, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)p23, orr, ob + 2 * rowo, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(p23 >> 16), orr, ob + 3 * rowo, 0, 0);
     }
     // ---- state update S = e^{g_n} S + U^T diag(e^{g_n - g}) K ----
-    const float gl = L.glast;
     h4v ud[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
+      const f4v egn4 = *reinterpret_cast<const f4v*>(&L.egn[16 * rb + 4 * g4]);
       f4v v4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * rb + 4 * g4 + i;
-        v4[i] = t < n ? __expf(gl - L.g[t]) * u[rb][i] : 0.f;
+        v4[i] = t < n ? egn4[i] * u[rb][i] : 0.f;
       }
       ud[rb] = to_h4(v4);
     }
-    const float egl = __expf(gl);
+    const float egl = L.egl;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       f4v acc = S[mb] * egl;
