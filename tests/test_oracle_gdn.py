@@ -173,3 +173,16 @@ def test_resume_from_checkpoint_equals_full_run():
     np.testing.assert_allclose(b["attn_o"], a["attn_o"][m:], atol=1e-13, rtol=0)
     for pa, pb in zip(a["probs"], b["probs"]):
         np.testing.assert_array_equal(pa, pb)
+
+
+def test_silu_option_closed_form():
+    """act = "silu": with identity conv taps, one-hot keys and queries, alpha = eta = 1 and a zero start
+    state, the output equals the activated value input: silu(ln 3) = 0.75 ln 3, silu(-ln 3) = -0.25 ln 3
+    (a sigmoid, a missing activation or one applied after the norm fails)."""
+    ln3 = np.log(3.0)
+    for xv, want in ((ln3, 0.75 * ln3), (-ln3, -0.25 * ln3)):
+        x = np.array([[1.0, 0.0, 1.0, 0.0, xv]])  # q (dk = 2) | k (dk = 2) | v (dv = 1)
+        o, S, _ = gdn_prompt(x, np.ones((1, 1)), np.ones((1, 1)), np.ones((5, 1)), H=1, dk=2, dv=1, act="silu")
+        np.testing.assert_allclose(o[0, 0, 0], want, rtol=1e-5)
+        o0, _, _ = gdn_prompt(x, np.ones((1, 1)), np.ones((1, 1)), np.ones((5, 1)), H=1, dk=2, dv=1)
+        np.testing.assert_allclose(o0[0, 0, 0], xv, rtol=1e-5)
