@@ -130,7 +130,8 @@ def check_round(rnd, got, lay, mode="memo", requests=None, questions=None, attn_
     rep: dict = {}
     for j in (range(len(rnd.requests)) if requests is None else requests):
         attn_rows = attn_rows_fn(j) if attn_rows_fn else None
-        ref = oround.run_request(rnd, j, conv_w, mode, questions=questions, attn_rows=attn_rows)
+        ref = oround.run_request(rnd, j, conv_w, mode, questions=questions, attn_rows=attn_rows,
+                                 act=rnd.shapes.gdn_act)
         compare_request(rnd, lay, got, ref, j, off, rep)
     print(f"[parity] {rep} (tol {tol}, tv {TV_TOL})", flush=True)
     for key in ("attn_o", "swa_o", "gdn_o", "S_P"):

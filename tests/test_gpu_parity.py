@@ -188,11 +188,13 @@ def test_short_rounds_full_size_graph_bucket(ctx):
     harness.check_round(rnd, harness.outputs(bufs), lay, mode="memo", requests=[0, 31, 63])
 
 
-@pytest.mark.parametrize("dtype", ["bf16"])
-def test_edge_cases_chunked_gdn(ctx, dtype):
+@pytest.mark.parametrize("dtype,act", [("bf16", "none"), ("bf16", "silu")])
+def test_edge_cases_chunked_gdn(ctx, dtype, act):
     """dk = dv = 128 routes the GDN layer to the chunked MFMA kernel: partial chunks, a question longer
-    than one chunk, empty and short trunks, resumes with fewer new rows than the conv width."""
-    sh = LayerShapes(H=2, dk=128, dv=128, conv_k=4, Hq=4, Hkv=1, d=128, theta=1e4, hidden=64, swa_window=40)
+    than one chunk, empty and short trunks, resumes with fewer new rows than the conv width; with and
+    without the SiLU after the conv."""
+    sh = LayerShapes(H=2, dk=128, dv=128, conv_k=4, Hq=4, Hkv=1, d=128, theta=1e4, hidden=64, swa_window=40,
+                     gdn_act=act)
     reqs = _edge_reqs() + [Request(P=300, m=0, q_len=(64, 65), n_opt=(2, 2), out_slot=8)]
     rnd = custom_round(sh, dtype, reqs, base=29)
     bufs, lay = harness.run_gpu(rnd, ctx, "direct")

@@ -242,8 +242,9 @@ __device__ __forceinline__ void diag_inverse(ChunkLds& L, const int (&gq)[4], in
 }  // namespace
 
 // PHASE 0: trunk segments (writes each request's state and conv window); PHASE 1: question segments.
-template <int PHASE>
-__global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K, int act,
+// ACT 1: SiLU after the conv.
+template <int PHASE, int ACT>
+__global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K,
                                                        const bf16_t* __restrict__ x, const float* __restrict__ conv_w,
                                                        const float* __restrict__ alpha,
                                                        const float* __restrict__ eta, float* __restrict__ state_pool,
@@ -400,7 +401,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
       for (int i = 0; i < 4; ++i) {
         auto xv = [&](int k) { return __uint_as_float(vraw[rb][k] << 16); };
         float acc = vw[0] * xv(i) + vw[1] * xv(i + 1) + vw[2] * xv(i + 2) + vw[3] * xv(i + 3);
-        if (act == 1) acc = silu(acc);
+        if (ACT == 1) acc = silu(acc);
         vv[rb][i] = acc;
       }
     // ---- conv + L2 norm of q and k -> fp16 hi/lo tiles ----
@@ -423,7 +424,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
             return (c & 1) ? __uint_as_float(wv & 0xFFFF0000u) : __uint_as_float(wv << 16);
           };
           float acc = wt.x * xv(jr) + wt.y * xv(jr + 1) + wt.z * xv(jr + 2) + wt.w * xv(jr + 3);
-          if (act == 1) acc = silu(acc);
+          if (ACT == 1) acc = silu(acc);
           y[c] = acc;
         }
         float ss = 0.f;
@@ -582,8 +583,9 @@ int launch_gdn(const MetaView& mv, const flide_gdn_params& p, int phase, const v
   if (!gdn_uses_chunk(p) || !offsets_fit)
     return launch_gdn_plain(mv, p, phase, x, conv_w, alpha, eta, state_pool, conv_pool, n_slots, o, stream);
   dim3 grid(phase == 0 ? mv.R_cap : (mv.Q_cap > 0 ? mv.Q_cap : 1), p.H);
-  hipLaunchKernelGGL(phase == 0 ? gdn_chunk_kernel<0> : gdn_chunk_kernel<1>, grid, dim3(NT), 0, (hipStream_t)stream,
-                     mv, p.H, p.conv_k, p.act,
+  auto kern = phase == 0 ? (p.act == 1 ? gdn_chunk_kernel<0, 1> : gdn_chunk_kernel<0, 0>)
+                        : (p.act == 1 ? gdn_chunk_kernel<1, 1> : gdn_chunk_kernel<1, 0>);
+  hipLaunchKernelGGL(kern, grid, dim3(NT), 0, (hipStream_t)stream, mv, p.H, p.conv_k,
                      (const bf16_t*)x, conv_w, alpha, eta, state_pool, (bf16_t*)conv_pool, n_slots, (bf16_t*)o);
   return int(hipGetLastError());
 }

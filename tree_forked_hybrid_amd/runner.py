@@ -72,7 +72,8 @@ class RoundBuffers:
             nbytes = F.flide_attn_workspace_bytes(self.caps, p)
             self.ws.append(torch.zeros(nbytes, dtype=torch.uint8, device=device))
         C = s.channels
-        self.gdn_params = F.flide_gdn_params(s.H, s.dk, s.dv, s.conv_k, 0, 64, _flide_dtype(spec.dtype), 0)
+        act = 1 if getattr(s, "gdn_act", "none") == "silu" else 0
+        self.gdn_params = F.flide_gdn_params(s.H, s.dk, s.dv, s.conv_k, act, 64, _flide_dtype(spec.dtype), 0)
         self.x = z(T, C)
         self.conv_w = z(C, s.conv_k, dtype=torch.float32)
         self.alpha = z(T, s.H, dtype=torch.float32)

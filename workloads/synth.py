@@ -71,6 +71,7 @@ class LayerShapes:
     # readout
     hidden: int
     swa_window: int = 0  # 0: no sliding-window layer in the round
+    gdn_act: str = "none"  # activation after the GDN conv: "none" or "silu"
 
     @property
     def channels(self) -> int:
