@@ -115,6 +115,11 @@ typedef struct {
  *   gdn_order   [seg_cap]  GDN work list: trunk segments, then question segments,
  *                          each by length, longest first (ties in stream order)
  *   tok_j/c/t   [T_cap]    per-row metadata (device only)
+ *   tile_desc   [tile_cap * 16] per attention work-list position: segment (-1 if
+ *                          unused), first row, rows, first position, m, P, checkpoint
+ *                          slot, question flag, key-row and value-column offsets of
+ *                          the trunk and own ranges, first position of the segment
+ *                          (device only)
  *   dev_error   [4]        device error word (device only)                     */
 typedef struct {
   int64_t host_words;
@@ -126,6 +131,7 @@ typedef struct {
   int64_t tile_seg, tile_row0;
   int64_t gdn_order;
   int64_t tok_j, tok_c, tok_t;
+  int64_t tile_desc;
   int64_t dev_error;
   int32_t seg_cap;
   int32_t tile_cap;

@@ -310,23 +310,30 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   const bool active = hl < G;
   const int h = kvh * G + hl;
 
-  const int seg = mv.tile_seg[tile];
-  if (seg == -1) return;  // unused position of the work list
-  if (seg < 0 || seg >= mv.hdr[H_NSEG]) {
-    if (tid == 0) flag_error(mv.dev_error, E_SEGMENT);
-    return;
+  // the position's descriptor (written by meta_expand): one 64-byte load instead of a chain of table lookups
+  int32_t td[kTileDescWords];
+  {
+    const int4* src = reinterpret_cast<const int4*>(mv.tile_desc + int64_t(tile) * kTileDescWords);
+#pragma unroll
+    for (int i = 0; i < kTileDescWords / 4; ++i) {
+      const int4 v = src[i];
+      td[4 * i] = v.x;
+      td[4 * i + 1] = v.y;
+      td[4 * i + 2] = v.z;
+      td[4 * i + 3] = v.w;
+    }
   }
-  const int seg_row0 = mv.seg_row0[seg], seg_len = mv.seg_len[seg], pos0 = mv.seg_pos0[seg];
-  const int j = mv.seg_req[seg];
-  const bool question = mv.seg_branch[seg] > 0;
-  const int P = mv.req_P[j], m = mv.req_m[j], ckpt = mv.req_ckpt[j];
+  const int seg = td[TD_SEG];
+  if (seg < 0) return;  // unused position (an inconsistent segment was flagged by meta_expand)
+  const bool question = td[TD_QUESTION] != 0;
+  const int P = td[TD_P], m = td[TD_M], ckpt = td[TD_CKPT], pos0 = td[TD_POS0];
   if (m > 0 && (m > cache_rows || k_cache == nullptr || ckpt < 0 || ckpt >= cache_slots)) {
     if (tid == 0) flag_error(mv.dev_error, E_CACHE);
     return;
   }
-  const int x0 = mv.tile_row0[tile];
-  const int nrows = min(kTileRows, seg_row0 + seg_len - x0);
-  const int qpos_min = pos0 + (x0 - seg_row0);
+  const int x0 = td[TD_ROW0];
+  const int nrows = td[TD_NROWS];
+  const int qpos_min = td[TD_QPOS0];
   const int qpos_max = qpos_min + nrows - 1;
   if (qpos_max >= max_pos) {
     if (tid == 0) flag_error(mv.dev_error, E_POSITION);
@@ -340,9 +347,8 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   const int lo0 = max(0, lo_w), hi0 = m > 0 ? min(m, qpos_max + 1) : 0;
   const int lo1 = max(m, lo_w), hi1 = question ? P : 0;
   const int lo2 = max(pos0, lo_w), hi2 = qpos_max + 1;
-  const int64_t roff0 = int64_t(ckpt) * cache_rows, roff1 = int64_t(mv.req_trunk_row0[j]) - m,
-                roff2 = int64_t(seg_row0) - pos0;
-  const int64_t voff1 = mv.seg_vcol0[j], voff2 = mv.seg_vcol0[seg];  // trunk segment index = request index
+  const int64_t roff0 = int64_t(ckpt) * cache_rows, roff1 = td[TD_ROFF_TRUNK], roff2 = td[TD_ROFF_OWN];
+  const int64_t voff1 = td[TD_VOFF_TRUNK], voff2 = td[TD_VOFF_OWN];
   const int ts00 = lo0 & ~(BN - 1), ts01 = lo1 & ~(BN - 1), ts02 = lo2 & ~(BN - 1);
   const int n0 = lo0 < hi0 ? (hi0 - ts00 + BN - 1) / BN : 0;
   const int n1 = lo1 < hi1 ? (hi1 - ts01 + BN - 1) / BN : 0;
@@ -409,33 +415,47 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   if (n_tiles > 0) issue(0, 0);
 
   // ---- rotated, pre-scaled queries as MFMA B fragments (query = column) ----
+  // All query and rotation-table loads are issued up front (lanes past the tile's rows read its first
+  // row and are zeroed afterwards), so the prologue waits for one memory round trip, not one per chunk.
   const float sl2 = 1.4426950408889634f * rsqrtf(float(D));
   u32x4v qf[2][NC];
   int qpos[2];
+  {
+    u32x4v qa[2][NC / 2], qb_[2][NC / 2];
+    float4 cs4[2][NC / 2][4];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int r = qb * 16 + r16;
-    const bool qv = active && r < nrows;
-    qpos[qb] = qpos_min + r;
+    for (int qb = 0; qb < 2; ++qb) {
+      const int r = qb * 16 + r16;
+      const int rr = (active && r < nrows) ? r : 0;
+      qpos[qb] = qpos_min + r;
+      const int64_t rowbase = (int64_t(x0 + rr) * Hq + h) * D + 8 * g4;
+      const float* csrow = table + (int64_t(qpos_min + rr) * (D / 2) + 8 * g4) * 2;
 #pragma unroll
-    for (int c = 0; c < NC / 2; ++c) {
-      u32x4v lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-      if (qv) {
-        const int64_t base = (int64_t(x0 + r) * Hq + h) * D + 32 * c + 8 * g4;
-        const u32x4v a = *reinterpret_cast<const u32x4v*>(q + base);
-        const u32x4v b = *reinterpret_cast<const u32x4v*>(q + base + D / 2);
-        const float* cs = table + (int64_t(qpos[qb]) * (D / 2) + 32 * c + 8 * g4) * 2;
+      for (int c = 0; c < NC / 2; ++c) {
+        qa[qb][c] = *reinterpret_cast<const u32x4v*>(q + rowbase + 32 * c);
+        qb_[qb][c] = *reinterpret_cast<const u32x4v*>(q + rowbase + 32 * c + D / 2);
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) cs4[qb][c][ww] = *reinterpret_cast<const float4*>(csrow + 64 * c + 4 * ww);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const bool qv = active && qb * 16 + r16 < nrows;
+#pragma unroll
+      for (int c = 0; c < NC / 2; ++c) {
+        u32x4v lo, hi;
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
-          float a0 = __uint_as_float(a[ww] << 16), a1 = __uint_as_float(a[ww] & 0xFFFF0000u);
-          float b0 = __uint_as_float(b[ww] << 16), b1 = __uint_as_float(b[ww] & 0xFFFF0000u);
-          float c0 = cs[4 * ww], s0 = cs[4 * ww + 1], c1 = cs[4 * ww + 2], s1 = cs[4 * ww + 3];
-          lo[ww] = pack_bf16x2((a0 * c0 - b0 * s0) * sl2, (a1 * c1 - b1 * s1) * sl2);
-          hi[ww] = pack_bf16x2((b0 * c0 + a0 * s0) * sl2, (b1 * c1 + a1 * s1) * sl2);
+          const uint32_t av = qa[qb][c][ww], bv = qb_[qb][c][ww];
+          const float a0 = __uint_as_float(av << 16), a1 = __uint_as_float(av & 0xFFFF0000u);
+          const float b0 = __uint_as_float(bv << 16), b1 = __uint_as_float(bv & 0xFFFF0000u);
+          const float4 t4 = cs4[qb][c][ww];  // (cos, sin) of two consecutive pairs
+          lo[ww] = pack_bf16x2((a0 * t4.x - b0 * t4.y) * sl2, (a1 * t4.z - b1 * t4.w) * sl2);
+          hi[ww] = pack_bf16x2((b0 * t4.x + a0 * t4.y) * sl2, (b1 * t4.z + a1 * t4.w) * sl2);
         }
+        qf[qb][c] = qv ? lo : u32x4v{0u, 0u, 0u, 0u};
+        qf[qb][c + NC / 2] = qv ? hi : u32x4v{0u, 0u, 0u, 0u};
       }
-      qf[qb][c] = lo;
-      qf[qb][c + NC / 2] = hi;
     }
   }
 

@@ -11,6 +11,10 @@ namespace flide {
 constexpr int kTileRows = 32;
 // XCDs of the chip: workgroup i of a grid runs on XCD i mod kXcdClasses.
 constexpr int kXcdClasses = 8;
+// int32 words of one attention work-list descriptor (filled on the device by meta_expand).
+constexpr int kTileDescWords = 16;
+enum TileDesc { TD_SEG, TD_ROW0, TD_NROWS, TD_QPOS0, TD_M, TD_P, TD_CKPT, TD_QUESTION, TD_ROFF_TRUNK, TD_ROFF_OWN,
+                TD_VOFF_TRUNK, TD_VOFF_OWN, TD_POS0 };
 // Words of the metadata header.
 constexpr int kHdrWords = 64;
 constexpr int32_t kMagic = 0x464C4944;  // 'FLID'
@@ -65,6 +69,7 @@ struct MetaView {
   int32_t* tok_j;
   int32_t* tok_c;
   int32_t* tok_t;
+  int32_t* tile_desc;
   int32_t* dev_error;
   int32_t T_cap, R_cap, Q_cap, seg_cap, tile_cap;
 };
@@ -93,6 +98,7 @@ inline MetaView make_view(int32_t* base, const flide_meta_layout& L, const flide
   v.tok_j = base + L.tok_j;
   v.tok_c = base + L.tok_c;
   v.tok_t = base + L.tok_t;
+  v.tile_desc = base + L.tile_desc;
   v.dev_error = base + L.dev_error;
   v.T_cap = c.T_cap;
   v.R_cap = c.R_cap;

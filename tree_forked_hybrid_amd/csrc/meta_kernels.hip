@@ -3,8 +3,10 @@
 // meta_expand turns the uploaded segment table into per-row (j, c, t) labels
 // ("Flide: Accelerating Decision Inference with Exact State Forking"
 // §方法步骤详情: every token carries request, branch and position; question
-// positions continue from P) and marks tail rows (-1, -1, -1) (Korean summary
-// §어떻게 쓰나: padding only at the tail).
+// positions continue from P), marks tail rows (-1, -1, -1) (Korean summary
+// §어떻게 쓰나: padding only at the tail), and writes one descriptor per
+// attention work-list position (tile_desc), so that an attention workgroup
+// reads its segment, request and key ranges with one 64-byte load.
 //
 // rope_k rotates every key row once to its metadata position (rotate-half
 // pairs (i, i + d/2), angle t * theta^(-2i/d), host fp64 table stored fp32), so
@@ -20,6 +22,38 @@ __global__ void __launch_bounds__(256) meta_expand_kernel(MetaView mv) {
                    mv.hdr[H_R] < 0 || mv.hdr[H_R] > mv.R_cap || mv.hdr[H_NQST] < 0 ||
                    mv.hdr[H_NQST] > mv.Q_cap || mv.hdr[H_NTILES] < 0 || mv.hdr[H_NTILES] > mv.tile_cap;
   const int stride = gridDim.x * blockDim.x;
+  // attention work-list descriptors: everything a tile's workgroup needs, in one 64-byte record
+  const int n_tiles = bad ? 0 : mv.hdr[H_NTILES];
+  for (int x = blockIdx.x * blockDim.x + threadIdx.x; x < mv.tile_cap; x += stride) {
+    int32_t d[kTileDescWords];
+#pragma unroll
+    for (int i = 0; i < kTileDescWords; ++i) d[i] = 0;
+    d[TD_SEG] = -1;
+    const int s = x < n_tiles ? mv.tile_seg[x] : -1;
+    if (s >= 0 && s < n_seg) {
+      const int j = mv.seg_req[s];
+      const int row0 = mv.seg_row0[s], pos0 = mv.seg_pos0[s];
+      const int x0 = mv.tile_row0[x];
+      d[TD_SEG] = s;
+      d[TD_ROW0] = x0;
+      d[TD_NROWS] = min(kTileRows, row0 + mv.seg_len[s] - x0);
+      d[TD_QPOS0] = pos0 + (x0 - row0);
+      d[TD_M] = mv.req_m[j];
+      d[TD_P] = mv.req_P[j];
+      d[TD_CKPT] = mv.req_ckpt[j];
+      d[TD_QUESTION] = mv.seg_branch[s] > 0 ? 1 : 0;
+      d[TD_ROFF_TRUNK] = mv.req_trunk_row0[j] - mv.req_m[j];
+      d[TD_ROFF_OWN] = row0 - pos0;
+      d[TD_VOFF_TRUNK] = mv.seg_vcol0[j];  // the trunk segment of request j is segment j
+      d[TD_VOFF_OWN] = mv.seg_vcol0[s];
+      d[TD_POS0] = pos0;
+    } else if (s != -1) {
+      flag_error(mv.dev_error, E_SEGMENT);
+    }
+    int4* dst = reinterpret_cast<int4*>(mv.tile_desc + int64_t(x) * kTileDescWords);
+#pragma unroll
+    for (int i = 0; i < kTileDescWords / 4; ++i) dst[i] = int4{d[4 * i], d[4 * i + 1], d[4 * i + 2], d[4 * i + 3]};
+  }
   if (bad) {
     if (blockIdx.x == 0 && threadIdx.x == 0) flag_error(mv.dev_error, E_HEADER);
     for (int row = blockIdx.x * blockDim.x + threadIdx.x; row < mv.T_cap; row += stride) {
@@ -53,7 +87,7 @@ __global__ void clear_error_kernel(int32_t* dev_error) {
 }
 
 int launch_meta_expand(const MetaView& mv, void* stream) {
-  int blocks = (mv.T_cap + 255) / 256;
+  int blocks = (max(mv.T_cap, mv.tile_cap) + 255) / 256;
   if (blocks > 2048) blocks = 2048;
   hipLaunchKernelGGL(meta_expand_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, mv);
   return int(hipGetLastError());

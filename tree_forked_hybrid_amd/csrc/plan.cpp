@@ -50,6 +50,7 @@ flide_status compute_layout(const flide_caps& c, flide_meta_layout& L) {
   L.tok_j = take(c.T_cap);
   L.tok_c = take(c.T_cap);
   L.tok_t = take(c.T_cap);
+  L.tile_desc = take(int64_t(L.tile_cap) * kTileDescWords);
   L.dev_error = take(4);
   L.dev_words = o;
   return FLIDE_OK;

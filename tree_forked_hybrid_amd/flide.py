@@ -46,7 +46,7 @@ class flide_meta_layout(C.Structure):
     _fields_ = [(n, C.c_int64) for n in (
         "host_words", "dev_words", "hdr", "seg_row0", "seg_len", "seg_req", "seg_branch", "seg_pos0",
         "seg_state", "seg_vcol0", "req_trunk_row0", "req_P", "req_m", "req_ckpt", "req_out", "req_q_seg0", "req_nq",
-        "qfin_row", "tile_seg", "tile_row0", "gdn_order", "tok_j", "tok_c", "tok_t", "dev_error")] + \
+        "qfin_row", "tile_seg", "tile_row0", "gdn_order", "tok_j", "tok_c", "tok_t", "tile_desc", "dev_error")] + \
         [("seg_cap", C.c_int32), ("tile_cap", C.c_int32), ("tile_rows", C.c_int32), ("reserved", C.c_int32)]
 
 
