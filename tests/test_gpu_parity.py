@@ -224,3 +224,63 @@ def test_split_round_graph_buckets_and_eager(ctx):
         else:
             bufs, lay = harness.run_gpu(sub, ctx, "graph", bufs=bucket)
         harness.check_round(sub, harness.outputs(bufs), lay, mode="memo")
+
+
+def _sample_rows(rnd, j, questions, n_trunk=48, seed=0):
+    """Request-local rows whose attention the oracle computes: random trunk rows, both trunk ends, and
+    the first, middle and last row of each checked question."""
+    r = rnd.requests[j]
+    tn = r.P - r.m
+    rows = []
+    if tn > 0:
+        rng = np.random.default_rng(seed + j)
+        rows = sorted(set(rng.choice(tn, min(n_trunk, tn), replace=False).tolist()) | {0, tn - 1})
+    segs = rnd.segment_rows(j)
+    for i in questions:
+        s, L = segs[1 + i]
+        rows += sorted({s, s + L // 2, s + L - 1})
+    return rows
+
+
+def test_long_document_rounds_full_size(ctx):
+    """Whole long-document round (4 requests, 48 questions each, full and sliding-window attention) in a
+    32768-row bucket graph; requests 0 and 3 checked on sampled attention rows, every GDN row of the
+    checked segments, the trunk states and the readout."""
+    from tree_forked_hybrid_amd.runner import spec_for_round
+    rnd = make_round(2, 0)
+    spec = spec_for_round(rnd, T_cap=32768, R_cap=4, Q_cap=192)
+    bufs, lay = harness.run_gpu(rnd, ctx, "graph", spec=spec)
+    qs = [0, 23, 47]
+    harness.check_round(rnd, harness.outputs(bufs), lay, mode="memo", requests=[0, 3], questions=qs,
+                        attn_rows_fn=lambda j: _sample_rows(rnd, j, qs, n_trunk=24))
+
+
+def test_agent_resume_rounds_full_size(ctx):
+    """Whole agent-resume round (8 trajectories resumed at m = 30720 from checkpoint slots, 2048 new rows
+    and 8 questions each) in deterministic mode; the last trajectory checked on sampled rows (the first is
+    checked alone at full size elsewhere, and bitwise composition invariance ties the two together)."""
+    from tree_forked_hybrid_amd.runner import spec_for_round
+    rnd = make_round(4, 0)
+    spec = spec_for_round(rnd, T_cap=20480)
+    bufs, lay = harness.run_gpu(rnd, ctx, "graph", spec=spec)
+    qs = [0, 7]
+    harness.check_round(rnd, harness.outputs(bufs), lay, mode="memo", requests=[7], questions=qs,
+                        attn_rows_fn=lambda j: _sample_rows(rnd, j, qs, n_trunk=12))
+
+
+def test_fan_out_round_first_split_full_size(ctx):
+    """The 64-question fan-out round exceeds one capacity: split at request boundaries into <= 65536-row
+    sub-rounds; the first sub-round runs in a 65536-row bucket graph and its first and last requests are
+    checked on sampled rows (two questions each)."""
+    from tree_forked_hybrid_amd import flide as F
+    from tree_forked_hybrid_amd.runner import spec_for_round
+    full = make_round(3, 0)
+    first, eager = F.flide_split_round(full.requests, full.t_max)
+    assert len(eager) >= 3 and not any(eager)
+    sub = full.subset(list(range(first[0], first[1])))
+    spec = spec_for_round(sub, T_cap=65536)
+    bufs, lay = harness.run_gpu(sub, ctx, "graph", spec=spec)
+    qs = [0, 63]
+    last = len(sub.requests) - 1
+    harness.check_round(sub, harness.outputs(bufs), lay, mode="memo", requests=[0, last], questions=qs,
+                        attn_rows_fn=lambda j: _sample_rows(sub, j, qs, n_trunk=32))

@@ -106,6 +106,7 @@ class RoundBuffers:
         names = ["attn_q", "attn_k", "attn_v"] + (["swa_q", "swa_k", "swa_v"] if self.n_attn == 2 else []) + \
                 ["gdn_x", "alpha", "eta", "hidden"]
         host = {}
+        pls = [rnd.payload(j) for j in range(len(rnd.requests))]   # generated once per request
         rows_idx = np.empty(T, np.int64)
         at = 0
         for j in range(len(rnd.requests)):
@@ -121,7 +122,7 @@ class RoundBuffers:
                 at += L
         # concatenated request payloads, in request-local order
         for name in names:
-            parts = [rnd.payload(j)[name] for j in range(len(rnd.requests))]
+            parts = [pl[name] for pl in pls]
             cat = np.concatenate(parts, axis=0) if parts else np.zeros((0,))
             buf = np.zeros((T,) + cat.shape[1:], np.float32)
             buf[rows_idx] = cat
@@ -139,7 +140,7 @@ class RoundBuffers:
         # options: question order of the stream = request order, then question order
         blocks, off = [], [0]
         for j, r in enumerate(rnd.requests):
-            w = rnd.payload(j)["w_opt"]
+            w = pls[j]["w_opt"]
             blocks.append(w)
             for n in r.n_opt:
                 off.append(off[-1] + int(n))
@@ -159,7 +160,7 @@ class RoundBuffers:
         # checkpoints
         for j, r in enumerate(rnd.requests):
             if r.m > 0:
-                pl = rnd.payload(j)
+                pl = pls[j]
                 self.state_pool[r.ckpt_slot].copy_(torch.from_numpy(pl["ckpt_state"]))
                 self.conv_pool[r.ckpt_slot].copy_(torch.from_numpy(pl["ckpt_window"]).to(dt))
                 for layer, pre in enumerate(["kv", "swa_kv"][:self.n_attn]):
