@@ -78,6 +78,26 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// One direct-to-LDS buffer load per lane of BYTES (4 or 16): lane i writes bytes [BYTES i, BYTES i + BYTES)
+// after the wave-uniform LDS byte address lds_addr, read at byte offset voff of the resource (zeros where
+// voff is outside it).  Written as inline asm so that the compiler does not track the copy: it would
+// otherwise make every later LDS access it cannot tell apart from the destination wait for it, while
+// the kernels wait for their copies explicitly (vmcnt), one stage later.  M0 is written here and used
+// by nothing else; the nops cover the SGPR-write and M0-write hazards.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 in the clobber list is intended
+template <int BYTES>
+__device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t r, unsigned lds_addr, int voff) {
+  static_assert(BYTES == 4 || BYTES == 16, "dword or dwordx4 copies");
+  if (BYTES == 16)
+    asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :: "v"(voff), "s"(lds_addr), "s"(r) : "memory", "m0");
+  else
+    asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 1\n\tbuffer_load_dword %0, %2, 0 offen lds"
+                 :: "v"(voff), "s"(lds_addr), "s"(r) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 __device__ __forceinline__ void flag_error(int32_t* dev_error, int32_t bit) { atomicOr(dev_error, bit); }
 
 // Stream row -> segment index: the last segment whose first row is <= row.

@@ -150,25 +150,13 @@ __device__ __forceinline__ void gram_store(ChunkLds& L, f4v acc, int r16, int g4
   *reinterpret_cast<h4v*>(base + 16 * ti * CK + sql[si]) = out;
 }
 
-// One direct-to-LDS buffer load per lane of `bytes` (4 or 16) into the wave-uniform LDS address dst
-// (lane i fills dst + bytes * i).  Written as inline asm so that the compiler does not track it: it
-// would otherwise make every later LDS access it cannot tell apart from dst wait for the copy, while
-// the kernel waits for the copies explicitly, one chunk later.  M0 is written here and used by
-// nothing else in this kernel; the nops cover the SGPR-write and M0-write hazards.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // M0 in the clobber list is intended
+// One direct-to-LDS buffer load per lane of `BYTES` into the LDS address dst (lane i fills
+// dst + BYTES * i); dst must be the same for every lane.
 template <int BYTES>
 __device__ __forceinline__ void lds_copy(__amdgpu_buffer_rsrc_t r, void* dst, int voff) {
-  const unsigned a = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)dst);
-  if (BYTES == 16)
-    asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-                 :: "v"(voff), "s"(a), "s"(r) : "memory", "m0");
-  else
-    asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 1\n\tbuffer_load_dword %0, %2, 0 offen lds"
-                 :: "v"(voff), "s"(a), "s"(r) : "memory", "m0");
+  dma_to_lds<BYTES>(r, __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)dst),
+                    voff);
 }
-#pragma clang diagnostic pop
 
 // Direct-to-LDS copies for the chunk starting at segment row cc: raw rows cc - 3 .. cc + 63 of the
 // head's q, k and v channels (rows outside the segment read as zero), and (wave 0) alpha, eta of rows
