@@ -15,6 +15,8 @@
 // therefore every rounding step of the online softmax — depends only on the
 // request, never on the rest of the round: outputs are bit-identical whatever
 // the round's composition.
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace flide {
@@ -371,17 +373,19 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
     return ti;
   };
   // Lane constants of the copies: wave w issues copy instructions I = w*IPW + ii; lane l of
-  // instruction I fills 16-byte LDS slot 64 I + l.
-  int k_row[IPW], k_off[IPW], v_dd[IPW], v_c[IPW];
+  // instruction I fills 16-byte LDS slot 64 I + l.  Key slot -> row k_row = I * 64 / KCH + l / KCH and
+  // swizzled chunk; the swizzle of a row depends on its bits 0-1 and 3-4 only, so instruction
+  // ii + KP reads the same chunk 4 rows further down.  Value slot -> channel row 16 I + l / 4 and
+  // chunk vc, the same chunk for every instruction.
+  constexpr int KP = 4 * KCH / 64;
+  int k_off0[KP];
 #pragma unroll
-  for (int ii = 0; ii < IPW; ++ii) {
+  for (int ii = 0; ii < KP; ++ii) {
     const int slot = (w * IPW + ii) * 64 + l;
-    k_row[ii] = slot / KCH;
-    const int kc = (slot % KCH) ^ ksw(k_row[ii]);
-    k_off[ii] = (k_row[ii] * Hkv * D + kc * 8) * 2;  // bytes from the tile's first key row
-    v_dd[ii] = slot / (BN / 8);
-    v_c[ii] = (slot % (BN / 8)) ^ ((v_dd[ii] >> 2) & 3);
+    const int krow = slot / KCH;
+    k_off0[ii] = (krow * Hkv * D + (((slot % KCH) ^ ksw(krow)) * 8)) * 2;  // bytes from the tile's first key row
   }
+  const int vc = (l & 3) ^ ((l >> 4) & 3);
   auto issue = [&](int t, int buf) {
     const TileInfo ti = tile_info(t);
     const int ts = ti.ts, lo = ti.lo, hi = ti.hi;
@@ -394,15 +398,18 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
     unsigned char* vl = lds + (2 + buf) * TILE_BYTES;
     const unsigned char* ktile = reinterpret_cast<const unsigned char*>(kbase + (int64_t(ts) + ti.roff) * Hkv * D);
     const unsigned char* vtile = reinterpret_cast<const unsigned char*>(vbase + (int64_t(ts) + ti.voff));
+    int lv = l;
+    asm volatile("" : "+v"(lv));  // recomputed per tile: registers are scarce in the key-tile loop
+    const int voff0 = (((w * IPW * 16) + (lv >> 2)) * vstride + 8 * vc) * 2;
 #pragma unroll
     for (int ii = 0; ii < IPW; ++ii) {
-      int koff = k_off[ii];
-      int voff = (v_dd[ii] * vstride + 8 * v_c[ii]) * 2;
+      int koff = k_off0[ii % KP] + (ii / KP) * 4 * Hkv * D * 2;
+      int voff = voff0 + ii * 16 * vstride * 2;
       if (edge) {  // masked keys read a valid row / value chunk of the range
-        const int p = ts + k_row[ii];
+        const int p = ts + ((w * IPW + ii) * 64 + lv) / KCH;
         const int pc = p < lo ? lo : (p >= hi ? hi - 1 : p);
         koff += (pc - p) * Hkv * D * 2;
-        const int p0 = ts + 8 * v_c[ii];
+        const int p0 = ts + 8 * vc;
         const int lo8 = lo & ~7, hi8 = (hi - 1) & ~7;
         const int p0c = p0 < lo8 ? lo8 : (p0 > hi8 ? hi8 : p0);
         voff += (p0c - p0) * 2;
@@ -465,36 +472,59 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4v{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  // LDS byte offset of this lane's V^T fragment (channel row r16 of a 16-row block, keys 8 g4 .. +7)
+  // LDS byte offsets of this lane's MFMA operand reads.  Key fragment (kb, c) (key row
+  // 8 (r16 / 4) + 4 kb + r16 % 4, chunk 4 c + g4 swizzled) sits at kfrag[c % 4] + kb * 4 * KROW +
+  // 256 (c / 4): the swizzle is the same for both kb and only permutes chunk groups of four, so four
+  // base offsets and immediate offsets cover all of them.  The V^T fragment of 16-channel block db
+  // (channel row r16, keys 8 g4 .. +7) sits at vfrag + db * 16 * VROW.
+  const int krow0 = 8 * (r16 >> 2) + (r16 & 3);
+  const int ks = ksw(krow0);
+  // (bits 6-7 of these offsets hold c % 4 ^ (ks >> 2) and nothing carries into them, so one base
+  // and an XOR give all four)
+  const int kfrag0 = krow0 * KROW + ((g4 ^ (ks & 3)) << 4) + ((ks >> 2) << 6);
   const int vfrag = r16 * VROW + ((g4 ^ ((r16 >> 2) & 3)) << 4);
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+  // One key tile.  Copies of tile t + 1 go out right after the barrier that frees their buffer; the
+  // operand reads run a few fragments ahead of the MFMAs that use them, and the value reads of the
+  // tile are issued before the softmax, which hides their latency.
+  auto step = [&](int t, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile t have landed
-    __syncthreads();                // ... and every wave's; buffer buf^1 is free
-    if (t + 1 < n_tiles) issue(t + 1, buf ^ 1);
-    if (!active) continue;
+    __syncthreads();                // ... and every wave's; buffer BUF ^ 1 is free
+    if (t + 1 < n_tiles) issue(t + 1, BUF ^ 1);
+    if (!active) return;
     const TileInfo cur = tile_info(t);
     const int ts = cur.ts, lo = cur.lo, hi = cur.hi;
-    const unsigned char* kl = lds + buf * TILE_BYTES;
-    const unsigned char* vl = lds + (2 + buf) * TILE_BYTES;
+    const unsigned char* kl = lds + BUF * TILE_BYTES;
+    const unsigned char* vl = lds + (2 + BUF) * TILE_BYTES;
+    int kf = kfrag0;
+    asm volatile("" : "+v"(kf));  // keep the four XORs inside the loop (registers are scarce here)
+    auto kread = [&](int j) {
+      const int kb = j / NC, c = j % NC;
+      return *reinterpret_cast<const u32x4v*>(kl + (kf ^ ((c & 3) << 6)) + kb * 4 * KROW + 256 * (c >> 2));
+    };
+    auto vread = [&](int db) { return *reinterpret_cast<const u32x4v*>(vl + db * 16 * VROW + vfrag); };
 
     // S^T = K Q^T over the 32 keys of the tile (already in log2 units)
     f32x4v s[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb][0] = f32x4v{0.f, 0.f, 0.f, 0.f};
-      s[kb][1] = f32x4v{0.f, 0.f, 0.f, 0.f};
-      const int krow = 8 * (r16 >> 2) + 4 * kb + (r16 & 3);
-      const unsigned char* kr = kl + krow * KROW;
-      const int ks = ksw(krow);
+    for (int kb = 0; kb < 2; ++kb) s[kb][0] = s[kb][1] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    constexpr int KD = 3;  // operand reads in flight
+    u32x4v fa[KD];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const u32x4v a = *reinterpret_cast<const u32x4v*>(kr + (((4 * c + g4) ^ ks) << 4));
-        s[kb][0] = mfma16x16x32(a, qf[0][c], s[kb][0]);
-        s[kb][1] = mfma16x16x32(a, qf[1][c], s[kb][1]);
-      }
+    for (int j = 0; j < KD; ++j) fa[j] = kread(j);
+#pragma unroll
+    for (int j = 0; j < 2 * NC; ++j) {
+      const int kb = j / NC, c = j % NC;
+      const u32x4v a = fa[j % KD];
+      if (j + KD < 2 * NC) fa[j % KD] = kread(j + KD);
+      s[kb][0] = mfma16x16x32(a, qf[0][c], s[kb][0]);
+      s[kb][1] = mfma16x16x32(a, qf[1][c], s[kb][1]);
     }
+    u32x4v fv[KD];
+#pragma unroll
+    for (int j = 0; j < KD; ++j) fv[j] = vread(j);
+
     // mask: key p is visible to query column q iff kmin(q) <= p <= kmax(q)
     const bool full = ts >= lo && ts + BN <= hi && ts + BN - 1 <= qpos_min &&
                       (window == 0 || qpos_max - ts < window);
@@ -545,11 +575,19 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
     // O^T += V^T P^T over the tile's 32 keys (lane k-slots 8 g4 .. +7 = keys 8 g4 .. +7)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const u32x4v a = *reinterpret_cast<const u32x4v*>(vl + db * 16 * VROW + vfrag);
+      const u32x4v a = fv[db % KD];
+      if (db + KD < NDB) fv[db % KD] = vread(db + KD);
       acc[0][db] = mfma16x16x32(a, pf[0], acc[0][db]);
       acc[1][db] = mfma16x16x32(a, pf[1], acc[1][db]);
     }
+  };
+  // unrolled by two so that each buffer's LDS offsets are immediates
+  int t = 0;
+  for (; t + 1 < n_tiles; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    step(t + 1, std::integral_constant<int, 1>{});
   }
+  if (t < n_tiles) step(t, std::integral_constant<int, 0>{});
 
   if (!active) return;
 #pragma unroll
