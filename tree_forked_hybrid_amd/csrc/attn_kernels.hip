@@ -301,7 +301,8 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
 
   // Workgroup i runs on XCD i mod 8: XCD c takes the work-list positions c, c + 8, ... (the planner
   // puts each group of tiles that share keys on one of them), every head group of a position in turn.
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g4 = l >> 4;
+  const int tid = threadIdx.x, l = tid & 63, r16 = l & 15, g4 = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (scalar: LDS copy targets are uniform)
   const int G = Hq / Hkv;
   const int HG = (G + 3) / 4;
   const int HY = Hkv * HG;
@@ -414,8 +415,10 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
         const int p0c = p0 < lo8 ? lo8 : (p0 > hi8 ? hi8 : p0);
         voff += (p0c - p0) * 2;
       }
-      async_copy16(ktile + koff, kl + (w * IPW + ii) * 1024);
-      async_copy16(vtile + voff, vl + (w * IPW + ii) * 1024);
+      // both offsets are >= 0 (clamped rows and chunks stay inside the range): 32-bit unsigned offsets
+      // from a scalar base
+      async_copy16(ktile + uint32_t(koff), kl + (w * IPW + ii) * 1024);
+      async_copy16(vtile + uint32_t(voff), vl + (w * IPW + ii) * 1024);
     }
   };
 
