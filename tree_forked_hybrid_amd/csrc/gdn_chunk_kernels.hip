@@ -178,25 +178,27 @@ __device__ __forceinline__ void issue_chunk_loads(ChunkIn& I, __amdgpu_buffer_rs
   }
 }
 
-// Row R of the substitution (the DPP broadcast lane must be a constant), then the next row.
+// Row R of the substitution (the DPP broadcast lane must be a constant), then the next row.  T starts
+// as the identity; row R becomes e_R - sum_{s<R} A[R][s] T[s][:].  A[R][s] is zero for s >= R (the
+// block is strictly lower), so the products need no mask, and the identity entry of row R stays in
+// place (every earlier row of column R is still zero).
 template <int R>
 struct InvRow {
-  static __device__ __forceinline__ void run(const float (&av)[4], float (&tq)[4], int g4, int col) {
+  static __device__ __forceinline__ void run(const float (&av)[4], float (&tq)[4], int g4) {
     float part[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float a = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(av[i]), 0x150 + R, 0xF, 0xF, false));
-      part[i] = (4 * g4 + i < R) ? a * tq[i] : 0.f;  // A[R][4 g4 + i] T[4 g4 + i][col]
+      part[i] = a * tq[i];  // A[R][4 g4 + i] T[4 g4 + i][col]
     }
     const float tot = rows4_sum((part[0] + part[1]) + (part[2] + part[3]));
-    const float v = (R == col ? 1.f : 0.f) - tot;
-    if (g4 == (R >> 2)) tq[R & 3] = v;
-    InvRow<R + 1>::run(av, tq, g4, col);
+    if (g4 == (R >> 2)) tq[R & 3] -= tot;
+    InvRow<R + 1>::run(av, tq, g4);
   }
 };
 template <>
 struct InvRow<16> {
-  static __device__ __forceinline__ void run(const float (&)[4], float (&)[4], int, int) {}
+  static __device__ __forceinline__ void run(const float (&)[4], float (&)[4], int) {}
 };
 
 // Diagonal block B of A (fp32, from the hi tiles) and T_BB = (I + A_BB)^{-1} by forward
@@ -221,8 +223,10 @@ __device__ __forceinline__ void diag_inverse(ChunkLds& L, const int (&gq)[4], in
     av[i] = s < t ? et * __expf(gt - L.g[s]) * acc[i] : 0.f;
   }
   const int col = r16;
-  float tq[4] = {0.f, 0.f, 0.f, 0.f};  // T[4 g4 + i][col]
-  InvRow<0>::run(av, tq, g4, col);
+  float tq[4];  // T[4 g4 + i][col], from the identity
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tq[i] = 4 * g4 + i == col ? 1.f : 0.f;
+  InvRow<0>::run(av, tq, g4);
 #pragma unroll
   for (int i = 0; i < 4; ++i) L.tinv[B][4 * g4 + i][col] = (_Float16)tq[i];
 }
