@@ -49,8 +49,11 @@ constexpr int CK = 64;   // chunk rows
 constexpr int DK = 128;  // key size
 constexpr int DV = 128;  // value size (8 waves x 16 channels)
 constexpr int NT = 512;  // threads
-constexpr int RAW_ROW = 3 * 128 * 2;                      // bytes of one raw row of a head: q | k | v channels
-constexpr int RAW_COPIES = ((CK + 3) * RAW_ROW + 1023) / 1024;  // 1 KB direct-to-LDS copies per chunk tile
+constexpr int RAW_ROW = 3 * 128 * 2;  // bytes of one raw row of a head: q | k | v channels
+// LDS stride of a raw row: 16 bytes of padding move each row 4 banks along, so the column reads of
+// rows 4 apart (the value conv) fall in different banks
+constexpr int RAW_STRIDE = RAW_ROW + 16;
+constexpr int RAW_COPIES = ((CK + 3) * RAW_STRIDE + 1023) / 1024;  // 1 KB direct-to-LDS copies per chunk tile
 
 __device__ __forceinline__ f4v mma16(h4v a, h4v b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
 __device__ __forceinline__ f4v mma32(h8v a, h8v b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
@@ -171,9 +174,10 @@ __device__ __forceinline__ void issue_chunk_loads(ChunkIn& I, __amdgpu_buffer_rs
   }
   for (int cp = w; cp < RAW_COPIES; cp += NT / 64) {
     const int byte = cp * 1024 + 16 * l;
-    const int row = byte / RAW_ROW, col = byte - row * RAW_ROW;
+    const int row = byte / RAW_STRIDE, col = byte - row * RAW_STRIDE;
     const int chb = (col >> 8) * sect_b + head_b + (col & 255);
-    const int voff = row < CK + 3 ? (cc - 3 + row) * rowb + chb : 0x7FFFFFF0;  // past the tile: zero fill
+    // padding bytes and rows past the tile: zero fill (never read)
+    const int voff = row < CK + 3 && col < RAW_ROW ? (cc - 3 + row) * rowb + chb : 0x7FFFFFF0;
     lds_copy<16>(xr, I.raw + cp * 1024, voff);
   }
 }
@@ -354,7 +358,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
       if (tid_v < 3 * RAW_ROW / 16) {
         const int row = tid_v / (RAW_ROW / 16), col = (tid_v % (RAW_ROW / 16)) * 16;
         const int chb = (col >> 8) * sect_b + head_b + (col & 255);
-        *reinterpret_cast<u4v*>(I.raw + row * RAW_ROW + col) =
+        *reinterpret_cast<u4v*>(I.raw + row * RAW_STRIDE + col) =
             __builtin_amdgcn_raw_buffer_load_b128(hr, (row - 3) * rowb + hoff + chb, 0, 0);
       }
       lds_barrier();
@@ -364,10 +368,10 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int i = 0; i < 7; ++i)
-        vraw[rb][i] = *reinterpret_cast<const unsigned short*>(I.raw + (16 * rb + 4 * g4 + i) * RAW_ROW + 512 + 2 * ncol);
+        vraw[rb][i] = *reinterpret_cast<const unsigned short*>(I.raw + (16 * rb + 4 * g4 + i) * RAW_STRIDE + 512 + 2 * ncol);
     u4v raw[7];  // this thread's q/k row window (8 channels) at tile rows 4 rq + i
 #pragma unroll
-    for (int i = 0; i < 7; ++i) raw[i] = *reinterpret_cast<const u4v*>(I.raw + (4 * rq + i) * RAW_ROW + sec * 256 + 2 * p8);
+    for (int i = 0; i < 7; ++i) raw[i] = *reinterpret_cast<const u4v*>(I.raw + (4 * rq + i) * RAW_STRIDE + sec * 256 + 2 * p8);
     if (w == 0) {
       // g = inclusive prefix sum of log alpha over the chunk
       const int t = l;
