@@ -491,7 +491,10 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
       default: gram_store<6, true>(L, gres[0], r16, g4, sql); gram_store<7, true>(L, gres[1], r16, g4, sql);
                gram_store<8, true>(L, gres[2], r16, g4, sql); break;
     }
-    {
+    // The state after a question's last chunk is not kept (only trunks emit a state), so the question
+    // call skips K^T and the state update there.
+    const bool keep_state = PHASE == 0 || c0 + CK < len;
+    if (keep_state) {
       const int dk = tid_v & 127, tq = tid_v >> 7;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -526,6 +529,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
       __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(p23 >> 16), orr, ob + 3 * rowo, 0, 0);
     }
     // ---- state update S = e^{g_n} S + U^T diag(e^{g_n - g}) K ----
+    if (!keep_state) continue;
     h4v ud[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
