@@ -463,14 +463,18 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
 #pragma unroll
     for (int c = 0; c < 4; ++c) sf[c] = cat8(to_h4(S[2 * c]), to_h4(S[2 * c + 1]));
     f4v qs[4], rhs[4];
+    const bool zero_state = c0 == 0 && in_slot < 0;  // a fresh trunk's first chunk: both products vanish
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       f4v ks = {0.f, 0.f, 0.f, 0.f};
       qs[rb] = f4v{0.f, 0.f, 0.f, 0.f};
+      if (!zero_state) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        ks = mma32(cat8(lds4(L.kh + 16 * rb * DK + kq[c][0]), lds4(L.kh + 16 * rb * DK + kq[c][1])), sf[c], ks);
-        qs[rb] = mma32(cat8(lds4(L.qh + 16 * rb * DK + kq[c][0]), lds4(L.qh + 16 * rb * DK + kq[c][1])), sf[c], qs[rb]);
+        for (int c = 0; c < 4; ++c) {
+          ks = mma32(cat8(lds4(L.kh + 16 * rb * DK + kq[c][0]), lds4(L.kh + 16 * rb * DK + kq[c][1])), sf[c], ks);
+          qs[rb] = mma32(cat8(lds4(L.qh + 16 * rb * DK + kq[c][0]), lds4(L.qh + 16 * rb * DK + kq[c][1])), sf[c],
+                         qs[rb]);
+        }
       }
       const f4v eg4 = *reinterpret_cast<const f4v*>(&L.eg[16 * rb + 4 * g4]);
       const f4v eta4 = *reinterpret_cast<const f4v*>(&L.eta[16 * rb + 4 * g4]);
