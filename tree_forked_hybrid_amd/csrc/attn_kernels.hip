@@ -258,6 +258,34 @@ __device__ __forceinline__ void async_copy16(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds((gbl_vptr_t)(src), (lds_vptr_t)(lds_base), 16, 0, 0);
 }
 
+// MFMA operand read from LDS, written as inline asm so that the compiler does not track it.  The
+// compiler models a direct-to-LDS copy (global_load_lds) as an access that may reach LDS through the
+// flat path; while one is in flight it drains every LDS read (lgkmcnt(0)) before the first use of any
+// of them, which exposes the full LDS latency at each wait.  Reads issued here are waited for
+// explicitly: lds_wait<N>(r) returns once at most N LDS reads issued after r's are outstanding (LDS
+// reads of a wave complete in issue order), and ties r's register to that wait, so nothing uses r
+// before it.  OFF is the instruction's immediate byte offset.
+template <int OFF>
+__device__ __forceinline__ u32x4v lds_read16(unsigned addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset field");
+  u32x4v r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4v& r) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt field");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
+}
+// f(integral_constant<int, I>) for I = B .. E - 1, in order (compile-time indices for the reads above).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // One workgroup = one query tile (32 rows of one segment) x up to 4 q heads of
 // one kv head; wave w owns q head (group * 4 + w).  Scores are computed
 // transposed (S^T = K Q^T: keys on MFMA rows, queries on columns) so that each
@@ -486,6 +514,7 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   // and an XOR give all four)
   const int kfrag0 = krow0 * KROW + ((g4 ^ (ks & 3)) << 4) + ((ks >> 2) << 6);
   const int vfrag = r16 * VROW + ((g4 ^ ((r16 >> 2) & 3)) << 4);
+  const unsigned lds_base = unsigned(uintptr_t((__attribute__((address_space(3))) void*)lds));
 
   // One key tile.  Copies of tile t + 1 go out right after the barrier that frees their buffer; the
   // operand reads run a few fragments ahead of the MFMAs that use them, and the value reads of the
@@ -498,15 +527,19 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
     if (!active) return;
     const TileInfo cur = tile_info(t);
     const int ts = cur.ts, lo = cur.lo, hi = cur.hi;
-    const unsigned char* kl = lds + BUF * TILE_BYTES;
-    const unsigned char* vl = lds + (2 + BUF) * TILE_BYTES;
+    // lane addresses of the operand reads (the array is 1024-byte aligned, so the chunk XOR of bits
+    // 6-7 commutes with adding its base); tile, buffer and block offsets are instruction immediates
     int kf = kfrag0;
     asm volatile("" : "+v"(kf));  // keep the four XORs inside the loop (registers are scarce here)
-    auto kread = [&](int j) {
-      const int kb = j / NC, c = j % NC;
-      return *reinterpret_cast<const u32x4v*>(kl + (kf ^ ((c & 3) << 6)) + kb * 4 * KROW + 256 * (c >> 2));
+    const unsigned kadr = lds_base + unsigned(kf), vadr = lds_base + unsigned(vfrag);
+    auto kread = [&](auto J) {
+      constexpr int j = decltype(J)::value, kb = j / NC, c = j % NC;
+      return lds_read16<BUF * TILE_BYTES + kb * 4 * KROW + 256 * (c >> 2)>(kadr ^ unsigned((c & 3) << 6));
     };
-    auto vread = [&](int db) { return *reinterpret_cast<const u32x4v*>(vl + db * 16 * VROW + vfrag); };
+    auto vread = [&](auto DB) {
+      constexpr int db = decltype(DB)::value;
+      return lds_read16<(2 + BUF) * TILE_BYTES + db * 16 * VROW>(vadr);
+    };
 
     // S^T = K Q^T over the 32 keys of the tile (already in log2 units)
     f32x4v s[2][2];
@@ -514,19 +547,16 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
     for (int kb = 0; kb < 2; ++kb) s[kb][0] = s[kb][1] = f32x4v{0.f, 0.f, 0.f, 0.f};
     constexpr int KD = 3;  // operand reads in flight
     u32x4v fa[KD];
-#pragma unroll
-    for (int j = 0; j < KD; ++j) fa[j] = kread(j);
-#pragma unroll
-    for (int j = 0; j < 2 * NC; ++j) {
-      const int kb = j / NC, c = j % NC;
-      const u32x4v a = fa[j % KD];
-      if (j + KD < 2 * NC) fa[j % KD] = kread(j + KD);
-      s[kb][0] = mfma16x16x32(a, qf[0][c], s[kb][0]);
-      s[kb][1] = mfma16x16x32(a, qf[1][c], s[kb][1]);
-    }
+    static_for<0, KD>([&](auto J) { fa[decltype(J)::value] = kread(J); });
+    static_for<0, 2 * NC>([&](auto J) {
+      constexpr int j = decltype(J)::value, kb = j / NC, c = j % NC;
+      lds_wait<(KD - 1 < 2 * NC - 1 - j ? KD - 1 : 2 * NC - 1 - j)>(fa[j % KD]);
+      s[kb][0] = mfma16x16x32(fa[j % KD], qf[0][c], s[kb][0]);
+      s[kb][1] = mfma16x16x32(fa[j % KD], qf[1][c], s[kb][1]);
+      if constexpr (j + KD < 2 * NC) fa[j % KD] = kread(std::integral_constant<int, j + KD>{});
+    });
     u32x4v fv[KD];
-#pragma unroll
-    for (int j = 0; j < KD; ++j) fv[j] = vread(j);
+    static_for<0, KD>([&](auto J) { fv[decltype(J)::value] = vread(J); });
 
     // mask: key p is visible to query column q iff kmin(q) <= p <= kmax(q)
     const bool full = ts >= lo && ts + BN <= hi && ts + BN - 1 <= qpos_min &&
@@ -576,13 +606,13 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
                       pack_bf16x2(s[1][qb][0], s[1][qb][1]), pack_bf16x2(s[1][qb][2], s[1][qb][3])};
     }
     // O^T += V^T P^T over the tile's 32 keys (lane k-slots 8 g4 .. +7 = keys 8 g4 .. +7)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const u32x4v a = fv[db % KD];
-      if (db + KD < NDB) fv[db % KD] = vread(db + KD);
-      acc[0][db] = mfma16x16x32(a, pf[0], acc[0][db]);
-      acc[1][db] = mfma16x16x32(a, pf[1], acc[1][db]);
-    }
+    static_for<0, NDB>([&](auto DB) {
+      constexpr int db = decltype(DB)::value;
+      lds_wait<(KD - 1 < NDB - 1 - db ? KD - 1 : NDB - 1 - db)>(fv[db % KD]);
+      acc[0][db] = mfma16x16x32(fv[db % KD], pf[0], acc[0][db]);
+      acc[1][db] = mfma16x16x32(fv[db % KD], pf[1], acc[1][db]);
+      if constexpr (db + KD < NDB) fv[db % KD] = vread(std::integral_constant<int, db + KD>{});
+    });
   };
   // unrolled by two so that each buffer's LDS offsets are immediates
   int t = 0;
