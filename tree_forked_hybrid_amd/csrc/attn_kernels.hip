@@ -336,12 +336,13 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   const int HY = Hkv * HG;
   const int i8 = blockIdx.x / kXcdClasses;
   const int tile = kXcdClasses * (i8 / HY) + int(blockIdx.x % kXcdClasses), yy = i8 % HY;
-  if (tile >= mv.hdr[H_NTILES]) return;
   const int kvh = yy / HG, hl = (yy % HG) * 4 + w;
   const bool active = hl < G;
   const int h = kvh * G + hl;
 
-  // the position's descriptor (written by meta_expand): one 64-byte load instead of a chain of table lookups
+  // the position's descriptor (written by meta_expand): one 64-byte load instead of a chain of table
+  // lookups.  The grid has tile_cap positions per head group, so the load is in bounds before the
+  // position is known to be used; issuing it beside the count saves a round trip.
   int32_t td[kTileDescWords];
   {
     const int4* src = reinterpret_cast<const int4*>(mv.tile_desc + int64_t(tile) * kTileDescWords);
@@ -354,6 +355,7 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
       td[4 * i + 3] = v.w;
     }
   }
+  if (tile >= mv.hdr[H_NTILES]) return;
   const int seg = td[TD_SEG];
   if (seg < 0) return;  // unused position (an inconsistent segment was flagged by meta_expand)
   const bool question = td[TD_QUESTION] != 0;
@@ -622,18 +624,33 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   }
   if (t < n_tiles) step(t, std::integral_constant<int, 0>{});
 
+  // Output: each wave stages its 32 x D tile row-major in its quarter of the LDS (16-byte chunk c of
+  // row r at slot c ^ (r % 16): conflict-free for both the 8-byte fragment writes and the 16-byte row
+  // reads), then stores whole rows, 16 bytes per lane.  The accumulator layout would otherwise give
+  // 8-byte pieces of sixteen rows per store.
+  __syncthreads();  // every wave is done with the key and value tiles
   if (!active) return;
+  constexpr int CPR = D / 8;  // 16-byte chunks per output row
+  unsigned char* ow = lds + w * TILE_BYTES;  // BN == 32 rows of D: one wave's output tile
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    if (qb * 16 + r16 >= nrows) continue;
-    const float inv = 1.f / l_run[qb];
-    bf16_t* dst = o + (int64_t(x0 + qb * 16 + r16) * Hq + h) * D + 4 * g4;
+    const int row = qb * 16 + r16;
+    const float inv = row < nrows ? 1.f / l_run[qb] : 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const f32x4v a = acc[qb][db];
-      *reinterpret_cast<u32x2v*>(dst + db * 16) =
+      const int chunk = 2 * db + (g4 >> 1);
+      *reinterpret_cast<u32x2v*>(ow + row * (D * 2) + ((chunk ^ (row & 15)) << 4) + ((g4 & 1) << 3)) =
           u32x2v{pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv)};
     }
+  }
+  constexpr int RPI = 64 / CPR;  // rows per 16-byte-per-lane read (a wave's LDS accesses run in order)
+  const int c16 = l % CPR;
+#pragma unroll
+  for (int k = 0; k < BN / RPI; ++k) {
+    const int row = k * RPI + l / CPR;
+    const u32x4v v = *reinterpret_cast<const u32x4v*>(ow + row * (D * 2) + ((c16 ^ (row & 15)) << 4));
+    if (row < nrows) *reinterpret_cast<u32x4v*>(o + (int64_t(x0 + row) * Hq + h) * D + c16 * 8) = v;
   }
 }
 
