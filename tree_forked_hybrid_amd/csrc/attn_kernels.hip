@@ -452,35 +452,50 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
     }
   };
 
-  if (n_tiles > 0) issue(0, 0);
-
   // ---- rotated, pre-scaled queries as MFMA B fragments (query = column) ----
-  // All query and rotation-table loads are issued up front (lanes past the tile's rows read its first
-  // row and are zeroed afterwards), so the prologue waits for one memory round trip, not one per chunk.
+  // The rotation table rows of the tile's 32 positions are the same for every head: they are copied
+  // once per workgroup into the second key and value buffers (rows 0-15 and 16-31; step 0 refills
+  // those with tile 1 only after the barrier that follows every wave's rotation), 16-byte chunk x of
+  // row r at slot x ^ (r % 16) so that the column reads of the rotation are conflict-free.  Rows past
+  // the tile's end copy its first row; their queries are zeroed.
+  constexpr int RB = D * 4;                 // bytes per table row: (cos, sin) in fp32 for D / 2 pairs
+  constexpr int TCH = RB / 16;              // 16-byte chunks per table row
+  constexpr int TPW = BN * RB / 1024 / 4;   // copy instructions per wave
+  static_assert(BN * RB == 2 * TILE_BYTES && TCH >= 16, "table rows fill the second K and V buffers");
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int I = w * TPW + i;  // uniform: copy instruction I fills image bytes [1024 I, 1024 I + 1024)
+    const int slot_img = I * 64 + l;
+    const int row = slot_img / TCH, slot = slot_img % TCH;
+    const int rr = row < nrows ? row : 0;
+    const unsigned char* src =
+        reinterpret_cast<const unsigned char*>(table) + int64_t(qpos_min + rr) * RB + ((slot ^ (row & 15)) << 4);
+    async_copy16(src, lds + (I * 1024 < TILE_BYTES ? TILE_BYTES + I * 1024 : 3 * TILE_BYTES + I * 1024 - TILE_BYTES));
+  }
   const float sl2 = 1.4426950408889634f * rsqrtf(float(D));
   u32x4v qf[2][NC];
   int qpos[2];
   {
     u32x4v qa[2][NC / 2], qb_[2][NC / 2];
-    float4 cs4[2][NC / 2][4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int r = qb * 16 + r16;
       const int rr = (active && r < nrows) ? r : 0;
       qpos[qb] = qpos_min + r;
       const int64_t rowbase = (int64_t(x0 + rr) * Hq + h) * D + 8 * g4;
-      const float* csrow = table + (int64_t(qpos_min + rr) * (D / 2) + 8 * g4) * 2;
 #pragma unroll
       for (int c = 0; c < NC / 2; ++c) {
         qa[qb][c] = *reinterpret_cast<const u32x4v*>(q + rowbase + 32 * c);
         qb_[qb][c] = *reinterpret_cast<const u32x4v*>(q + rowbase + 32 * c + D / 2);
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) cs4[qb][c][ww] = *reinterpret_cast<const float4*>(csrow + 64 * c + 4 * ww);
       }
     }
+    if (n_tiles > 0) issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's table rows (and everything else) have landed
+    __syncthreads();                // ... and every wave's
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const bool qv = active && qb * 16 + r16 < nrows;
+      const unsigned char* trow = lds + (qb == 0 ? TILE_BYTES : 3 * TILE_BYTES) + r16 * RB;
 #pragma unroll
       for (int c = 0; c < NC / 2; ++c) {
         u32x4v lo, hi;
@@ -489,7 +504,8 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
           const uint32_t av = qa[qb][c][ww], bv = qb_[qb][c][ww];
           const float a0 = __uint_as_float(av << 16), a1 = __uint_as_float(av & 0xFFFF0000u);
           const float b0 = __uint_as_float(bv << 16), b1 = __uint_as_float(bv & 0xFFFF0000u);
-          const float4 t4 = cs4[qb][c][ww];  // (cos, sin) of two consecutive pairs
+          // (cos, sin) of pairs 8 g4 + 32 c + 2 ww and the next one: chunk 4 g4 + 16 c + ww of the row
+          const float4 t4 = *reinterpret_cast<const float4*>(trow + (((4 * g4 + 16 * c + ww) ^ r16) << 4));
           lo[ww] = pack_bf16x2((a0 * t4.x - b0 * t4.y) * sl2, (a1 * t4.z - b1 * t4.w) * sl2);
           hi[ww] = pack_bf16x2((b0 * t4.x + a0 * t4.y) * sl2, (b1 * t4.z + a1 * t4.w) * sl2);
         }
