@@ -185,6 +185,12 @@ __host__ __device__ __forceinline__ int64_t vt_cols(int T_cap, int seg_cap) {
 // the row's metadata position) into k_rot [T_cap, Hkv, D], and write the values
 // transposed into vt [Hkv, D, vt_cols]; the value of position p of segment s
 // lands in column seg_vcol0[s] + p, so 8-aligned positions are 16-byte aligned.
+//
+// One workgroup = 64 rows of one kv head.  Every load of a thread is issued before the first use
+// (value rows, key rows and positions, then the rotation table rows at those positions), so a
+// workgroup waits for two memory round trips instead of one per loop step.  Workgroup ids are laid
+// out so that the Hkv workgroups of one row block sit eight apart: they run on the same XCD at about
+// the same time and share the table rows through its L2.
 template <int D>
 __global__ void __launch_bounds__(256) kv_prep_kernel(MetaView mv, const bf16_t* __restrict__ k,
                                                       const bf16_t* __restrict__ v, bf16_t* __restrict__ k_rot,
@@ -192,58 +198,90 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(MetaView mv, const bf16_t*
                                                       int max_pos, int Hkv) {
   constexpr int ROWS = 64;
   constexpr int STR = D + 2;
+  constexpr int HALF = D / 2;
+  constexpr int GROUPS = HALF / 8;             // 8 pairs per key work item
+  constexpr int KIT = ROWS * GROUPS / 256;     // key work items per thread
+  constexpr int VIT = ROWS * (D / 8) / 256;    // 16-byte value chunks per thread
+  static_assert(KIT >= 1 && VIT >= 1, "64 rows over 256 threads");
   __shared__ bf16_t v_lds[ROWS * STR];
-  const int r0 = blockIdx.x * ROWS;
-  const int g = blockIdx.y;
+  const int i8 = blockIdx.x / kXcdClasses;
+  const int rb = kXcdClasses * (i8 / Hkv) + int(blockIdx.x % kXcdClasses), g = i8 % Hkv;
+  const int r0 = rb * ROWS;
   const int T = mv.hdr[H_T];
   if (r0 >= T) return;
   const int tid = threadIdx.x;
-  constexpr int HALF = D / 2;
-  constexpr int GROUPS = HALF / 8;  // 8 pairs per work item
-  for (int it = tid; it < ROWS * GROUPS; it += 256) {
-    const int rr = it / GROUPS, i0 = (it % GROUPS) * 8;
+
+  u32x4v vv[VIT];
+#pragma unroll
+  for (int i = 0; i < VIT; ++i) {
+    const int it = tid + 256 * i, rr = it / (D / 8), ch = it % (D / 8);
+    const int row = min(r0 + rr, T - 1);
+    vv[i] = *reinterpret_cast<const u32x4v*>(v + (int64_t(row) * Hkv + g) * D + ch * 8);
+  }
+  u32x4v ka[KIT], kb[KIT];
+  int kpos[KIT];
+#pragma unroll
+  for (int i = 0; i < KIT; ++i) {
+    const int it = tid + 256 * i, rr = it / GROUPS, i0 = (it % GROUPS) * 8;
+    const int row = min(r0 + rr, T - 1);
+    const int64_t base = (int64_t(row) * Hkv + g) * D;
+    ka[i] = *reinterpret_cast<const u32x4v*>(k + base + i0);
+    kb[i] = *reinterpret_cast<const u32x4v*>(k + base + i0 + HALF);
+    kpos[i] = mv.tok_t[row];
+  }
+  float4 cs[KIT][4];
+#pragma unroll
+  for (int i = 0; i < KIT; ++i) {
+    const int it = tid + 256 * i, i0 = (it % GROUPS) * 8;
+    const int pos = kpos[i] < 0 ? 0 : (kpos[i] >= max_pos ? max_pos - 1 : kpos[i]);
+    const float4* c4 = reinterpret_cast<const float4*>(table + (int64_t(pos) * HALF + i0) * 2);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) cs[i][w] = c4[w];
+  }
+  // values -> LDS (rows past T hold a copy of row T - 1 and are never stored)
+#pragma unroll
+  for (int i = 0; i < VIT; ++i) {
+    const int it = tid + 256 * i, rr = it / (D / 8), ch = it % (D / 8);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(v_lds + rr * STR + ch * 8);
+    dst[0] = vv[i][0];
+    dst[1] = vv[i][1];
+    dst[2] = vv[i][2];
+    dst[3] = vv[i][3];
+  }
+  // rotated keys
+#pragma unroll
+  for (int i = 0; i < KIT; ++i) {
+    const int it = tid + 256 * i, rr = it / GROUPS, i0 = (it % GROUPS) * 8;
     const int row = r0 + rr;
-    if (row >= T) continue;
-    const int pos = mv.tok_t[row];
-    if (pos < 0 || pos >= max_pos) {
-      if (pos >= max_pos) flag_error(mv.dev_error, E_POSITION);
+    if (row >= T || kpos[i] < 0) continue;
+    if (kpos[i] >= max_pos) {
+      flag_error(mv.dev_error, E_POSITION);
       continue;
     }
     const int64_t base = (int64_t(row) * Hkv + g) * D;
-    const u32x4v a = *reinterpret_cast<const u32x4v*>(k + base + i0);
-    const u32x4v b = *reinterpret_cast<const u32x4v*>(k + base + i0 + HALF);
-    const float* cs = table + (int64_t(pos) * HALF + i0) * 2;
     u32x4v lo, hi;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      float a0 = __uint_as_float(a[w] << 16), a1 = __uint_as_float(a[w] & 0xFFFF0000u);
-      float b0 = __uint_as_float(b[w] << 16), b1 = __uint_as_float(b[w] & 0xFFFF0000u);
-      float c0 = cs[4 * w], s0 = cs[4 * w + 1], c1 = cs[4 * w + 2], s1 = cs[4 * w + 3];
-      lo[w] = pack_bf16x2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
-      hi[w] = pack_bf16x2(b0 * c0 + a0 * s0, b1 * c1 + a1 * s1);
+      const float a0 = __uint_as_float(ka[i][w] << 16), a1 = __uint_as_float(ka[i][w] & 0xFFFF0000u);
+      const float b0 = __uint_as_float(kb[i][w] << 16), b1 = __uint_as_float(kb[i][w] & 0xFFFF0000u);
+      const float4 t4 = cs[i][w];  // (cos, sin) of two consecutive pairs
+      lo[w] = pack_bf16x2(a0 * t4.x - b0 * t4.y, a1 * t4.z - b1 * t4.w);
+      hi[w] = pack_bf16x2(b0 * t4.x + a0 * t4.y, b1 * t4.z + a1 * t4.w);
     }
     *reinterpret_cast<u32x4v*>(k_rot + base + i0) = lo;
     *reinterpret_cast<u32x4v*>(k_rot + base + i0 + HALF) = hi;
   }
-  // values: stage the rows in LDS, then write columns (lane = row, so stores coalesce)
-  for (int it = tid; it < ROWS * (D / 8); it += 256) {
-    const int rr = it / (D / 8), ch = it % (D / 8);
-    const int row = r0 + rr;
-    u32x4v val = {0u, 0u, 0u, 0u};
-    if (row < T) val = *reinterpret_cast<const u32x4v*>(v + (int64_t(row) * Hkv + g) * D + ch * 8);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(v_lds + rr * STR + ch * 8);
-    dst[0] = val[0];
-    dst[1] = val[1];
-    dst[2] = val[2];
-    dst[3] = val[3];
-  }
-  __syncthreads();
+  // the row's value column: trunk rows belong to segment j (one trunk segment per request, in request
+  // order), question c of request j to segment req_q_seg0[j] + c - 1; column = seg_vcol0[s] + position
   const int lane = tid & 63, w = tid >> 6;
   const int row = r0 + lane;
-  if (row >= T) return;
-  const int n_seg = mv.hdr[H_NSEG];
-  const int s = find_segment(mv.seg_row0, n_seg, row);
-  const int64_t col = int64_t(mv.seg_vcol0[s]) + mv.seg_pos0[s] + (row - mv.seg_row0[s]);
+  int64_t col = -1;
+  if (row < T) {
+    const int j = mv.tok_j[row], c = mv.tok_c[row], t = mv.tok_t[row];
+    if (j >= 0 && t >= 0) col = int64_t(mv.seg_vcol0[c == 0 ? j : mv.req_q_seg0[j] + c - 1]) + t;
+  }
+  __syncthreads();
+  if (col < 0) return;
   const int64_t VT = vt_cols(mv.T_cap, mv.seg_cap);
   bf16_t* dst = vt + int64_t(g) * D * VT + col;
   for (int dd = w; dd < D; dd += 4) dst[int64_t(dd) * VT] = v_lds[lane * STR + dd];
@@ -688,7 +726,8 @@ int launch_attn_prepare(const MetaView& mv, const flide_attn_params& p, const Ro
   if (attn_uses_mfma(p)) {
     bf16_t* k_rot = (bf16_t*)workspace;
     bf16_t* vt = k_rot + int64_t(mv.T_cap) * p.Hkv * p.d;
-    dim3 pg((mv.T_cap + 63) / 64, p.Hkv);
+    // row blocks rounded up to a multiple of kXcdClasses (see the id layout in kv_prep_kernel)
+    dim3 pg(int((((mv.T_cap + 63) / 64 + kXcdClasses - 1) / kXcdClasses) * kXcdClasses) * p.Hkv);
     if (p.d == 256)
       hipLaunchKernelGGL(kv_prep_kernel<256>, pg, dim3(256), 0, (hipStream_t)stream, mv, (const bf16_t*)k,
                          (const bf16_t*)v, k_rot, vt, rope.table, rope.max_pos, p.Hkv);
