@@ -558,7 +558,7 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4v{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};  // l_run: this lane's share of the sum
   // LDS byte offsets of this lane's MFMA operand reads.  Key fragment (kb, c) (key row
   // 8 (r16 / 4) + 4 kb + r16 % 4, chunk 4 c + g4 swizzled) sits at kfrag[c % 4] + kb * 4 * KROW +
   // 256 (c / 4): the swizzle is the same for both kb and only permutes chunk groups of four, so four
@@ -656,8 +656,7 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
           s[kb][qb][i] = pv;
           rs += pv;
         }
-      rs = rows4_sum(rs);
-      l_run[qb] += rs;
+      l_run[qb] += rs;  // this lane's 8 keys; the four lanes of a column are summed once, at the end
       pf[qb] = u32x4v{pack_bf16x2(s[0][qb][0], s[0][qb][1]), pack_bf16x2(s[0][qb][2], s[0][qb][3]),
                       pack_bf16x2(s[1][qb][0], s[1][qb][1]), pack_bf16x2(s[1][qb][2], s[1][qb][3])};
     }
@@ -689,7 +688,8 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int row = qb * 16 + r16;
-    const float inv = row < nrows ? 1.f / l_run[qb] : 0.f;
+    const float l_col = rows4_sum(l_run[qb]);
+    const float inv = row < nrows ? 1.f / l_col : 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const f32x4v a = acc[qb][db];

@@ -178,22 +178,37 @@ def _check(status: int, where: str, ctx: Optional[int] = None) -> None:
 
 # ----------------------------------------------------------------------------- host structures
 
+# numpy image of struct flide_request (int32 P, m, n_q; pointer q_len; int32 ckpt_slot, out_slot)
+_REQ_DTYPE = np.dtype({"names": ["P", "m", "n_q", "q_len", "ckpt_slot", "out_slot"],
+                       "formats": ["<i4", "<i4", "<i4", "<u8", "<i4", "<i4"],
+                       "offsets": [flide_request.P.offset, flide_request.m.offset, flide_request.n_q.offset,
+                                   flide_request.q_len.offset, flide_request.ckpt_slot.offset,
+                                   flide_request.out_slot.offset],
+                       "itemsize": C.sizeof(flide_request)})
+
+
 class Requests:
-    """A round's requests as a C array (keeps the q_len arrays alive)."""
+    """A round's requests as a C array of flide_request (keeps the q_len storage alive).  Built as one
+    numpy record array: per-field ctypes assignment costs more host time than the planner itself."""
 
     def __init__(self, requests: Sequence):
-        self._keep = []
-        self.arr = (flide_request * max(1, len(requests)))()
-        self.n = len(requests)
-        for j, r in enumerate(requests):
-            ql = np.ascontiguousarray(np.asarray(r.q_len, dtype=np.int32))
-            self._keep.append(ql)
-            self.arr[j].P = int(r.P)
-            self.arr[j].m = int(r.m)
-            self.arr[j].n_q = int(len(ql))
-            self.arr[j].q_len = ql.ctypes.data_as(C.POINTER(C.c_int32)) if len(ql) else None
-            self.arr[j].ckpt_slot = int(r.ckpt_slot)
-            self.arr[j].out_slot = int(r.out_slot)
+        n = len(requests)
+        self.n = n
+        qls = [r.q_len for r in requests]
+        nq = np.fromiter((len(q) for q in qls), np.int64, n)
+        self._q = np.ascontiguousarray(np.concatenate([np.asarray(q, dtype=np.int32).ravel() for q in qls])
+                                       if n and nq.sum() else np.zeros(1, np.int32), dtype=np.int32)
+        rec = np.zeros(max(1, n), _REQ_DTYPE)
+        if n:
+            rec["P"][:n] = np.fromiter((r.P for r in requests), np.int64, n)
+            rec["m"][:n] = np.fromiter((r.m for r in requests), np.int64, n)
+            rec["n_q"][:n] = nq
+            off = np.concatenate([[0], np.cumsum(nq)[:-1]])
+            rec["q_len"][:n] = np.where(nq > 0, self._q.ctypes.data + 4 * off, 0).astype(np.uint64)
+            rec["ckpt_slot"][:n] = np.fromiter((r.ckpt_slot for r in requests), np.int64, n)
+            rec["out_slot"][:n] = np.fromiter((r.out_slot for r in requests), np.int64, n)
+        self._rec = rec
+        self.arr = rec.ctypes.data_as(C.POINTER(flide_request))
 
 
 def caps_of(T_cap: int, R_cap: int, Q_cap: int) -> flide_caps:
