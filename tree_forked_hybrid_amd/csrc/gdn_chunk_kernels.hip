@@ -338,6 +338,15 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
   const __amdgpu_buffer_rsrc_t orr =
       __builtin_amdgcn_make_buffer_rsrc((void*)(o + int64_t(row0) * H * DV), 0, len * rowo, 0x00020000);
   if (len > 0) issue_chunk_loads(I, xr, ar, er, 0, w, l, rowb, head_b, sect_b, H * 4);
+  // rows -3 .. -1 of the first chunk: the conv history window (K - 1 rows; older rows stay zero), loaded
+  // beside the first chunk's copies and patched into the tile once those have landed
+  constexpr int HIST_THREADS = 3 * RAW_ROW / 16;
+  u4v hist_v = {0u, 0u, 0u, 0u};
+  if (hist != nullptr && tid < HIST_THREADS) {
+    const int row = tid / (RAW_ROW / 16), col = (tid % (RAW_ROW / 16)) * 16;
+    const int chb = (col >> 8) * sect_b + head_b + (col & 255);
+    hist_v = __builtin_amdgcn_raw_buffer_load_b128(hr, (row - 3) * rowb + hoff + chb, 0, 0);
+  }
 
   _Float16* const am = L.kl;           // -A [t][s] (strictly lower blocks), after the Gram products
   _Float16* const pm = L.kl + CK * CK;  // P [t][s] (lower blocks)
@@ -354,12 +363,9 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
     lds_barrier();                  // ... and every wave's; the previous chunk is done with the LDS tiles
     if (c0 == 0 && hist != nullptr) {
-      // rows -3 .. -1 of the first chunk: the conv history window (K - 1 rows; older rows stay zero)
-      if (tid_v < 3 * RAW_ROW / 16) {
+      if (tid_v < HIST_THREADS) {
         const int row = tid_v / (RAW_ROW / 16), col = (tid_v % (RAW_ROW / 16)) * 16;
-        const int chb = (col >> 8) * sect_b + head_b + (col & 255);
-        *reinterpret_cast<u4v*>(I.raw + row * RAW_STRIDE + col) =
-            __builtin_amdgcn_raw_buffer_load_b128(hr, (row - 3) * rowb + hoff + chb, 0, 0);
+        *reinterpret_cast<u4v*>(I.raw + row * RAW_STRIDE + col) = hist_v;
       }
       lds_barrier();
     }
