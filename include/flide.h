@@ -103,7 +103,9 @@ typedef struct {
  * per-row arrays tok_j/tok_c/tok_t and the device error words are filled on the
  * device.  Segments are ordered trunks first (index j = request j), then
  * questions in stream order.
- *   hdr[0..15]  T, R, n_seg, n_qst, n_tiles, max_pos, 0..., magic
+ *   hdr[0..15]  T, R, n_seg, n_qst, n_tiles, max_pos, tile_group, 0..., magic  (tile_group: attention
+ *               work order, 0 = every head group of a tile position in turn, n = runs of n positions
+ *               per head group; chosen by the planner for rounds whose tiles see thousands of keys)
  *   seg_*       [seg_cap]  row0, len, req, branch, pos0, state (slot or -1),
  *                          vcol0: column offset of the segment in the transposed
  *                          value workspace (column = vcol0 + position, so that

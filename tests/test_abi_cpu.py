@@ -94,6 +94,17 @@ def test_planner_matches_oracle_on_workloads(config):
     assert got["max_pos"] == max(r.P + max(r.q_len) for r in rnd.requests)
 
 
+@pytest.mark.parametrize("config,group", [(0, 0), (1, 0), (2, 0), (4, 64)])
+def test_planner_attention_work_order(config, group):
+    # Rounds whose tiles see >= 4096 keys on average (agent-resume: 30,720 cached keys per request)
+    # take the tile-group order; the short and long-document rounds keep the default order.
+    rnd = make_round(config, 0)
+    T = sum((r.P - r.m) + sum(r.q_len) for r in rnd.requests)
+    caps = F.caps_of(T + 5, len(rnd.requests), sum(len(r.q_len) for r in rnd.requests))
+    got = _planner_layout(rnd.requests, caps)
+    assert got["tile_group"] == group
+
+
 def test_planner_worked_example_tiles():
     rnd = make_round(0, 0)
     got = _planner_layout(rnd.requests, F.caps_of(69, 1, 3))

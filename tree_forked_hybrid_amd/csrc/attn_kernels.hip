@@ -366,23 +366,25 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * TILE_BYTES];  // K0 K1 V0 V1
 
   // Workgroup i runs on XCD i mod 8: XCD c takes the work-list positions c, c + 8, ... (the planner
-  // puts each group of tiles that share keys on one of them), every head group of a position in turn.
+  // puts each group of tiles that share keys on one of them).  By default every head group of a
+  // position runs in turn (neighbouring workgroups share one query tile's keys); when the planner sets
+  // a tile group n (rounds whose tiles see thousands of keys each), a run of n positions of the class
+  // goes first for head group 0, then for head group 1, and so on, so that the workgroups resident on
+  // an XCD at one time stream the same kv head's keys through its L2.
   const int tid = threadIdx.x, l = tid & 63, r16 = l & 15, g4 = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (scalar: LDS copy targets are uniform)
   const int G = Hq / Hkv;
   const int HG = (G + 3) / 4;
   const int HY = Hkv * HG;
   const int i8 = blockIdx.x / kXcdClasses;
-  const int tile = kXcdClasses * (i8 / HY) + int(blockIdx.x % kXcdClasses), yy = i8 % HY;
-  const int kvh = yy / HG, hl = (yy % HG) * 4 + w;
-  const bool active = hl < G;
-  const int h = kvh * G + hl;
+  const int xcd = int(blockIdx.x % kXcdClasses);
+  int tile = kXcdClasses * (i8 / HY) + xcd, yy = i8 % HY;
 
   // the position's descriptor (written by meta_expand): one 64-byte load instead of a chain of table
   // lookups.  The grid has tile_cap positions per head group, so the load is in bounds before the
-  // position is known to be used; issuing it beside the count saves a round trip.
+  // position is known to be used; issuing it beside the header saves a round trip.
   int32_t td[kTileDescWords];
-  {
+  auto load_desc = [&]() {
     const int4* src = reinterpret_cast<const int4*>(mv.tile_desc + int64_t(tile) * kTileDescWords);
 #pragma unroll
     for (int i = 0; i < kTileDescWords / 4; ++i) {
@@ -392,8 +394,22 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
       td[4 * i + 2] = v.z;
       td[4 * i + 3] = v.w;
     }
+  };
+  load_desc();
+  const int n_tiles_round = mv.hdr[H_NTILES];
+  const int K8 = mv.tile_cap / kXcdClasses;  // positions per class
+  const int tgroup = min(max(mv.hdr[H_TGROUP], 0), K8);
+  if (tgroup > 0) {  // tile-group order: a bijection of the same (position, head group) pairs
+    const int sb = i8 / (tgroup * HY), first = sb * tgroup, run = min(tgroup, K8 - first);
+    const int rem = i8 - sb * tgroup * HY;
+    tile = kXcdClasses * (first + rem % run) + xcd;
+    yy = rem / run;
+    load_desc();
   }
-  if (tile >= mv.hdr[H_NTILES]) return;
+  if (tile >= n_tiles_round) return;
+  const int kvh = yy / HG, hl = (yy % HG) * 4 + w;
+  const bool active = hl < G;
+  const int h = kvh * G + hl;
   const int seg = td[TD_SEG];
   if (seg < 0) return;  // unused position (an inconsistent segment was flagged by meta_expand)
   const bool question = td[TD_QUESTION] != 0;

@@ -27,6 +27,7 @@ enum : int {
   H_NQST = 3,
   H_NTILES = 4,
   H_MAXPOS = 5,
+  H_TGROUP = 6,  // attention work order: 0 = head groups of a position together, n > 0 = runs of n positions
   H_MAGIC = 15,
 };
 

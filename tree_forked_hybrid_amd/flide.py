@@ -259,7 +259,8 @@ def decode_image(image: np.ndarray, caps: flide_caps) -> dict:
     L = flide_meta_layout_for(caps)
     hdr = image[L.hdr:L.hdr + 16]
     T, R, n_seg, n_qst, n_tiles = (int(v) for v in hdr[:5])
-    out = {"T": T, "R": R, "n_seg": n_seg, "n_qst": n_qst, "n_tiles": n_tiles, "max_pos": int(hdr[5])}
+    out = {"T": T, "R": R, "n_seg": n_seg, "n_qst": n_qst, "n_tiles": n_tiles, "max_pos": int(hdr[5]),
+           "tile_group": int(hdr[6])}
     for name in ("seg_row0", "seg_len", "seg_req", "seg_branch", "seg_pos0", "seg_state", "seg_vcol0"):
         off = getattr(L, name)
         out[name] = image[off:off + n_seg].copy()
