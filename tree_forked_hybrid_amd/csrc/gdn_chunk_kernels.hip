@@ -68,6 +68,14 @@ __device__ __forceinline__ h8v lds8(const _Float16* p) { return *reinterpret_cas
 // tile (A, P, K^T) keeps chunk c of row r at c ^ ((r >> 1) & 7).  Both make the
 // MFMA operand reads (16 rows x 16 or 8 bytes) bank-conflict free.
 __device__ __forceinline__ int qk_off(int t, int c) { return t * DK + ((((c >> 3) ^ (t & 15))) << 3) + (c & 7); }
+// The q/k tiles hold their key channels permuted within each block of 32: channel 32 b + 16 h + 4 g + i
+// sits at column 32 b + 8 g + 4 h + i.  A 16-byte operand chunk 4 c + g4 then holds channels
+// 32 c + 16 h + 4 g4 + i (h = 0, 1), exactly the k-slots of the state fragment built from the
+// registers S[2 c], S[2 c + 1], so K S0^T and Q S0^T read each operand with one 16-byte access.  The
+// Gram products contract both operands over the same columns and do not see the permutation.
+__device__ __forceinline__ int dk_col(int x) {
+  return (x & ~31) + (((x >> 2) & 3) << 3) + (((x >> 4) & 1) << 2) + (x & 3);
+}
 __device__ __forceinline__ int sq_off(int r, int c) { return r * CK + ((((c >> 3) ^ ((r >> 1) & 7))) << 3) + (c & 7); }
 
 // sum over the 16 lanes of a DPP row (butterfly: quad swaps, half-row and row mirrors)
@@ -313,12 +321,6 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
   int gq[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) gq[c] = r16 * DK + ((((4 * c + g4) ^ r16)) << 3);
-  // q/k tile, 8-byte operands at columns 32 c + 16 hh + 4 g4
-  int kq[4][2];
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) kq[c][hh] = r16 * DK + ((((4 * c + 2 * hh + (g4 >> 1)) ^ r16)) << 3) + 4 * (g4 & 1);
   // [rows][64] tiles, 8-byte operands at columns 16 jb + 4 g4
   int sql[4];
 #pragma unroll
@@ -442,9 +444,23 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
           hv[c] = hi;
           lv[c] = (_Float16)(nv - (float)hi);
         }
-        const int wo = t * DK + ((r16 ^ (4 * g4 + jr)) << 3);
-        *reinterpret_cast<h8v*>(th + wo) = hv;
-        *reinterpret_cast<h8v*>(tl + wo) = lv;
+        // Channels 8 r16 .. +7 fall into columns of two 16-byte chunks (see dk_col), each shared with
+        // the thread two lanes over (r16 ^ 2): the lower thread of the pair keeps both first halves, the
+        // upper one both second halves, swapping the other half through a DPP quad permutation.
+        const bool upper = (r16 & 2) != 0;
+        u4v hb = __builtin_bit_cast(u4v, hv), lb = __builtin_bit_cast(u4v, lv);
+        const uint32_t hs0 = upper ? hb[0] : hb[2], hs1 = upper ? hb[1] : hb[3];
+        const uint32_t ls0 = upper ? lb[0] : lb[2], ls1 = upper ? lb[1] : lb[3];
+        const uint32_t hr0 = __builtin_amdgcn_mov_dpp(hs0, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+        const uint32_t hr1 = __builtin_amdgcn_mov_dpp(hs1, 0x4E, 0xF, 0xF, false);
+        const uint32_t lr0 = __builtin_amdgcn_mov_dpp(ls0, 0x4E, 0xF, 0xF, false);
+        const uint32_t lr1 = __builtin_amdgcn_mov_dpp(ls1, 0x4E, 0xF, 0xF, false);
+        hb = upper ? u4v{hr0, hr1, hb[2], hb[3]} : u4v{hb[0], hb[1], hr0, hr1};
+        lb = upper ? u4v{lr0, lr1, lb[2], lb[3]} : u4v{lb[0], lb[1], lr0, lr1};
+        const int pch = 4 * (r16 >> 2) + 2 * (r16 & 1) + (upper ? 1 : 0);  // physical chunk of the row
+        const int wo = t * DK + ((pch ^ (4 * g4 + jr)) << 3);
+        *reinterpret_cast<u4v*>(th + wo) = hb;
+        *reinterpret_cast<u4v*>(tl + wo) = lb;
       }
     }
     lds_barrier();
@@ -477,9 +493,8 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
       if (!zero_state) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          ks = mma32(cat8(lds4(L.kh + 16 * rb * DK + kq[c][0]), lds4(L.kh + 16 * rb * DK + kq[c][1])), sf[c], ks);
-          qs[rb] = mma32(cat8(lds4(L.qh + 16 * rb * DK + kq[c][0]), lds4(L.qh + 16 * rb * DK + kq[c][1])), sf[c],
-                         qs[rb]);
+          ks = mma32(lds8(L.kh + 16 * rb * DK + gq[c]), sf[c], ks);
+          qs[rb] = mma32(lds8(L.qh + 16 * rb * DK + gq[c]), sf[c], qs[rb]);
         }
       }
       const f4v eg4 = *reinterpret_cast<const f4v*>(&L.eg[16 * rb + 4 * g4]);
@@ -505,11 +520,11 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
     // call skips K^T and the state update there.
     const bool keep_state = PHASE == 0 || c0 + CK < len;
     if (keep_state) {
-      const int dk = tid_v & 127, tq = tid_v >> 7;
+      const int dk = tid_v & 127, tq = tid_v >> 7, dc = dk_col(dk);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int t0 = 16 * tq + 4 * jj;
-        const h4v v = {L.kh[qk_off(t0, dk)], L.kh[qk_off(t0 + 1, dk)], L.kh[qk_off(t0 + 2, dk)], L.kh[qk_off(t0 + 3, dk)]};
+        const h4v v = {L.kh[qk_off(t0, dc)], L.kh[qk_off(t0 + 1, dc)], L.kh[qk_off(t0 + 2, dc)], L.kh[qk_off(t0 + 3, dc)]};
         *reinterpret_cast<h4v*>(kt + sq_off(dk, t0)) = v;
       }
     }
