@@ -525,7 +525,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
       for (int jj = 0; jj < 4; ++jj) {
         const int t0 = 16 * tq + 4 * jj;
         const h4v v = {L.kh[qk_off(t0, dc)], L.kh[qk_off(t0 + 1, dc)], L.kh[qk_off(t0 + 2, dc)], L.kh[qk_off(t0 + 3, dc)]};
-        *reinterpret_cast<h4v*>(kt + sq_off(dk, t0)) = v;
+        *reinterpret_cast<h4v*>(kt + sq_off(dk, dk_col(t0))) = v;  // rows t permuted like the q/k columns
       }
     }
     lds_barrier();
@@ -571,8 +571,12 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       f4v acc = S[mb] * egl;
+      // rows t of K^T are permuted within blocks of 32 (dk_col), so chunk 4 p + g4 of a K^T row holds
+      // t = 32 p + 16 h + 4 g4 + i, the k-slots of cat8(ud[2 p], ud[2 p + 1])
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) acc = mma16(lds4(kt + 16 * mb * CK + sql[rb]), ud[rb], acc);
+      for (int p2 = 0; p2 < 2; ++p2)
+        acc = mma32(lds8(kt + 16 * mb * CK + r16 * CK + (((4 * p2 + g4) ^ ((r16 >> 1) & 7)) << 3)),
+                    cat8(ud[2 * p2], ud[2 * p2 + 1]), acc);
       S[mb] = acc;
     }
   }
