@@ -146,7 +146,7 @@ __device__ __forceinline__ f4v gram_block(const ChunkLds& L, const int (&gq)[4])
 
 // decayed, masked Gram block -> fp16 rows of -A (s < t) or P (s <= t)
 template <int B, bool IS_A>
-__device__ __forceinline__ void gram_store(ChunkLds& L, f4v acc, int r16, int g4, const int (&sql)[4]) {
+__device__ __forceinline__ void gram_store(ChunkLds& L, f4v acc, int r16, int g4) {
   constexpr int ti = Tri<B>::ti, si = Tri<B>::si;
   const int t = 16 * ti + r16;
   const float gt = L.g[t], et = L.eta[t];
@@ -157,8 +157,11 @@ __device__ __forceinline__ void gram_store(ChunkLds& L, f4v acc, int r16, int g4
     const float dec = __expf(gt - L.g[s]);
     out[i] = IS_A ? (_Float16)(s < t ? -(et * dec * acc[i]) : 0.f) : (_Float16)(s <= t ? dec * acc[i] : 0.f);
   }
+  // columns s permuted within blocks of 32 like the q/k columns (dk_col): s = 16 si + 4 g4 + i sits at
+  // column 32 (si / 2) + 8 g4 + 4 (si % 2) + i; 16-byte chunks swizzled by row pair as in sq_off
   _Float16* base = IS_A ? L.kl : L.kl + CK * CK;
-  *reinterpret_cast<h4v*>(base + 16 * ti * CK + sql[si]) = out;
+  *reinterpret_cast<h4v*>(base + 16 * ti * CK + r16 * CK + (((4 * (si >> 1) + g4) ^ ((r16 >> 1) & 7)) << 3) +
+                          4 * (si & 1)) = out;
 }
 
 // One direct-to-LDS buffer load per lane of `BYTES` into the LDS address dst (lane i fills
@@ -321,10 +324,6 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
   int gq[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) gq[c] = r16 * DK + ((((4 * c + g4) ^ r16)) << 3);
-  // [rows][64] tiles, 8-byte operands at columns 16 jb + 4 g4
-  int sql[4];
-#pragma unroll
-  for (int jb = 0; jb < 4; ++jb) sql[jb] = r16 * CK + ((((2 * jb + (g4 >> 1)) ^ ((r16 >> 1) & 7))) << 3) + 4 * (g4 & 1);
 
   // The copies of the next chunk are issued once the current chunk's conv is done with the tile; the
   // first chunk's history rows are patched in at its top.
@@ -505,16 +504,16 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
     lds_barrier();  // every wave is done with the lo tiles; the diagonal inverses are in LDS
     // ---- -A, P and K^T over the lo tiles ----
     switch (w) {
-      case 0: gram_store<0, false>(L, gres[0], r16, g4, sql); gram_store<4, false>(L, gres[1], r16, g4, sql); break;
-      case 1: gram_store<1, false>(L, gres[0], r16, g4, sql); gram_store<5, false>(L, gres[1], r16, g4, sql); break;
-      case 2: gram_store<2, false>(L, gres[0], r16, g4, sql); gram_store<6, false>(L, gres[1], r16, g4, sql); break;
-      case 3: gram_store<3, false>(L, gres[0], r16, g4, sql); gram_store<7, false>(L, gres[1], r16, g4, sql); break;
-      case 4: gram_store<8, false>(L, gres[0], r16, g4, sql); break;
-      case 5: gram_store<9, false>(L, gres[0], r16, g4, sql); break;
-      case 6: gram_store<1, true>(L, gres[0], r16, g4, sql); gram_store<3, true>(L, gres[1], r16, g4, sql);
-              gram_store<4, true>(L, gres[2], r16, g4, sql); break;
-      default: gram_store<6, true>(L, gres[0], r16, g4, sql); gram_store<7, true>(L, gres[1], r16, g4, sql);
-               gram_store<8, true>(L, gres[2], r16, g4, sql); break;
+      case 0: gram_store<0, false>(L, gres[0], r16, g4); gram_store<4, false>(L, gres[1], r16, g4); break;
+      case 1: gram_store<1, false>(L, gres[0], r16, g4); gram_store<5, false>(L, gres[1], r16, g4); break;
+      case 2: gram_store<2, false>(L, gres[0], r16, g4); gram_store<6, false>(L, gres[1], r16, g4); break;
+      case 3: gram_store<3, false>(L, gres[0], r16, g4); gram_store<7, false>(L, gres[1], r16, g4); break;
+      case 4: gram_store<8, false>(L, gres[0], r16, g4); break;
+      case 5: gram_store<9, false>(L, gres[0], r16, g4); break;
+      case 6: gram_store<1, true>(L, gres[0], r16, g4); gram_store<3, true>(L, gres[1], r16, g4);
+              gram_store<4, true>(L, gres[2], r16, g4); break;
+      default: gram_store<6, true>(L, gres[0], r16, g4); gram_store<7, true>(L, gres[1], r16, g4);
+               gram_store<8, true>(L, gres[2], r16, g4); break;
     }
     // The state after a question's last chunk is not kept (only trunks emit a state), so the question
     // call skips K^T and the state update there.
@@ -532,11 +531,19 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
     // ---- blocked forward substitution U = (I + A)^{-1} RHS ----
     h4v uh[4];
     f4v u[4];
+    // Rows of -A and P hold their columns s permuted within blocks of 32 (gram_store), so two 16-column
+    // blocks jb = 2 p, 2 p + 1 are one 16-byte operand chunk 4 p + g4 against cat8(uh[2 p], uh[2 p + 1]);
+    // a lone block jb is the 8-byte half 4 (jb % 2) of chunk 4 (jb / 2) + g4.
+    const int swz = (r16 >> 1) & 7;
+    auto pair_off = [&](int p2) { return r16 * CK + (((4 * p2 + g4) ^ swz) << 3); };
+    auto half_off = [&](int jb) { return r16 * CK + (((4 * (jb >> 1) + g4) ^ swz) << 3) + 4 * (jb & 1); };
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       f4v acc = rhs[rb];
 #pragma unroll
-      for (int jb = 0; jb < rb; ++jb) acc = mma16(lds4(am + 16 * rb * CK + sql[jb]), uh[jb], acc);
+      for (int p2 = 0; 2 * p2 + 1 < rb; ++p2)
+        acc = mma32(lds8(am + 16 * rb * CK + pair_off(p2)), cat8(uh[2 * p2], uh[2 * p2 + 1]), acc);
+      if (rb & 1) acc = mma16(lds4(am + 16 * rb * CK + half_off(rb - 1)), uh[rb - 1], acc);
       u[rb] = mma16(lds4(&L.tinv[rb][r16][4 * g4]), to_h4(acc), f4v{0.f, 0.f, 0.f, 0.f});
       uh[rb] = to_h4(u[rb]);
     }
@@ -545,7 +552,9 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
     for (int rb = 0; rb < 4; ++rb) {
       f4v acc = *reinterpret_cast<const f4v*>(&L.eg[16 * rb + 4 * g4]) * qs[rb];
 #pragma unroll
-      for (int jb = 0; jb <= rb; ++jb) acc = mma16(lds4(pm + 16 * rb * CK + sql[jb]), uh[jb], acc);
+      for (int p2 = 0; 2 * p2 + 1 <= rb; ++p2)
+        acc = mma32(lds8(pm + 16 * rb * CK + pair_off(p2)), cat8(uh[2 * p2], uh[2 * p2 + 1]), acc);
+      if ((rb & 1) == 0) acc = mma16(lds4(pm + 16 * rb * CK + half_off(rb)), uh[rb], acc);
       const uint32_t p01 = pack_bf16x2(acc[0], acc[1]), p23 = pack_bf16x2(acc[2], acc[3]);
       const int ob = (c0 + 16 * rb + 4 * g4) * rowo + (h * DV + ncol) * 2;  // row 16 rb + 4 g4 of this chunk
       __builtin_amdgcn_raw_buffer_store_b16((unsigned short)p01, orr, ob, 0, 0);
