@@ -78,6 +78,22 @@ __device__ __forceinline__ int dk_col(int x) {
 }
 __device__ __forceinline__ int sq_off(int r, int c) { return r * CK + ((((c >> 3) ^ ((r >> 1) & 7))) << 3) + (c & 7); }
 
+// Inclusive prefix sum over the 64 lanes on the VALU: shifts by 1, 2, 4 and 8 within each 16-lane row
+// (lanes without a source add zero), then the last lane of row 0 / 2 is added to row 1 / 3 and the last
+// lane of row 1 to rows 2 and 3.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v = dpp_add<0x111, 0xF>(v);  // row_shr:1
+  v = dpp_add<0x112, 0xF>(v);  // row_shr:2
+  v = dpp_add<0x114, 0xF>(v);  // row_shr:4
+  v = dpp_add<0x118, 0xF>(v);  // row_shr:8
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  return dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+}
+
 // sum over the 16 lanes of a DPP row (butterfly: quad swaps, half-row and row mirrors)
 __device__ __forceinline__ float row16_sum(float v) {
   v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
@@ -384,11 +400,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
       const int t = l;
       const float e = t < n ? I.eta[t] : 0.f;
       float gsum = t < n ? __logf(I.alpha[t]) : 0.f;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float up = __shfl_up(gsum, off, 64);
-        if (t >= off) gsum += up;
-      }
+      gsum = wave_prefix_sum(gsum);
       const float gn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gsum), n - 1));
       L.g[t] = gsum;
       L.eta[t] = e;
