@@ -44,6 +44,7 @@ typedef _Float16 h4v __attribute__((ext_vector_type(4)));
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
 
 constexpr int CK = 64;   // chunk rows
 constexpr int DK = 128;  // key size
@@ -117,7 +118,7 @@ struct ChunkLds {
   _Float16 ql[CK * DK];  // q - hi (lo part); after the Gram products: K^T [dk][t]
   _Float16 kl[CK * DK];  // k - hi (lo part); after the Gram products: -A [t][s] then P [t][s]
   _Float16 tinv[4][16][16];
-  float cw[2][8][16][4];  // q/k conv taps [section][channel % 8][channel / 8][tap], right-aligned (tap 3 = current row)
+  float cw[2][8][16][4];  // q/k conv taps [section][channel j][conv thread][tap] (tile writer's channel order), right-aligned
   alignas(16) float g[CK];    // g_t = sum of log alpha over the chunk's rows up to t
   alignas(16) float eta[CK];  // eta_t (0 past the chunk)
   alignas(16) float eg[CK];   // e^{g_t}
@@ -322,12 +323,14 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
     for (int mb = 0; mb < 8; ++mb) S[mb] = f4v{0.f, 0.f, 0.f, 0.f};
   }
   // q/k conv threads: waves 0-3 -> q, 4-7 -> k; row quad rq (rows 4 rq .. 4 rq + 3), channels 8 r16 .. 8 r16 + 7
-  const int sec = w >> 2, rq = (w & 3) * 4 + g4, p8 = 8 * r16;
+  const int sec = w >> 2, rq = (w & 3) * 4 + g4, p8 = 32 * (r16 >> 2) + 4 * (r16 & 3);
   for (int it = tid; it < 2 * DK * 4; it += NT) {
     const int ci = it >> 2, tap = it & 3;
     const int sc = ci / DK, cc = ci % DK;
     const int tau = tap - (4 - K);
-    L.cw[sc][cc & 7][cc >> 3][tap] = tau >= 0 ? conv_w[int64_t((sc ? kch : qch) + cc) * K + tau] : 0.f;
+    // channel cc = 32 b + 16 h + 4 g + i is channel 4 h + i of conv thread 4 b + g (see the tile writer)
+    L.cw[sc][4 * ((cc >> 4) & 1) + (cc & 3)][4 * (cc >> 5) + ((cc >> 2) & 3)][tap] =
+        tau >= 0 ? conv_w[int64_t((sc ? kch : qch) + cc) * K + tau] : 0.f;
   }
   float vw[4];  // this lane's value-channel taps, right-aligned
 #pragma unroll
@@ -392,9 +395,15 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
 #pragma unroll
       for (int i = 0; i < 7; ++i)
         vraw[rb][i] = *reinterpret_cast<const unsigned short*>(I.raw + (16 * rb + 4 * g4 + i) * RAW_STRIDE + 512 + 2 * ncol);
-    u4v raw[7];  // this thread's q/k row window (8 channels) at tile rows 4 rq + i
+    // this thread's q/k row window at tile rows 4 rq + i: channels 32 b + 4 g + (0..3) and 32 b + 16 + 4 g + (0..3)
+    // for r16 = 4 b + g, the two halves of one 16-byte operand chunk of the permuted tiles (dk_col)
+    u4v raw[7];
 #pragma unroll
-    for (int i = 0; i < 7; ++i) raw[i] = *reinterpret_cast<const u4v*>(I.raw + (4 * rq + i) * RAW_STRIDE + sec * 256 + 2 * p8);
+    for (int i = 0; i < 7; ++i) {
+      const unsigned char* rp = I.raw + (4 * rq + i) * RAW_STRIDE + sec * 256 + 2 * p8;
+      const u2v a = *reinterpret_cast<const u2v*>(rp), b = *reinterpret_cast<const u2v*>(rp + 32);
+      raw[i] = u4v{a[0], a[1], b[0], b[1]};
+    }
     if (w == 0) {
       // g = inclusive prefix sum of log alpha over the chunk
       const int t = l;
@@ -455,23 +464,10 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
           hv[c] = hi;
           lv[c] = (_Float16)(nv - (float)hi);
         }
-        // Channels 8 r16 .. +7 fall into columns of two 16-byte chunks (see dk_col), each shared with
-        // the thread two lanes over (r16 ^ 2): the lower thread of the pair keeps both first halves, the
-        // upper one both second halves, swapping the other half through a DPP quad permutation.
-        const bool upper = (r16 & 2) != 0;
-        u4v hb = __builtin_bit_cast(u4v, hv), lb = __builtin_bit_cast(u4v, lv);
-        const uint32_t hs0 = upper ? hb[0] : hb[2], hs1 = upper ? hb[1] : hb[3];
-        const uint32_t ls0 = upper ? lb[0] : lb[2], ls1 = upper ? lb[1] : lb[3];
-        const uint32_t hr0 = __builtin_amdgcn_mov_dpp(hs0, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
-        const uint32_t hr1 = __builtin_amdgcn_mov_dpp(hs1, 0x4E, 0xF, 0xF, false);
-        const uint32_t lr0 = __builtin_amdgcn_mov_dpp(ls0, 0x4E, 0xF, 0xF, false);
-        const uint32_t lr1 = __builtin_amdgcn_mov_dpp(ls1, 0x4E, 0xF, 0xF, false);
-        hb = upper ? u4v{hr0, hr1, hb[2], hb[3]} : u4v{hb[0], hb[1], hr0, hr1};
-        lb = upper ? u4v{lr0, lr1, lb[2], lb[3]} : u4v{lb[0], lb[1], lr0, lr1};
-        const int pch = 4 * (r16 >> 2) + 2 * (r16 & 1) + (upper ? 1 : 0);  // physical chunk of the row
-        const int wo = t * DK + ((pch ^ (4 * g4 + jr)) << 3);
-        *reinterpret_cast<u4v*>(th + wo) = hb;
-        *reinterpret_cast<u4v*>(tl + wo) = lb;
+        // the thread's 8 channels are exactly the permuted tile's chunk r16 (dk_col)
+        const int wo = t * DK + ((r16 ^ (4 * g4 + jr)) << 3);
+        *reinterpret_cast<h8v*>(th + wo) = hv;
+        *reinterpret_cast<h8v*>(tl + wo) = lv;
       }
     }
     lds_barrier();
