@@ -115,8 +115,9 @@ struct ChunkIn {
 struct ChunkLds {
   _Float16 qh[CK * DK];  // normalised q, fp16 (hi part)
   _Float16 kh[CK * DK];  // normalised k, fp16 (hi part)
-  _Float16 ql[CK * DK];  // q - hi (lo part); after the Gram products: K^T [dk][t]
+  _Float16 ql[CK * DK];  // q - hi (lo part)
   _Float16 kl[CK * DK];  // k - hi (lo part); after the Gram products: -A [t][s] then P [t][s]
+  _Float16 kt[DK * CK];  // K^T [dk][t] (hi part), rows t permuted like the q/k columns (dk_col)
   _Float16 tinv[4][16][16];
   float cw[2][8][16][4];  // q/k conv taps [section][channel j][conv thread][tap] (tile writer's channel order), right-aligned
   alignas(16) float g[CK];    // g_t = sum of log alpha over the chunk's rows up to t
@@ -370,7 +371,6 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
 
   _Float16* const am = L.kl;           // -A [t][s] (strictly lower blocks), after the Gram products
   _Float16* const pm = L.kl + CK * CK;  // P [t][s] (lower blocks)
-  _Float16* const kt = L.ql;           // K^T [dk][t]
 
   for (int c0 = 0; c0 < len; c0 += CK) {
     const int n = min(CK, len - c0);
@@ -435,6 +435,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
       float4 wt4[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) wt4[c] = *reinterpret_cast<const float4*>(L.cw[sec][c][r16]);
+      h4v kcol[8];  // hi values of the thread's channels at its four rows
 #pragma unroll
       for (int jr = 0; jr < 4; ++jr) {
         const int t = 4 * rq + jr;
@@ -468,6 +469,16 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
         const int wo = t * DK + ((r16 ^ (4 * g4 + jr)) << 3);
         *reinterpret_cast<h8v*>(th + wo) = hv;
         *reinterpret_cast<h8v*>(tl + wo) = lv;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) kcol[c][jr] = hv[c];
+      }
+      if (sec == 1) {  // K^T: the k threads hold four consecutive rows of each of their 8 channels
+        const int t0 = 4 * rq;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int dk = 32 * (r16 >> 2) + 4 * (r16 & 3) + 16 * (c >> 2) + (c & 3);
+          *reinterpret_cast<h4v*>(L.kt + sq_off(dk, dk_col(t0))) = kcol[c];
+        }
       }
     }
     lds_barrier();
@@ -524,17 +535,8 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
                gram_store<8, true>(L, gres[2], r16, g4); break;
     }
     // The state after a question's last chunk is not kept (only trunks emit a state), so the question
-    // call skips K^T and the state update there.
+    // call skips the state update there.
     const bool keep_state = PHASE == 0 || c0 + CK < len;
-    if (keep_state) {
-      const int dk = tid_v & 127, tq = tid_v >> 7, dc = dk_col(dk);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int t0 = 16 * tq + 4 * jj;
-        const h4v v = {L.kh[qk_off(t0, dc)], L.kh[qk_off(t0 + 1, dc)], L.kh[qk_off(t0 + 2, dc)], L.kh[qk_off(t0 + 3, dc)]};
-        *reinterpret_cast<h4v*>(kt + sq_off(dk, dk_col(t0))) = v;  // rows t permuted like the q/k columns
-      }
-    }
     lds_barrier();
     // ---- blocked forward substitution U = (I + A)^{-1} RHS ----
     h4v uh[4];
@@ -592,7 +594,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
       // t = 32 p + 16 h + 4 g4 + i, the k-slots of cat8(ud[2 p], ud[2 p + 1])
 #pragma unroll
       for (int p2 = 0; p2 < 2; ++p2)
-        acc = mma32(lds8(kt + 16 * mb * CK + r16 * CK + (((4 * p2 + g4) ^ ((r16 >> 1) & 7)) << 3)),
+        acc = mma32(lds8(L.kt + 16 * mb * CK + r16 * CK + (((4 * p2 + g4) ^ ((r16 >> 1) & 7)) << 3)),
                     cat8(ud[2 * p2], ud[2 * p2 + 1]), acc);
       S[mb] = acc;
     }
