@@ -95,6 +95,34 @@ def test_attention_prepare_then_core_equals_fork_attn(ctx, config):
         assert torch.equal(out[:T], ref[:T])
 
 
+def test_attention_work_order_does_not_change_bits(ctx):
+    """The attention launch gives the same bits in every work order the header can select (tile groups
+    of 0 = every head group of a position in turn, 16 and 64 positions per head group): tiles are
+    independent.  Agent-resume requests, whose tiles see > 30k keys, so the planner itself picks 64."""
+    import torch
+    from tree_forked_hybrid_amd import flide as F
+    rnd = make_round(4, 0, requests=range(2))
+    bufs, _ = harness.run_gpu(rnd, ctx, "direct")
+    img = F.flide_plan_round(rnd.requests, bufs.caps)
+    L = F.flide_meta_layout_for(bufs.caps)
+    assert img[L.hdr + 6] == 64
+    T = sum((r.P - r.m) + sum(r.q_len) for r in rnd.requests)
+    outs = []
+    for group in (0, 16, 64):
+        img[L.hdr + 6] = group
+        bufs.upload(ctx, img)
+        p = bufs.attn_params[0]
+        out = torch.zeros_like(bufs.o_attn[0])
+        F.flide_attn_prepare(ctx, bufs.caps, bufs.dev_meta, p, bufs.k[0], bufs.v[0], bufs.ws[0])
+        F.flide_attn_core(ctx, bufs.caps, bufs.dev_meta, p, bufs.q[0], bufs.v[0], bufs.k_cache[0], bufs.v_cache[0],
+                          out, bufs.ws[0])
+        torch.cuda.synchronize()
+        F.flide_check_device(ctx, bufs.caps, bufs.dev_meta)
+        outs.append(out[:T].clone())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    assert torch.equal(outs[2], bufs.o_attn[0][:T])
+
+
 EDGE = LayerShapes(H=2, dk=32, dv=32, conv_k=4, Hq=4, Hkv=2, d=64, theta=1e4, hidden=64, swa_window=5)
 
 
