@@ -483,10 +483,12 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
     }
     lds_barrier();
     if (c0 + CK < len) issue_chunk_loads(I, xr, ar, er, c0 + CK, w, l, rowb, head_b, sect_b, H * 4);
-    // ---- Gram blocks, held in registers until every wave is done with the lo tiles.  Waves 0-6 take
-    // the P blocks and the strictly lower A blocks; wave 7 the diagonal A blocks and their inverses ----
+    // ---- Gram blocks, held in registers until every wave is done with the lo tiles.  Waves 4-7 take
+    // two P blocks each; waves 0-3 the remaining P and strictly lower A blocks and, one each, the
+    // diagonal A blocks and their inverses: the substitution chain runs on the older wave of each SIMD,
+    // which the hardware issues first ----
     f4v gres[3];
-    switch (w) {
+    switch (w ^ 4) {
       case 0: gres[0] = gram_block<0, false>(L, gq); gres[1] = gram_block<4, false>(L, gq); break;
       case 1: gres[0] = gram_block<1, false>(L, gq); gres[1] = gram_block<5, false>(L, gq); break;
       case 2: gres[0] = gram_block<2, false>(L, gq); gres[1] = gram_block<6, false>(L, gq); break;
@@ -522,7 +524,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
     }
     lds_barrier();  // every wave is done with the lo tiles; the diagonal inverses are in LDS
     // ---- -A, P and K^T over the lo tiles ----
-    switch (w) {
+    switch (w ^ 4) {
       case 0: gram_store<0, false>(L, gres[0], r16, g4); gram_store<4, false>(L, gres[1], r16, g4); break;
       case 1: gram_store<1, false>(L, gres[0], r16, g4); gram_store<5, false>(L, gres[1], r16, g4); break;
       case 2: gram_store<2, false>(L, gres[0], r16, g4); gram_store<6, false>(L, gres[1], r16, g4); break;
