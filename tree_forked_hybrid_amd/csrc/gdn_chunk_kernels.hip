@@ -484,21 +484,23 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
     lds_barrier();
     if (c0 + CK < len) issue_chunk_loads(I, xr, ar, er, c0 + CK, w, l, rowb, head_b, sect_b, H * 4);
     // ---- Gram blocks, held in registers until every wave is done with the lo tiles.  Waves 4-7 take
-    // two P blocks each; waves 0-3 the remaining P and strictly lower A blocks and, one each, the
-    // diagonal A blocks and their inverses: the substitution chain runs on the older wave of each SIMD,
-    // which the hardware issues first ----
+    // two P blocks and one strictly lower A block each; waves 0-3 one remaining block and, one each,
+    // the diagonal A blocks and their inverses: the substitution chain runs on the older wave of each
+    // SIMD, which the hardware issues first ----
     f4v gres[3];
     switch (w ^ 4) {
-      case 0: gres[0] = gram_block<0, false>(L, gq); gres[1] = gram_block<4, false>(L, gq); break;
-      case 1: gres[0] = gram_block<1, false>(L, gq); gres[1] = gram_block<5, false>(L, gq); break;
-      case 2: gres[0] = gram_block<2, false>(L, gq); gres[1] = gram_block<6, false>(L, gq); break;
-      case 3: gres[0] = gram_block<3, false>(L, gq); gres[1] = gram_block<7, false>(L, gq); break;
+      case 0: gres[0] = gram_block<0, false>(L, gq); gres[1] = gram_block<4, false>(L, gq);
+              gres[2] = gram_block<1, true>(L, gq); break;
+      case 1: gres[0] = gram_block<1, false>(L, gq); gres[1] = gram_block<5, false>(L, gq);
+              gres[2] = gram_block<3, true>(L, gq); break;
+      case 2: gres[0] = gram_block<2, false>(L, gq); gres[1] = gram_block<6, false>(L, gq);
+              gres[2] = gram_block<6, true>(L, gq); break;
+      case 3: gres[0] = gram_block<3, false>(L, gq); gres[1] = gram_block<7, false>(L, gq);
+              gres[2] = gram_block<7, true>(L, gq); break;
       case 4: gres[0] = gram_block<8, false>(L, gq); diag_inverse<0>(L, gq, r16, g4); break;
       case 5: gres[0] = gram_block<9, false>(L, gq); diag_inverse<1>(L, gq, r16, g4); break;
-      case 6: gres[0] = gram_block<1, true>(L, gq); gres[1] = gram_block<3, true>(L, gq);
-              gres[2] = gram_block<4, true>(L, gq); diag_inverse<2>(L, gq, r16, g4); break;
-      default: gres[0] = gram_block<6, true>(L, gq); gres[1] = gram_block<7, true>(L, gq);
-               gres[2] = gram_block<8, true>(L, gq); diag_inverse<3>(L, gq, r16, g4); break;
+      case 6: gres[0] = gram_block<4, true>(L, gq); diag_inverse<2>(L, gq, r16, g4); break;
+      default: gres[0] = gram_block<8, true>(L, gq); diag_inverse<3>(L, gq, r16, g4); break;
     }
     // ---- K S0^T and Q S0^T for this wave's channels, and the solve's right-hand side ----
     h8v sf[4];  // S as the B operand (k-slots permuted to match the register layout)
@@ -523,18 +525,20 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
       for (int i = 0; i < 4; ++i) rhs[rb][i] = eta4[i] * (vv[rb][i] - eg4[i] * ks[i]);
     }
     lds_barrier();  // every wave is done with the lo tiles; the diagonal inverses are in LDS
-    // ---- -A, P and K^T over the lo tiles ----
+    // ---- -A and P over the lo tiles ----
     switch (w ^ 4) {
-      case 0: gram_store<0, false>(L, gres[0], r16, g4); gram_store<4, false>(L, gres[1], r16, g4); break;
-      case 1: gram_store<1, false>(L, gres[0], r16, g4); gram_store<5, false>(L, gres[1], r16, g4); break;
-      case 2: gram_store<2, false>(L, gres[0], r16, g4); gram_store<6, false>(L, gres[1], r16, g4); break;
-      case 3: gram_store<3, false>(L, gres[0], r16, g4); gram_store<7, false>(L, gres[1], r16, g4); break;
+      case 0: gram_store<0, false>(L, gres[0], r16, g4); gram_store<4, false>(L, gres[1], r16, g4);
+              gram_store<1, true>(L, gres[2], r16, g4); break;
+      case 1: gram_store<1, false>(L, gres[0], r16, g4); gram_store<5, false>(L, gres[1], r16, g4);
+              gram_store<3, true>(L, gres[2], r16, g4); break;
+      case 2: gram_store<2, false>(L, gres[0], r16, g4); gram_store<6, false>(L, gres[1], r16, g4);
+              gram_store<6, true>(L, gres[2], r16, g4); break;
+      case 3: gram_store<3, false>(L, gres[0], r16, g4); gram_store<7, false>(L, gres[1], r16, g4);
+              gram_store<7, true>(L, gres[2], r16, g4); break;
       case 4: gram_store<8, false>(L, gres[0], r16, g4); break;
       case 5: gram_store<9, false>(L, gres[0], r16, g4); break;
-      case 6: gram_store<1, true>(L, gres[0], r16, g4); gram_store<3, true>(L, gres[1], r16, g4);
-              gram_store<4, true>(L, gres[2], r16, g4); break;
-      default: gram_store<6, true>(L, gres[0], r16, g4); gram_store<7, true>(L, gres[1], r16, g4);
-               gram_store<8, true>(L, gres[2], r16, g4); break;
+      case 6: gram_store<4, true>(L, gres[0], r16, g4); break;
+      default: gram_store<8, true>(L, gres[0], r16, g4); break;
     }
     // The state after a question's last chunk is not kept (only trunks emit a state), so the question
     // call skips the state update there.
