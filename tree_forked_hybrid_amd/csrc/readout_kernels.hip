@@ -62,32 +62,51 @@ __global__ void __launch_bounds__(256) readout_kernel(MetaView mv, int hidden, c
   const int o0 = opt_off[qi], o1 = opt_off[qi + 1];
   // logits with a running max and a rescaled running sum (every lane holds the
   // wave-reduced values); lane 0 stores the logits and later normalises them
-  // itself, so no lane reads another lane's global store.
+  // itself, so no lane reads another lane's global store.  Options go in
+  // batches of four: their row loads and wave reductions are independent, so
+  // a batch waits for one memory round trip instead of one per option.
+  constexpr int OB = 4;
   float zmax = -INFINITY, se = 0.f;
-  for (int k = o0; k < o1; ++k) {
-    const int orow = opt_id[k];
-    if (orow < 0 || orow >= n_opt_rows) {
-      if (lane == 0) {
-        flag_error(mv.dev_error, E_OPTION);
-        probs[k] = -INFINITY;
-      }
-      continue;
+  for (int kb = o0; kb < o1; kb += OB) {
+    int orow[OB];
+    bool ok[OB];
+#pragma unroll
+    for (int j = 0; j < OB; ++j) {
+      orow[j] = kb + j < o1 ? opt_id[kb + j] : 0;
+      ok[j] = kb + j < o1 && orow[j] >= 0 && orow[j] < n_opt_rows;
     }
-    float acc = 0.f;
+    float acc[OB] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
       if (c * 64 + lane < chunks) {
-        float wv[8];
-        load8(w_opt + int64_t(orow) * hidden + (c * 64 + lane) * 8, wv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc += hv[c][e] * wv[e];
+        for (int j = 0; j < OB; ++j) {
+          if (!ok[j]) continue;
+          float wv[8];
+          load8(w_opt + int64_t(orow[j]) * hidden + (c * 64 + lane) * 8, wv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[j] += hv[c][e] * wv[e];
+        }
       }
     }
-    acc = wave_sum(acc);
-    const float znew = fmaxf(zmax, acc);
-    se = (zmax == -INFINITY ? 0.f : se * __expf(zmax - znew)) + __expf(acc - znew);
-    zmax = znew;
-    if (lane == 0) probs[k] = acc;
+#pragma unroll
+    for (int j = 0; j < OB; ++j) acc[j] = wave_sum(acc[j]);
+#pragma unroll
+    for (int j = 0; j < OB; ++j) {
+      const int k = kb + j;
+      if (k >= o1) break;
+      if (!ok[j]) {
+        if (lane == 0) {
+          flag_error(mv.dev_error, E_OPTION);
+          probs[k] = -INFINITY;
+        }
+        continue;
+      }
+      const float znew = fmaxf(zmax, acc[j]);
+      se = (zmax == -INFINITY ? 0.f : se * __expf(zmax - znew)) + __expf(acc[j] - znew);
+      zmax = znew;
+      if (lane == 0) probs[k] = acc[j];
+    }
   }
   if (lane == 0) {
     const float inv = se > 0.f ? 1.f / se : 0.f;
