@@ -584,13 +584,9 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const f4v egn4 = *reinterpret_cast<const f4v*>(&L.egn[16 * rb + 4 * g4]);
-      f4v v4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * rb + 4 * g4 + i;
-        v4[i] = t < n ? egn4[i] * u[rb][i] : 0.f;
-      }
-      ud[rb] = to_h4(v4);
+      // rows past the chunk contribute nothing: egn is 0 there, and u is exactly 0 (eta = 0 makes their
+      // right-hand sides and their rows of A vanish)
+      ud[rb] = to_h4(egn4 * u[rb]);
     }
     const float egl = L.egl;
 #pragma unroll
