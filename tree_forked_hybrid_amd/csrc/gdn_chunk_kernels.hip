@@ -97,10 +97,10 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
 
 // sum over the 16 lanes of a DPP row (butterfly: quad swaps, half-row and row mirrors)
 __device__ __forceinline__ float row16_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));  // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));  // row_mirror
   return v;
 }
 
@@ -221,7 +221,7 @@ struct InvRow {
     float part[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float a = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(av[i]), 0x150 + R, 0xF, 0xF, false));
+      const float a = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(av[i]), 0x150 + R, 0xF, 0xF, true));
       part[i] = a * tq[i];  // A[R][4 g4 + i] T[4 g4 + i][col]
     }
     const float tot = rows4_sum((part[0] + part[1]) + (part[2] + part[3]));
@@ -323,15 +323,17 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) S[mb] = f4v{0.f, 0.f, 0.f, 0.f};
   }
+  constexpr float kQkTapScale = ACT == 1 ? 1.4426950408889634f : 1.f;
   // q/k conv threads: waves 0-3 -> q, 4-7 -> k; row quad rq (rows 4 rq .. 4 rq + 3), channels 8 r16 .. 8 r16 + 7
   const int sec = w >> 2, rq = (w & 3) * 4 + g4, p8 = 32 * (r16 >> 2) + 4 * (r16 & 3);
   for (int it = tid; it < 2 * DK * 4; it += NT) {
     const int ci = it >> 2, tap = it & 3;
     const int sc = ci / DK, cc = ci % DK;
     const int tau = tap - (4 - K);
-    // channel cc = 32 b + 16 h + 4 g + i is channel 4 h + i of conv thread 4 b + g (see the tile writer)
+    // channel cc = 32 b + 16 h + 4 g + i is channel 4 h + i of conv thread 4 b + g (see the tile writer);
+    // with SiLU the taps carry a factor log2(e) (the conv's output then feeds exp2 directly)
     L.cw[sc][4 * ((cc >> 4) & 1) + (cc & 3)][4 * (cc >> 5) + ((cc >> 2) & 3)][tap] =
-        tau >= 0 ? conv_w[int64_t((sc ? kch : qch) + cc) * K + tau] : 0.f;
+        tau >= 0 ? kQkTapScale * conv_w[int64_t((sc ? kch : qch) + cc) * K + tau] : 0.f;
   }
   float vw[4];  // this lane's value-channel taps, right-aligned
 #pragma unroll
@@ -449,21 +451,22 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
             return (c & 1) ? __uint_as_float(wv & 0xFFFF0000u) : __uint_as_float(wv << 16);
           };
           float acc = wt.x * xv(jr) + wt.y * xv(jr + 1) + wt.z * xv(jr + 2) + wt.w * xv(jr + 3);
-          if (ACT == 1) acc = silu(acc);
+          // SiLU of u = acc / log2(e), times log2(e): acc sigmoid(u), with e^-u = 2^-acc
+          if (ACT == 1) acc *= __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-acc));
           y[c] = acc;
         }
         float ss = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) ss += y[c] * y[c];
         ss = row16_sum(ss);
-        const float inv = t < n ? rsqrtf(ss + 1e-6f) : 0.f;
+        // the L2 norm is blind to the common factor log2(e) but for its epsilon, scaled to match
+        const float inv = t < n ? rsqrtf(ss + 1e-6f * kQkTapScale * kQkTapScale) : 0.f;
         h8v hv, lv;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const float nv = y[c] * inv;
-          const _Float16 hi = (_Float16)nv;
+        for (int c = 0; c < 8; ++c) {  // hi and lo of y inv, each one fused multiply-add rounded to fp16
+          const _Float16 hi = (_Float16)__builtin_fmaf(y[c], inv, 0.f);
           hv[c] = hi;
-          lv[c] = (_Float16)(nv - (float)hi);
+          lv[c] = (_Float16)__builtin_fmaf(y[c], inv, -(float)hi);
         }
         // the thread's 8 channels are exactly the permuted tile's chunk r16 (dk_col)
         const int wo = t * DK + ((r16 ^ (4 * g4 + jr)) << 3);
