@@ -420,16 +420,22 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
       if (t == 0) L.egl = __expf(gn);
     }
     // ---- values of this lane's channel at rows 16 rb + 4 g4 + i (the solve's layout) ----
+    // (computed at the end of each wave's share of the Gram stage, pinned there: left to the compiler
+    // it lands after the K S0^T products)
     f4v vv[4];
+    auto value_conv = [&]() {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        auto xv = [&](int k) { return __uint_as_float(vraw[rb][k] << 16); };
-        float acc = vw[0] * xv(i) + vw[1] * xv(i + 1) + vw[2] * xv(i + 2) + vw[3] * xv(i + 3);
-        if (ACT == 1) acc = silu(acc);
-        vv[rb][i] = acc;
-      }
+        for (int i = 0; i < 4; ++i) {
+          auto xv = [&](int k) { return __uint_as_float(vraw[rb][k] << 16); };
+          float acc = vw[0] * xv(i) + vw[1] * xv(i + 1) + vw[2] * xv(i + 2) + vw[3] * xv(i + 3);
+          if (ACT == 1) acc = silu(acc);
+          vv[rb][i] = acc;
+        }
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) asm volatile("" : "+v"(vv[rb]));
+    };
     // ---- conv + L2 norm of q and k -> fp16 hi/lo tiles ----
     {
       _Float16* th = sec ? L.kh : L.qh;
@@ -493,17 +499,17 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
     f4v gres[3];
     switch (w ^ 4) {
       case 0: gres[0] = gram_block<0, false>(L, gq); gres[1] = gram_block<4, false>(L, gq);
-              gres[2] = gram_block<1, true>(L, gq); break;
+              gres[2] = gram_block<1, true>(L, gq); value_conv(); break;
       case 1: gres[0] = gram_block<1, false>(L, gq); gres[1] = gram_block<5, false>(L, gq);
-              gres[2] = gram_block<3, true>(L, gq); break;
+              gres[2] = gram_block<3, true>(L, gq); value_conv(); break;
       case 2: gres[0] = gram_block<2, false>(L, gq); gres[1] = gram_block<6, false>(L, gq);
-              gres[2] = gram_block<6, true>(L, gq); break;
+              gres[2] = gram_block<6, true>(L, gq); value_conv(); break;
       case 3: gres[0] = gram_block<3, false>(L, gq); gres[1] = gram_block<7, false>(L, gq);
-              gres[2] = gram_block<7, true>(L, gq); break;
-      case 4: gres[0] = gram_block<8, false>(L, gq); diag_inverse<0>(L, gq, r16, g4); break;
-      case 5: gres[0] = gram_block<9, false>(L, gq); diag_inverse<1>(L, gq, r16, g4); break;
-      case 6: gres[0] = gram_block<4, true>(L, gq); diag_inverse<2>(L, gq, r16, g4); break;
-      default: gres[0] = gram_block<8, true>(L, gq); diag_inverse<3>(L, gq, r16, g4); break;
+              gres[2] = gram_block<7, true>(L, gq); value_conv(); break;
+      case 4: gres[0] = gram_block<8, false>(L, gq); diag_inverse<0>(L, gq, r16, g4); value_conv(); break;
+      case 5: gres[0] = gram_block<9, false>(L, gq); diag_inverse<1>(L, gq, r16, g4); value_conv(); break;
+      case 6: gres[0] = gram_block<4, true>(L, gq); diag_inverse<2>(L, gq, r16, g4); value_conv(); break;
+      default: gres[0] = gram_block<8, true>(L, gq); diag_inverse<3>(L, gq, r16, g4); value_conv(); break;
     }
     // ---- K S0^T and Q S0^T for this wave's channels, and the solve's right-hand side ----
     h8v sf[4];  // S as the B operand (k-slots permuted to match the register layout)
