@@ -25,7 +25,7 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-from .attention import prompt_attention
+from .attention import prompt_attention, rope_rotate
 from .gdn import gdn_prompt
 from .readout import option_probs
 
@@ -139,6 +139,42 @@ def run_request(rnd, j: int, conv_w: Optional[np.ndarray] = None, mode: str = "m
         off = int(sum(req.n_opt[:i]))
         h = pl["hidden"][qs + L - 1]
         out["probs"][i] = option_probs(h, pl["w_opt"][off:off + req.n_opt[i]])
+    return out
+
+
+def make_checkpoint(rnd, j: int, save_m: int, conv_w: Optional[np.ndarray] = None,
+                    payload: Optional[dict] = None, act: str = "none") -> Dict[str, np.ndarray]:
+    """The checkpoint of request ``j`` at trunk position ``save_m`` (``m < save_m <= P``): what a later
+    round resumes from (Korean summary, §어떻게 쓰나).  It is the trunk-only prompt cut at ``save_m``:
+    the GDN state after position ``save_m - 1``, the raw conv window of the ``K - 1`` positions before
+    ``save_m``, and per attention layer the rotated keys and the values of positions ``0..save_m-1``
+    (positions below the request's own resume point ``m`` are those of its checkpoint).  Keys are named
+    like a resumed request's payload: ``ckpt_state``, ``ckpt_window``, ``kv_k``, ``kv_v`` (and
+    ``swa_kv_k``, ``swa_kv_v`` with a sliding-window layer)."""
+    req = rnd.requests[j]
+    if not req.m < save_m <= req.P:
+        raise ValueError("need m < save_m <= P")
+    sh = rnd.shapes
+    pl = rnd.payload(j) if payload is None else payload
+    if conv_w is None:
+        conv_w = rnd.conv_w()
+    t0, _ = rnd.segment_rows(j)[0]
+    rows = np.arange(t0, t0 + save_m - req.m)
+    pos = np.arange(req.m, save_m)
+    window0 = pl.get("ckpt_window") if req.m > 0 else None
+    S0 = pl.get("ckpt_state") if req.m > 0 else None
+    _, S, win = gdn_prompt(pl["gdn_x"][rows], pl["alpha"][rows], pl["eta"][rows], conv_w, sh.H, sh.dk, sh.dv,
+                           window0, S0, act)
+    out: Dict[str, np.ndarray] = {"ckpt_state": S, "ckpt_window": win}
+    layers = [("attn", "kv")] + ([("swa", "swa_kv")] if sh.swa_window > 0 else [])
+    for name, cpre in layers:
+        kr = rope_rotate(np.asarray(pl[name + "_k"][rows], np.float64), pos[:, None], sh.theta)
+        v = np.asarray(pl[name + "_v"][rows], np.float64)
+        if req.m > 0:
+            kr = np.concatenate([np.asarray(pl[cpre + "_k"], np.float64), kr], axis=0)
+            v = np.concatenate([np.asarray(pl[cpre + "_v"], np.float64), v], axis=0)
+        out[cpre + "_k"] = kr
+        out[cpre + "_v"] = v
     return out
 
 

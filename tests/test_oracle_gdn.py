@@ -186,3 +186,53 @@ def test_silu_option_closed_form():
         np.testing.assert_allclose(o[0, 0, 0], want, rtol=1e-5)
         o0, _, _ = gdn_prompt(x, np.ones((1, 1)), np.ones((1, 1)), np.ones((5, 1)), H=1, dk=2, dv=1)
         np.testing.assert_allclose(o0[0, 0, 0], xv, rtol=1e-5)
+
+
+def _resume_payload(pl: dict, m: int, ckpt: dict) -> dict:
+    """Payload of the same request resumed at m from checkpoint ``ckpt`` (stream rows from m on)."""
+    out = {k: np.asarray(v)[m:] if k in ("attn_q", "attn_k", "attn_v", "gdn_x", "alpha", "eta", "hidden")
+           else v for k, v in pl.items()}
+    out.update(ckpt)
+    return out
+
+
+def test_created_checkpoint_resumes_to_full_run():
+    """make_checkpoint at an interior position, then a resume from it, reproduces the uncut run: GDN
+    outputs, S_P and option probabilities bit for bit, attention to rounding (a checkpoint taken one
+    row off, with unrotated keys or without the conv window fails this)."""
+    full_req = Request(P=14, m=0, q_len=(3, 2), n_opt=(2, 2), out_slot=0)
+    rnd_full = custom_round(SMALL, "f32", [full_req], base=11)
+    cw = rnd_full.conv_w()
+    a = oround.run_request(rnd_full, 0, cw, "isolated")
+    for save_m in (1, 5, 13):
+        ck = oround.make_checkpoint(rnd_full, 0, save_m, cw)
+        res_req = Request(P=14, m=save_m, q_len=(3, 2), n_opt=(2, 2), ckpt_slot=1, out_slot=0)
+        rnd_res = custom_round(SMALL, "f32", [res_req], base=11)
+        b = oround.run_request(rnd_res, 0, cw, "isolated", payload=_resume_payload(rnd_full.payload(0), save_m, ck))
+        np.testing.assert_array_equal(b["gdn_o"], a["gdn_o"][save_m:])
+        np.testing.assert_array_equal(b["S_P"], a["S_P"])
+        np.testing.assert_allclose(b["attn_o"], a["attn_o"][save_m:], atol=1e-13, rtol=0)
+        for pa, pb in zip(a["probs"], b["probs"]):
+            np.testing.assert_array_equal(pa, pb)
+
+
+def test_checkpoint_of_a_resumed_request_chains():
+    """A checkpoint made by a request that itself resumed (positions below its m come from its own
+    checkpoint) resumes to the same values as one made by the uncut run; at save_m = P it is the trunk's
+    end state and window."""
+    full_req = Request(P=14, m=0, q_len=(2,), n_opt=(2,), out_slot=0)
+    rnd_full = custom_round(SMALL, "f32", [full_req], base=12)
+    cw = rnd_full.conv_w()
+    pl = rnd_full.payload(0)
+    ck6 = oround.make_checkpoint(rnd_full, 0, 6, cw)
+    res_req = Request(P=14, m=6, q_len=(2,), n_opt=(2,), ckpt_slot=1, out_slot=0)
+    rnd_res = custom_round(SMALL, "f32", [res_req], base=12)
+    pl6 = _resume_payload(pl, 6, ck6)
+    direct = oround.make_checkpoint(rnd_full, 0, 11, cw)
+    chained = oround.make_checkpoint(rnd_res, 0, 11, cw, payload=pl6)
+    for key in direct:
+        np.testing.assert_array_equal(chained[key], direct[key], err_msg=key)
+    end = oround.make_checkpoint(rnd_full, 0, 14, cw)
+    a = oround.run_request(rnd_full, 0, cw, "memo")
+    np.testing.assert_array_equal(end["ckpt_state"], a["S_P"])
+    np.testing.assert_array_equal(end["ckpt_window"], a["window_P"])
