@@ -81,7 +81,16 @@ const char* flide_version(void);
  *  ckpt_slot pool slot holding the checkpoint at m (GDN state, conv window,
  *            attention K/V of positions 0..m-1); required when m > 0, else -1
  *  out_slot  pool slot that receives S_P and the conv window after the trunk,
- *            >= 0 and != ckpt_slot when m > 0                                  */
+ *            >= 0 and != ckpt_slot when m > 0
+ *  save_m    0, or a checkpoint to create at trunk position save_m in the same
+ *            pass (the interior checkpoints that a later round resumes from,
+ *            [KO] §어떻게 쓰나): m < save_m <= P, and save_m - m a multiple of
+ *            64 (a chunk boundary of the trunk) unless save_m == P
+ *  save_slot pool slot that receives the GDN state after position save_m - 1
+ *            and the conv window of positions save_m - conv_k + 1 .. save_m - 1
+ *            (flide_fork_gdn, phase 0), and the attention K/V of positions
+ *            0..save_m-1 (flide_attn_save_kv); -1 when save_m == 0.  Distinct
+ *            from every out_slot, ckpt_slot and save_slot of the round.        */
 typedef struct {
   int32_t P;
   int32_t m;
@@ -89,6 +98,8 @@ typedef struct {
   const int32_t* q_len;
   int32_t ckpt_slot;
   int32_t out_slot;
+  int32_t save_m;
+  int32_t save_slot;
 } flide_request;
 
 /* Capacity of a metadata image / graph bucket: stream rows, requests, questions. */
@@ -110,7 +121,8 @@ typedef struct {
  *                          vcol0: column offset of the segment in the transposed
  *                          value workspace (column = vcol0 + position, so that
  *                          8-aligned positions land on 16-byte aligned columns)
- *   req_*       [R_cap]    trunk_row0, P, m, ckpt_slot, out_slot, q_seg0, n_q
+ *   req_*       [R_cap]    trunk_row0, P, m, ckpt_slot, out_slot, q_seg0, n_q,
+ *                          save_m, save_slot (0 and -1 when no checkpoint is made)
  *   qfin_row    [Q_cap]    last stream row of every question (stream order)
  *   tile_seg    [tile_cap] attention work list: segment of each tile
  *   tile_row0   [tile_cap]                      first stream row of each tile
@@ -128,7 +140,7 @@ typedef struct {
   int64_t dev_words;
   int64_t hdr;
   int64_t seg_row0, seg_len, seg_req, seg_branch, seg_pos0, seg_state, seg_vcol0;
-  int64_t req_trunk_row0, req_P, req_m, req_ckpt, req_out, req_q_seg0, req_nq;
+  int64_t req_trunk_row0, req_P, req_m, req_ckpt, req_out, req_q_seg0, req_nq, req_save_m, req_save_slot;
   int64_t qfin_row;
   int64_t tile_seg, tile_row0;
   int64_t gdn_order;
@@ -247,7 +259,8 @@ flide_status flide_fork_attn(flide_ctx* ctx, const flide_caps* caps, const int32
  *  phase 0 (FLIDE_GDN_TRUNKS): every trunk segment from a zero state and zero
  *     conv history, or, for m > 0, from state_pool/conv_pool[ckpt_slot]; writes
  *     S_P to state_pool[out_slot] and the last conv_k-1 raw trunk inputs to
- *     conv_pool[out_slot].
+ *     conv_pool[out_slot]; for save_m > 0 also the state after position
+ *     save_m - 1 and the conv_k-1 raw inputs before save_m to save_slot.
  *  phase 1 (FLIDE_GDN_QUESTIONS): every question segment at once, each seeded
  *     by index from state_pool/conv_pool[its request's out_slot] (no copy);
  *     the pools are only read.
@@ -286,6 +299,23 @@ flide_status flide_attn_prepare(flide_ctx* ctx, const flide_caps* caps, const in
 flide_status flide_attn_core(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
                              const flide_attn_params* p, const void* q, const void* v, const void* k_cache,
                              const void* v_cache, void* o, const void* workspace, void* stream);
+
+/* Interior checkpoint K/V ([KO] §어떻게 쓰나: a later round resumes at m from a
+ * checkpoint holding the attention K/V of positions 0..m-1): for every request
+ * of the metadata with save_m > 0, copy the rotated keys and the values of its
+ * trunk positions 0..save_m-1 into k_cache/v_cache slot save_slot, in the cache
+ * layouts of flide_fork_attn.  Positions below the request's resume point m come
+ * from its ckpt_slot; the rest from `workspace` as flide_attn_prepare left it for
+ * the same metadata (rotated keys; on the bf16 MFMA path the transposed values,
+ * else the value rows of v).  Run it after flide_attn_prepare (or a whole round)
+ * and before the workspace is reused.  p->cache_rows must be >= every save_m;
+ * a slot or position outside the cache sets the device error word (read by
+ * flide_check_device).  The GDN half of the checkpoint is written by
+ * flide_fork_gdn phase 0.
+ * Errors: FLIDE_E_INVALID_ARG (NULL buffers, no cache), FLIDE_E_UNSUPPORTED, FLIDE_E_HIP. */
+flide_status flide_attn_save_kv(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
+                                const flide_attn_params* p, const void* v, const void* workspace, void* k_cache,
+                                void* v_cache, void* stream);
 
 flide_status flide_fork_gdn(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
                             const flide_gdn_params* p, int32_t phase, const void* x, const float* conv_w,

@@ -147,9 +147,20 @@ def test_split_matches_oracle(rows, t_max):
     [Request(P=4, m=0, q_len=(), n_opt=(), out_slot=1), Request(P=3, m=0, q_len=(), n_opt=(), out_slot=1)],
     [Request(P=4, m=2, q_len=(), n_opt=(), ckpt_slot=5, out_slot=1),
      Request(P=3, m=0, q_len=(), n_opt=(), out_slot=5)],
+    # interior checkpoints: position outside (m, P], off a chunk boundary, no slot, slot collisions
+    [Request(P=200, m=64, q_len=(), n_opt=(), ckpt_slot=0, out_slot=1, save_m=64, save_slot=2)],
+    [Request(P=200, m=0, q_len=(), n_opt=(), out_slot=1, save_m=201, save_slot=2)],
+    [Request(P=200, m=0, q_len=(), n_opt=(), out_slot=1, save_m=100, save_slot=2)],
+    [Request(P=200, m=0, q_len=(), n_opt=(), out_slot=1, save_m=128, save_slot=-1)],
+    [Request(P=200, m=0, q_len=(), n_opt=(), out_slot=1, save_m=128, save_slot=1)],
+    [Request(P=200, m=64, q_len=(), n_opt=(), ckpt_slot=2, out_slot=1, save_m=128, save_slot=2)],
+    [Request(P=200, m=0, q_len=(), n_opt=(), out_slot=1, save_m=128, save_slot=3),
+     Request(P=200, m=0, q_len=(), n_opt=(), out_slot=2, save_m=64, save_slot=3)],
+    [Request(P=200, m=0, q_len=(), n_opt=(), out_slot=1, save_m=128, save_slot=3),
+     Request(P=200, m=64, q_len=(), n_opt=(), ckpt_slot=3, out_slot=2)],
 ])
 def test_planner_rejects_invalid_rounds(bad):
-    caps = F.caps_of(64, 4, 4)
+    caps = F.caps_of(512, 4, 4)
     image = np.full(F.flide_meta_layout_for(caps).host_words, 7, np.int32)
     with pytest.raises(F.FlideError) as e:
         F.flide_plan_round(bad, caps, image)
@@ -170,3 +181,16 @@ def test_layout_rejects_bad_capacity():
     for caps in (F.caps_of(0, 1, 1), F.caps_of(10, 0, 1), F.caps_of(10, 1, -1)):
         with pytest.raises(F.FlideError):
             F.flide_meta_layout_for(caps)
+
+
+def test_planner_interior_checkpoints():
+    """save_m / save_slot reach the metadata per request (0 / -1 where no checkpoint is made); a
+    checkpoint off the chunk grid is accepted only at the trunk's end."""
+    reqs = [Request(P=300, m=0, q_len=(3,), n_opt=(2,), out_slot=0, save_m=256, save_slot=4),
+            Request(P=90, m=0, q_len=(), n_opt=(), out_slot=1),
+            Request(P=200, m=64, q_len=(2,), n_opt=(2,), ckpt_slot=2, out_slot=3, save_m=200, save_slot=5)]
+    caps = F.caps_of(1024, 4, 4)
+    d = F.decode_image(F.flide_plan_round(reqs, caps), caps)
+    assert d["req_save_m"].tolist() == [256, 0, 200]
+    assert d["req_save_slot"].tolist() == [4, -1, 5]
+    assert d["req_ckpt"].tolist() == [-1, -1, 2]

@@ -312,3 +312,67 @@ def test_fan_out_round_first_split_full_size(ctx):
     last = len(sub.requests) - 1
     harness.check_round(sub, harness.outputs(bufs), lay, mode="memo", requests=[0, last], questions=qs,
                         attn_rows_fn=lambda j: _sample_rows(sub, j, qs, n_trunk=32))
+
+
+def _check_created_checkpoint(rnd, bufs, j: int, tol: float):
+    """The save slot of request j against the oracle's checkpoint at save_m: GDN state (relative error
+    per state row), conv window (exact: raw inputs), and per attention layer the rotated keys (relative
+    error per position) and the values (exact: copies)."""
+    import torch
+    from oracle import round as oround
+    r = rnd.requests[j]
+    ck = oround.make_checkpoint(rnd, j, r.save_m, act=rnd.shapes.gdn_act)
+    torch.cuda.synchronize()
+    s = r.save_slot
+    st = bufs.state_pool[s].cpu().numpy().astype(np.float64)
+    e_state = harness.rel_err(st.reshape(rnd.shapes.H, -1), ck["ckpt_state"].reshape(rnd.shapes.H, -1))
+    win = bufs.conv_pool[s].float().cpu().numpy().astype(np.float64)[:rnd.shapes.conv_k - 1]
+    print(f"[checkpoint] request {j} save_m={r.save_m} slot={s} state err {e_state:.3e}", flush=True)
+    assert e_state <= tol
+    np.testing.assert_array_equal(win, ck["ckpt_window"])
+    for l, cpre in enumerate(["kv", "swa_kv"][:bufs.n_attn]):
+        kc = bufs.k_cache[l][s, :r.save_m].float().cpu().numpy().astype(np.float64)
+        vc = bufs.v_cache[l][s, :, :, :r.save_m].float().cpu().numpy().astype(np.float64)
+        e_k = harness.rel_err(kc, ck[cpre + "_k"])
+        print(f"[checkpoint] layer {l} key err {e_k:.3e}", flush=True)
+        assert e_k <= tol
+        np.testing.assert_array_equal(vc, np.transpose(ck[cpre + "_v"], (1, 2, 0)))
+
+
+def test_interior_checkpoint_creation_f32(ctx):
+    """Checkpoints made in the same pass (GDN state and window by the trunk call, K/V by the save call):
+    a fresh trunk at a chunk boundary, a resumed trunk at its end (the per-token GDN kernel and the fp32
+    attention path), against the oracle's cut prompt."""
+    shapes = LayerShapes(H=2, dk=32, dv=32, conv_k=4, Hq=2, Hkv=1, d=32, theta=1e4, hidden=32)
+    reqs = [Request(P=150, m=0, q_len=(5,), n_opt=(3,), out_slot=0, save_m=128, save_slot=3),
+            Request(P=150, m=64, q_len=(4, 6), n_opt=(2, 2), ckpt_slot=1, out_slot=2, save_m=150, save_slot=4)]
+    rnd = custom_round(shapes, "f32", reqs, base=21)
+    bufs, lay = harness.run_gpu(rnd, ctx, "direct")
+    bufs.save_checkpoint_kv(ctx)
+    from tree_forked_hybrid_amd import flide as F
+    F.flide_check_device(ctx, bufs.caps, bufs.dev_meta)
+    harness.check_round(rnd, harness.outputs(bufs), lay, mode="memo")
+    for j in range(len(reqs)):
+        _check_created_checkpoint(rnd, bufs, j, harness.TOL["f32"])
+
+
+def test_interior_checkpoint_creation_bf16(ctx):
+    """The same on the chunked GDN kernel and the MFMA attention path: an agent-resume request (resumed
+    at 30720) makes a checkpoint 1024 rows further; a short-round request makes one at row 256."""
+    import dataclasses
+    rnd4 = make_round(4, 0, requests=[0])
+    r = rnd4.requests[0]
+    rnd4 = dataclasses.replace(rnd4, requests=[dataclasses.replace(r, save_m=r.m + 1024, save_slot=r.out_slot + 8)])
+    bufs, lay = harness.run_gpu(rnd4, ctx, "direct")
+    bufs.save_checkpoint_kv(ctx)
+    from tree_forked_hybrid_amd import flide as F
+    F.flide_check_device(ctx, bufs.caps, bufs.dev_meta)
+    _check_created_checkpoint(rnd4, bufs, 0, harness.TOL["bf16"])
+    rnd1 = make_round(1, 0, requests=[0, 1])
+    r0 = rnd1.requests[0]
+    new0 = dataclasses.replace(r0, save_m=256, save_slot=max(q.out_slot for q in rnd1.requests) + 1)
+    rnd1 = dataclasses.replace(rnd1, requests=[new0, rnd1.requests[1]])
+    bufs, lay = harness.run_gpu(rnd1, ctx, "direct")
+    bufs.save_checkpoint_kv(ctx)
+    F.flide_check_device(ctx, bufs.caps, bufs.dev_meta)
+    _check_created_checkpoint(rnd1, bufs, 0, harness.TOL["bf16"])

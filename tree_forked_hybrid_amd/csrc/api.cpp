@@ -382,6 +382,23 @@ flide_status flide_attn_prepare(flide_ctx* ctx, const flide_caps* caps, const in
   }
 }
 
+flide_status flide_attn_save_kv(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
+                                const flide_attn_params* p, const void* v, const void* workspace, void* k_cache,
+                                void* v_cache, void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    FLIDE_TRY(check_attn(ctx, p));
+    if (!v || !workspace || !k_cache || !v_cache || p->cache_rows < 1 || p->cache_slots < 1)
+      return fail(ctx, FLIDE_E_INVALID_ARG, "checkpoint K/V needs v, the workspace and a K/V cache");
+    MetaView mv;
+    FLIDE_TRY(view_of(ctx, caps, dev_meta, &mv));
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    return launched(ctx, launch_attn_save_kv(mv, *p, v, workspace, k_cache, v_cache, stream), "attn_save_kv");
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_attn_save_kv");
+  }
+}
+
 flide_status flide_attn_core(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
                              const flide_attn_params* p, const void* q, const void* v, const void* k_cache,
                              const void* v_cache, void* o, const void* workspace, void* stream) {

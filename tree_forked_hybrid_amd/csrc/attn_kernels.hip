@@ -755,6 +755,93 @@ int launch_attn_prepare(const MetaView& mv, const flide_attn_params& p, const Ro
   return launch_rope_k(mv, p, rope, k, workspace, stream);
 }
 
+// Interior checkpoint K/V: for every request that creates a checkpoint at save_m, the rotated keys and
+// the values of positions 0..save_m-1 go to K/V cache slot save_slot, in the cache layouts (keys
+// [slot][position][kv head][d], values [slot][kv head][d][position]).  Positions below the resume
+// point m come from the cache slot the request resumed from, the others from this round's prepared
+// workspace (rotated key rows; values transposed on the MFMA path, plain rows otherwise), so nothing is
+// recomputed.  One workgroup per (request, kv head, 64 positions); the write slot differs from every
+// slot read in the round (checked by the planner), and a slot or position outside the cache sets the
+// device error word.
+template <typename T, bool TRANSPOSED_V>
+__global__ void __launch_bounds__(256) attn_save_kv_kernel(MetaView mv, const T* __restrict__ k_rot,
+                                                           const T* __restrict__ vsrc, T* __restrict__ k_cache,
+                                                           T* __restrict__ v_cache, int Hkv, int D, int cache_rows,
+                                                           int cache_slots, int64_t VT) {
+  const int j = blockIdx.x, g = blockIdx.y, p0 = blockIdx.z * 64;
+  if (j >= mv.hdr[H_R]) return;
+  const int slot = mv.req_save_slot[j];
+  if (slot < 0) return;
+  const int sm = mv.req_save_m[j], m = mv.req_m[j], ck = mv.req_ckpt[j];
+  if (slot >= cache_slots || sm > cache_rows || (m > 0 && (ck < 0 || ck >= cache_slots))) {
+    if (blockIdx.z == 0 && g == 0 && threadIdx.x == 0) flag_error(mv.dev_error, E_CACHE);
+    return;
+  }
+  if (p0 >= sm) return;
+  const int np = min(64, sm - p0);
+  const int64_t row0 = mv.req_trunk_row0[j];
+  const int64_t vcol0 = mv.seg_vcol0[j];  // trunk segment j: value column = vcol0 + position
+  constexpr int EPC = 16 / int(sizeof(T));  // elements per 16-byte piece
+  auto key_src = [&](int t) {
+    return t < m ? k_cache + ((int64_t(ck) * cache_rows + t) * Hkv + g) * D : k_rot + ((row0 + t - m) * Hkv + g) * D;
+  };
+  if (D % EPC == 0) {  // keys: a row per position, d fastest, in 16-byte pieces
+    const int cpr = D / EPC;
+    for (int c = threadIdx.x; c < np * cpr; c += 256) {
+      const int t = p0 + c / cpr, e0 = (c % cpr) * EPC;
+      *reinterpret_cast<u32x4v*>(k_cache + ((int64_t(slot) * cache_rows + t) * Hkv + g) * D + e0) =
+          *reinterpret_cast<const u32x4v*>(key_src(t) + e0);
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < np * D; idx += 256) {
+      const int t = p0 + idx / D, dd = idx % D;
+      k_cache[((int64_t(slot) * cache_rows + t) * Hkv + g) * D + dd] = key_src(t)[dd];
+    }
+  }
+  auto value_at = [&](int dd, int t) {
+    if (t < m) return v_cache[((int64_t(ck) * Hkv + g) * D + dd) * cache_rows + t];
+    if (TRANSPOSED_V) return vsrc[(int64_t(g) * D + dd) * VT + vcol0 + t];
+    return vsrc[((row0 + t - m) * Hkv + g) * D + dd];
+  };
+  // values: a row per channel, position fastest; a whole 16-byte piece of positions on one side of m is
+  // one copy when both sides are transposed rows (piece starts are multiples of 8 positions: 16-byte
+  // aligned in the cache and, with 8-aligned segment columns, in the workspace), else element by element
+  const int cpc = (np + EPC - 1) / EPC;
+  for (int c = threadIdx.x; c < D * cpc; c += 256) {
+    const int dd = c / cpc, t0 = p0 + (c % cpc) * EPC, n = min(EPC, p0 + np - t0);
+    T* dst = v_cache + ((int64_t(slot) * Hkv + g) * D + dd) * cache_rows + t0;
+    if (TRANSPOSED_V && n == EPC && (t0 + EPC <= m || t0 >= m)) {
+      const T* src = t0 < m ? v_cache + ((int64_t(ck) * Hkv + g) * D + dd) * cache_rows + t0
+                            : vsrc + (int64_t(g) * D + dd) * VT + vcol0 + t0;
+      *reinterpret_cast<u32x4v*>(dst) = *reinterpret_cast<const u32x4v*>(src);
+    } else {
+      for (int e = 0; e < n; ++e) dst[e] = value_at(dd, t0 + e);
+    }
+  }
+}
+
+int launch_attn_save_kv(const MetaView& mv, const flide_attn_params& p, const void* v, const void* workspace,
+                        void* k_cache, void* v_cache, void* stream) {
+  const dim3 grid(mv.R_cap, p.Hkv, (p.cache_rows + 63) / 64);
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t krot_elems = int64_t(mv.T_cap) * p.Hkv * p.d;
+  if (attn_uses_mfma(p)) {
+    const bf16_t* k_rot = (const bf16_t*)workspace;
+    hipLaunchKernelGGL((attn_save_kv_kernel<bf16_t, true>), grid, dim3(256), 0, st, mv, k_rot, k_rot + krot_elems,
+                       (bf16_t*)k_cache, (bf16_t*)v_cache, p.Hkv, p.d, p.cache_rows, p.cache_slots,
+                       vt_cols(mv.T_cap, mv.seg_cap));
+  } else if (p.dtype == FLIDE_BF16) {
+    hipLaunchKernelGGL((attn_save_kv_kernel<bf16_t, false>), grid, dim3(256), 0, st, mv, (const bf16_t*)workspace,
+                       (const bf16_t*)v, (bf16_t*)k_cache, (bf16_t*)v_cache, p.Hkv, p.d, p.cache_rows,
+                       p.cache_slots, int64_t(0));
+  } else {
+    hipLaunchKernelGGL((attn_save_kv_kernel<float, false>), grid, dim3(256), 0, st, mv, (const float*)workspace,
+                       (const float*)v, (float*)k_cache, (float*)v_cache, p.Hkv, p.d, p.cache_rows, p.cache_slots,
+                       int64_t(0));
+  }
+  return int(hipGetLastError());
+}
+
 int launch_attn_core(const MetaView& mv, const flide_attn_params& p, const RopeArgs& rope, const void* q,
                      const void* v, const void* k_cache, const void* v_cache, void* o, const void* workspace,
                      void* stream) {

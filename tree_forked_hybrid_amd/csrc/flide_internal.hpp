@@ -13,6 +13,8 @@ constexpr int kTileRows = 32;
 constexpr int kXcdClasses = 8;
 // int32 words of one attention work-list descriptor (filled on the device by meta_expand).
 constexpr int kTileDescWords = 16;
+// rows per GDN chunk: an interior checkpoint of a trunk sits at a multiple of it from the resume point
+constexpr int kCheckpointChunk = 64;
 enum TileDesc { TD_SEG, TD_ROW0, TD_NROWS, TD_QPOS0, TD_M, TD_P, TD_CKPT, TD_QUESTION, TD_ROFF_TRUNK, TD_ROFF_OWN,
                 TD_VOFF_TRUNK, TD_VOFF_OWN, TD_POS0 };
 // Words of the metadata header.
@@ -63,6 +65,8 @@ struct MetaView {
   const int32_t* req_out;
   const int32_t* req_q_seg0;
   const int32_t* req_nq;
+  const int32_t* req_save_m;
+  const int32_t* req_save_slot;
   const int32_t* qfin_row;
   const int32_t* tile_seg;
   const int32_t* tile_row0;
@@ -92,6 +96,8 @@ inline MetaView make_view(int32_t* base, const flide_meta_layout& L, const flide
   v.req_out = base + L.req_out;
   v.req_q_seg0 = base + L.req_q_seg0;
   v.req_nq = base + L.req_nq;
+  v.req_save_m = base + L.req_save_m;
+  v.req_save_slot = base + L.req_save_slot;
   v.qfin_row = base + L.qfin_row;
   v.tile_seg = base + L.tile_seg;
   v.tile_row0 = base + L.tile_row0;
@@ -127,6 +133,9 @@ int launch_attn_prepare(const MetaView& mv, const flide_attn_params& p, const Ro
 int launch_attn_core(const MetaView& mv, const flide_attn_params& p, const RopeArgs& rope, const void* q,
                      const void* v, const void* k_cache, const void* v_cache, void* o, const void* workspace,
                      void* stream);
+// Interior checkpoints: K/V of positions 0..save_m-1 of every saving request into its cache slot.
+int launch_attn_save_kv(const MetaView& mv, const flide_attn_params& p, const void* v, const void* workspace,
+                        void* k_cache, void* v_cache, void* stream);
 bool attn_uses_mfma(const flide_attn_params& p);
 int64_t attn_workspace_bytes(const flide_caps& c, const flide_attn_params& p);
 int launch_gdn(const MetaView& mv, const flide_gdn_params& p, int phase, const void* x, const float* conv_w,

@@ -295,7 +295,10 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
   const int row0 = mv.seg_row0[seg], len = mv.seg_len[seg];
   const int in_slot = mv.seg_state[seg];
   const int out_slot = PHASE == 0 ? mv.req_out[j] : -1;
-  if (in_slot >= n_slots || out_slot >= n_slots || (PHASE == 1 && in_slot < 0)) {
+  // an interior checkpoint of the trunk: its slot and the segment rows it covers (a chunk boundary)
+  const int save_slot = PHASE == 0 ? mv.req_save_slot[j] : -1;
+  const int save_rows = save_slot >= 0 ? mv.req_save_m[j] - mv.req_m[j] : -1;
+  if (in_slot >= n_slots || out_slot >= n_slots || save_slot >= n_slots || (PHASE == 1 && in_slot < 0)) {
     if (tid == 0) flag_error(mv.dev_error, E_SLOT);
     return;
   }
@@ -609,26 +612,36 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
                     cat8(ud[2 * p2], ud[2 * p2 + 1]), acc);
       S[mb] = acc;
     }
+    if (PHASE == 0 && c0 + n == save_rows) {  // the checkpoint's state: S after this chunk's last row
+      float* sdst = state_pool + ((int64_t(save_slot) * H + h) * DV + ncol) * DK;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<f4v*>(sdst + 16 * mb + 4 * g4) = S[mb];
+    }
   }
 
   if (PHASE == 0) {
     float* dst = state_pool + ((int64_t(out_slot) * H + h) * DV + ncol) * DK;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<f4v*>(dst + 16 * mb + 4 * g4) = S[mb];
-    // conv window: last K-1 raw inputs of (history ++ segment) over the head's q, k and v channels
-    bf16_t* wdst = conv_pool + int64_t(out_slot) * (K - 1) * C;
-    const int nch = 2 * DK + DV;
-    for (int it = tid; it < (K - 1) * nch; it += NT) {
-      const int wr = it / nch, ci = it - wr * nch;
-      const int ch = ci < DK ? qch + ci : (ci < 2 * DK ? kch + ci - DK : vch + ci - 2 * DK);
-      const int u = len - (K - 1) + wr;
-      bf16_t val = 0;
-      if (u >= 0)
-        val = x[int64_t(row0 + u) * C + ch];
-      else if (hist != nullptr)
-        val = hist[int64_t(K - 1 + u) * C + ch];
-      wdst[int64_t(wr) * C + ch] = val;
-    }
+    // conv window: the K-1 raw inputs of (history ++ segment) before segment row `upto`, over the
+    // head's q, k and v channels; for the trunk's end and for an interior checkpoint
+    auto write_window = [&](int slot, int upto) {
+      bf16_t* wdst = conv_pool + int64_t(slot) * (K - 1) * C;
+      const int nch = 2 * DK + DV;
+      for (int it = tid; it < (K - 1) * nch; it += NT) {
+        const int wr = it / nch, ci = it - wr * nch;
+        const int ch = ci < DK ? qch + ci : (ci < 2 * DK ? kch + ci - DK : vch + ci - 2 * DK);
+        const int u = upto - (K - 1) + wr;
+        bf16_t val = 0;
+        if (u >= 0)
+          val = x[int64_t(row0 + u) * C + ch];
+        else if (hist != nullptr)
+          val = hist[int64_t(K - 1 + u) * C + ch];
+        wdst[int64_t(wr) * C + ch] = val;
+      }
+    };
+    write_window(out_slot, len);
+    if (save_slot >= 0) write_window(save_slot, save_rows);
   }
 }
 

@@ -70,7 +70,10 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_plain_kernel(MetaView mv, int
   const int len = mv.seg_len[seg];
   int in_slot = mv.seg_state[seg];  // -1: zero state and zero history
   const int out_slot = phase == 0 ? mv.req_out[j] : -1;
-  if (in_slot >= n_slots || out_slot >= n_slots || (phase == 1 && in_slot < 0)) {
+  // an interior checkpoint of the trunk: its slot and the segment rows it covers
+  const int save_slot = phase == 0 ? mv.req_save_slot[j] : -1;
+  const int save_rows = save_slot >= 0 ? mv.req_save_m[j] - mv.req_m[j] : -1;
+  if (in_slot >= n_slots || out_slot >= n_slots || save_slot >= n_slots || (phase == 1 && in_slot < 0)) {
     if (tid == 0) flag_error(mv.dev_error, E_SLOT);
     return;
   }
@@ -155,6 +158,11 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_plain_kernel(MetaView mv, int
 #pragma unroll
       for (int off = 1; off < TPR; off <<= 1) so += __shfl_xor(so, off, 64);
       if (cl == 0) store_f32(o, (int64_t(row0 + c0 + t) * H + h) * DV + blk * DB + r, so);
+      if (c0 + t + 1 == save_rows) {  // the checkpoint's state: S after this row
+        float* sdst = state_pool + ((int64_t(save_slot) * H + h) * DV + blk * DB + r) * DK;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) sdst[cl + TPR * i] = S[i];
+      }
     }
     __syncthreads();
   }
@@ -163,21 +171,26 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_plain_kernel(MetaView mv, int
     float* dst = state_pool + ((int64_t(out_slot) * H + h) * DV + blk * DB + r) * DK;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) dst[cl + TPR * i] = S[i];
-    // conv window: the last K-1 raw inputs of (history ++ segment); q/k channels by block 0 only
-    T* wdst = conv_pool + int64_t(out_slot) * (K - 1) * C;
-    const int nch = (blk == 0 ? 2 * DK : 0) + DB;
-    for (int w = tid; w < (K - 1) * nch; w += kGdnThreads) {
-      const int wr = w / nch, ci = w - wr * nch;
-      int ch;
-      if (blk == 0 && ci < DK)
-        ch = qch + ci;
-      else if (blk == 0 && ci < 2 * DK)
-        ch = kch + ci - DK;
-      else
-        ch = vch + ci - (blk == 0 ? 2 * DK : 0);
-      const float val = gdn_raw(x, hist, C, K, row0, len - (K - 1) + wr, ch);
-      store_f32(wdst, int64_t(wr) * C + ch, val);
-    }
+    // conv window: the K-1 raw inputs of (history ++ segment) before segment row `upto`; q/k channels
+    // by block 0 only; for the trunk's end and for an interior checkpoint
+    auto write_window = [&](int slot, int upto) {
+      T* wdst = conv_pool + int64_t(slot) * (K - 1) * C;
+      const int nch = (blk == 0 ? 2 * DK : 0) + DB;
+      for (int w = tid; w < (K - 1) * nch; w += kGdnThreads) {
+        const int wr = w / nch, ci = w - wr * nch;
+        int ch;
+        if (blk == 0 && ci < DK)
+          ch = qch + ci;
+        else if (blk == 0 && ci < 2 * DK)
+          ch = kch + ci - DK;
+        else
+          ch = vch + ci - (blk == 0 ? 2 * DK : 0);
+        const float val = gdn_raw(x, hist, C, K, row0, upto - (K - 1) + wr, ch);
+        store_f32(wdst, int64_t(wr) * C + ch, val);
+      }
+    };
+    write_window(out_slot, len);
+    if (save_slot >= 0) write_window(save_slot, save_rows);
   }
 }
 

@@ -42,6 +42,8 @@ flide_status compute_layout(const flide_caps& c, flide_meta_layout& L) {
   L.req_out = take(c.R_cap);
   L.req_q_seg0 = take(c.R_cap);
   L.req_nq = take(c.R_cap);
+  L.req_save_m = take(c.R_cap);
+  L.req_save_slot = take(c.R_cap);
   L.qfin_row = take(c.Q_cap > 0 ? c.Q_cap : 1);
   L.tile_seg = take(L.tile_cap);
   L.tile_row0 = take(L.tile_cap);
@@ -65,6 +67,10 @@ static flide_status check_requests(const flide_request* reqs, int32_t R, int64_t
     if (r.n_q > 0 && r.q_len == nullptr) return FLIDE_E_INVALID_ARG;
     if (r.out_slot < 0) return FLIDE_E_INVALID_ARG;
     if (r.m > 0 && (r.ckpt_slot < 0 || r.ckpt_slot == r.out_slot)) return FLIDE_E_INVALID_ARG;
+    // an interior checkpoint sits on a chunk boundary of the trunk (or at its end)
+    if (r.save_m != 0 && (r.save_m <= r.m || r.save_m > r.P || r.save_slot < 0 ||
+                          ((r.save_m - r.m) % kCheckpointChunk != 0 && r.save_m != r.P)))
+      return FLIDE_E_INVALID_ARG;
     rows += r.P - r.m;
     for (int32_t i = 0; i < r.n_q; ++i) {
       if (r.q_len[i] < 1) return FLIDE_E_INVALID_ARG;
@@ -73,11 +79,12 @@ static flide_status check_requests(const flide_request* reqs, int32_t R, int64_t
     nq += r.n_q;
     if (rows > (int64_t(1) << 30)) return FLIDE_E_INVALID_ARG;
   }
-  // Slots written by the trunk call must be distinct from each other and from
-  // every slot a resumed trunk reads, or two workgroups would race on a slot.
+  // Slots written by the trunk call (outputs and new checkpoints) must be distinct from each other
+  // and from every slot a resumed trunk reads, or two workgroups would race on a slot.
   std::vector<int32_t> outs, ckpts;
   for (int32_t j = 0; j < R; ++j) {
     outs.push_back(reqs[j].out_slot);
+    if (reqs[j].save_m != 0) outs.push_back(reqs[j].save_slot);
     if (reqs[j].m > 0) ckpts.push_back(reqs[j].ckpt_slot);
   }
   std::sort(outs.begin(), outs.end());
@@ -154,6 +161,8 @@ flide_status flide_plan_round(const flide_request* reqs, int32_t R, const flide_
     int32_t* r_out = img.data() + L.req_out;
     int32_t* r_qs = img.data() + L.req_q_seg0;
     int32_t* r_nq = img.data() + L.req_nq;
+    int32_t* r_sm = img.data() + L.req_save_m;
+    int32_t* r_ss = img.data() + L.req_save_slot;
     int32_t* qfin = img.data() + L.qfin_row;
     int32_t* s_vc = img.data() + L.seg_vcol0;
 
@@ -167,6 +176,8 @@ flide_status flide_plan_round(const flide_request* reqs, int32_t R, const flide_
       r_ck[j] = r.m > 0 ? r.ckpt_slot : -1;
       r_out[j] = r.out_slot;
       r_nq[j] = r.n_q;
+      r_sm[j] = r.save_m;
+      r_ss[j] = r.save_m != 0 ? r.save_slot : -1;
       s_row0[seg] = row;
       s_len[seg] = r.P - r.m;
       s_req[seg] = j;

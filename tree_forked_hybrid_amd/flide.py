@@ -35,7 +35,8 @@ class FlideError(RuntimeError):
 
 class flide_request(C.Structure):
     _fields_ = [("P", C.c_int32), ("m", C.c_int32), ("n_q", C.c_int32), ("q_len", C.POINTER(C.c_int32)),
-                ("ckpt_slot", C.c_int32), ("out_slot", C.c_int32)]
+                ("ckpt_slot", C.c_int32), ("out_slot", C.c_int32), ("save_m", C.c_int32),
+                ("save_slot", C.c_int32)]
 
 
 class flide_caps(C.Structure):
@@ -46,6 +47,7 @@ class flide_meta_layout(C.Structure):
     _fields_ = [(n, C.c_int64) for n in (
         "host_words", "dev_words", "hdr", "seg_row0", "seg_len", "seg_req", "seg_branch", "seg_pos0",
         "seg_state", "seg_vcol0", "req_trunk_row0", "req_P", "req_m", "req_ckpt", "req_out", "req_q_seg0", "req_nq",
+        "req_save_m", "req_save_slot",
         "qfin_row", "tile_seg", "tile_row0", "gdn_order", "tok_j", "tok_c", "tok_t", "tile_desc", "dev_error")] + \
         [("seg_cap", C.c_int32), ("tile_cap", C.c_int32), ("tile_rows", C.c_int32), ("reserved", C.c_int32)]
 
@@ -102,6 +104,8 @@ _SIGNATURES = {
                                   _VP, _VP, _VP, _VP, _VP]),
     "flide_attn_prepare": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.POINTER(flide_attn_params), _VP, _VP, _VP,
                                      _VP]),
+    "flide_attn_save_kv": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.POINTER(flide_attn_params), _VP, _VP, _VP,
+                                     _VP, _VP]),
     "flide_attn_core": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.POINTER(flide_attn_params), _VP, _VP, _VP, _VP,
                                   _VP, _VP, _VP]),
     "flide_fork_gdn": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.POINTER(flide_gdn_params), C.c_int32, _VP,
@@ -178,12 +182,12 @@ def _check(status: int, where: str, ctx: Optional[int] = None) -> None:
 
 # ----------------------------------------------------------------------------- host structures
 
-# numpy image of struct flide_request (int32 P, m, n_q; pointer q_len; int32 ckpt_slot, out_slot)
-_REQ_DTYPE = np.dtype({"names": ["P", "m", "n_q", "q_len", "ckpt_slot", "out_slot"],
-                       "formats": ["<i4", "<i4", "<i4", "<u8", "<i4", "<i4"],
-                       "offsets": [flide_request.P.offset, flide_request.m.offset, flide_request.n_q.offset,
-                                   flide_request.q_len.offset, flide_request.ckpt_slot.offset,
-                                   flide_request.out_slot.offset],
+# numpy image of struct flide_request (int32 P, m, n_q; pointer q_len; int32 ckpt_slot, out_slot, save_m,
+# save_slot)
+_REQ_FIELDS = ("P", "m", "n_q", "q_len", "ckpt_slot", "out_slot", "save_m", "save_slot")
+_REQ_DTYPE = np.dtype({"names": list(_REQ_FIELDS),
+                       "formats": ["<u8" if n == "q_len" else "<i4" for n in _REQ_FIELDS],
+                       "offsets": [getattr(flide_request, n).offset for n in _REQ_FIELDS],
                        "itemsize": C.sizeof(flide_request)})
 
 
@@ -207,6 +211,8 @@ class Requests:
             rec["q_len"][:n] = np.where(nq > 0, self._q.ctypes.data + 4 * off, 0).astype(np.uint64)
             rec["ckpt_slot"][:n] = np.fromiter((r.ckpt_slot for r in requests), np.int64, n)
             rec["out_slot"][:n] = np.fromiter((r.out_slot for r in requests), np.int64, n)
+            rec["save_m"][:n] = np.fromiter((getattr(r, "save_m", 0) for r in requests), np.int64, n)
+            rec["save_slot"][:n] = np.fromiter((getattr(r, "save_slot", -1) for r in requests), np.int64, n)
         self._rec = rec
         self.arr = rec.ctypes.data_as(C.POINTER(flide_request))
 
@@ -264,7 +270,8 @@ def decode_image(image: np.ndarray, caps: flide_caps) -> dict:
     for name in ("seg_row0", "seg_len", "seg_req", "seg_branch", "seg_pos0", "seg_state", "seg_vcol0"):
         off = getattr(L, name)
         out[name] = image[off:off + n_seg].copy()
-    for name in ("req_trunk_row0", "req_P", "req_m", "req_ckpt", "req_out", "req_q_seg0", "req_nq"):
+    for name in ("req_trunk_row0", "req_P", "req_m", "req_ckpt", "req_out", "req_q_seg0", "req_nq", "req_save_m",
+                 "req_save_slot"):
         off = getattr(L, name)
         out[name] = image[off:off + R].copy()
     out["qfin_row"] = image[L.qfin_row:L.qfin_row + n_qst].copy()
@@ -330,6 +337,13 @@ def flide_attn_prepare(ctx: Context, caps: flide_caps, dev_meta, p: flide_attn_p
                        stream=None) -> None:
     _check(load_library().flide_attn_prepare(ctx.handle, C.byref(caps), _ptr(dev_meta), C.byref(p), _ptr(k), _ptr(v),
                                              _ptr(workspace), _stream(stream)), "flide_attn_prepare", ctx.handle)
+
+
+def flide_attn_save_kv(ctx: Context, caps: flide_caps, dev_meta, p: flide_attn_params, v, workspace, k_cache,
+                       v_cache, stream=None) -> None:
+    _check(load_library().flide_attn_save_kv(ctx.handle, C.byref(caps), _ptr(dev_meta), C.byref(p), _ptr(v),
+                                             _ptr(workspace), _ptr(k_cache), _ptr(v_cache), _stream(stream)),
+           "flide_attn_save_kv", ctx.handle)
 
 
 def flide_attn_core(ctx: Context, caps: flide_caps, dev_meta, p: flide_attn_params, q, v, k_cache, v_cache, o,

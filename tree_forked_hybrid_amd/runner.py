@@ -226,6 +226,14 @@ class RoundBuffers:
                         self.opt_id, max(1, self.spec.opt_cap), self.probs, stream)
         del s
 
+    def save_checkpoint_kv(self, ctx: F.Context, stream=None) -> None:
+        """After a round: the attention K/V of every request's interior checkpoint (save_m > 0) into its
+        cache slot, per attention layer, from the workspace the round's prepare step left (the GDN half
+        was written by the trunk call)."""
+        for l in range(self.n_attn):
+            F.flide_attn_save_kv(ctx, self.caps, self.dev_meta, self.attn_params[l], self.v[l], self.ws[l],
+                                 self.k_cache[l], self.v_cache[l], stream)
+
 
 def spec_for_round(rnd, T_cap: Optional[int] = None, R_cap: Optional[int] = None, Q_cap: Optional[int] = None,
                    opt_cap: Optional[int] = None) -> RoundSpec:
@@ -235,7 +243,8 @@ def spec_for_round(rnd, T_cap: Optional[int] = None, R_cap: Optional[int] = None
     Q = int(sum(len(r.q_len) for r in rnd.requests))
     n_opt = int(sum(sum(r.n_opt) for r in rnd.requests))
     slots = [r.out_slot for r in rnd.requests] + [r.ckpt_slot for r in rnd.requests if r.m > 0]
-    max_m = max([r.m for r in rnd.requests] + [0])
+    slots += [r.save_slot for r in rnd.requests if getattr(r, "save_m", 0) > 0]
+    max_m = max([r.m for r in rnd.requests] + [getattr(r, "save_m", 0) for r in rnd.requests] + [0])
     max_m = (max_m + 7) // 8 * 8
     max_pos = max([r.P + (max(r.q_len) if r.q_len else 0) for r in rnd.requests] + [1])
     return RoundSpec(rnd.shapes, rnd.dtype, T_cap or max(T, 1), R_cap or max(R, 1), Q_cap if Q_cap is not None else Q,

@@ -87,6 +87,8 @@ class Request:
     n_opt: tuple                # options per question
     ckpt_slot: int = -1         # pool slot holding the checkpoint at m (m > 0)
     out_slot: int = -1          # pool slot receiving S_P and the conv window
+    save_m: int = 0             # 0, or the trunk position of a checkpoint to create in the same pass
+    save_slot: int = -1         # pool slot receiving that checkpoint (save_m > 0)
 
 
 def rows_of(r: Request) -> int:
