@@ -376,3 +376,38 @@ def test_interior_checkpoint_creation_bf16(ctx):
     bufs.save_checkpoint_kv(ctx)
     F.flide_check_device(ctx, bufs.caps, bufs.dev_meta)
     _check_created_checkpoint(rnd1, bufs, 0, harness.TOL["bf16"])
+
+
+def test_resume_from_created_checkpoint_matches_uncut_round(ctx):
+    """A round resumed from a checkpoint the library made (GDN state and window from the trunk call, K/V
+    from the save call) reproduces the uncut round's rows past the checkpoint: the resumed chunks start
+    on the same chunk boundary and the key tiles fall on the same 32-key grid, so the arithmetic is the
+    same and the outputs must be bit-identical (short-round request, bf16)."""
+    import dataclasses
+    import torch
+    from tree_forked_hybrid_amd import flide as F
+    base = make_round(1, 0, requests=[0])
+    r0 = base.requests[0]
+    sm, ss = 256, r0.out_slot + 1
+    ra = dataclasses.replace(base, requests=[dataclasses.replace(r0, save_m=sm, save_slot=ss)])
+    ba, la = harness.run_gpu(ra, ctx, "direct")
+    ba.save_checkpoint_kv(ctx)
+    F.flide_check_device(ctx, ba.caps, ba.dev_meta)
+    ga = harness.outputs(ba)
+    row_keys = ("attn_q", "attn_k", "attn_v", "gdn_x", "alpha", "eta", "hidden")
+    pb = {k: (np.asarray(v)[sm:] if k in row_keys else v) for k, v in ra.payload(0).items()}
+    torch.cuda.synchronize()
+    pb["ckpt_state"] = ba.state_pool[ss].cpu().numpy()
+    pb["ckpt_window"] = ba.conv_pool[ss].float().cpu().numpy()
+    pb["kv_k"] = ba.k_cache[0][ss, :sm].float().cpu().numpy()
+    pb["kv_v"] = np.transpose(ba.v_cache[0][ss, :, :, :sm].float().cpu().numpy(), (2, 0, 1))
+    rb = dataclasses.replace(base, requests=[dataclasses.replace(r0, m=sm, ckpt_slot=ss)], _cache={0: pb})
+    bb, lb = harness.run_gpu(rb, ctx, "direct")
+    gb = harness.outputs(bb)
+    rows_a = harness.stream_rows(ra, la, 0)[sm:]
+    rows_b = harness.stream_rows(rb, lb, 0)
+    for key in ("gdn_o", "attn_o"):
+        np.testing.assert_array_equal(gb[key][rows_b], ga[key][rows_a], err_msg=key)
+    np.testing.assert_array_equal(gb["state_pool"][r0.out_slot], ga["state_pool"][r0.out_slot])
+    n = harness.option_offsets(ra)[-1]
+    np.testing.assert_array_equal(gb["probs"][:n], ga["probs"][:n])
