@@ -61,11 +61,14 @@ __global__ void __launch_bounds__(256) readout_kernel(MetaView mv, int hidden, c
   }
   const int o0 = opt_off[qi], o1 = opt_off[qi + 1];
   // logits with a running max and a rescaled running sum (every lane holds the
-  // wave-reduced values); lane 0 stores the logits and later normalises them
-  // itself, so no lane reads another lane's global store.  Options go in
-  // batches of four: their row loads and wave reductions are independent, so
-  // a batch waits for one memory round trip instead of one per option.
-  constexpr int OB = 4;
+  // wave-reduced values).  Options go in batches of eight: their row loads and
+  // wave reductions are independent, so a batch waits for one memory round trip
+  // instead of one per option.  A question with at most one batch of options
+  // keeps its logits in registers; with more, lane 0 stores the logits and later
+  // normalises them itself (no lane reads another lane's global store).
+  constexpr int OB = 8;
+  const bool one_batch = o1 - o0 <= OB;
+  float lg[OB];
   float zmax = -INFINITY, se = 0.f;
   for (int kb = o0; kb < o1; kb += OB) {
     int orow[OB];
@@ -75,7 +78,7 @@ __global__ void __launch_bounds__(256) readout_kernel(MetaView mv, int hidden, c
       orow[j] = kb + j < o1 ? opt_id[kb + j] : 0;
       ok[j] = kb + j < o1 && orow[j] >= 0 && orow[j] < n_opt_rows;
     }
-    float acc[OB] = {0.f, 0.f, 0.f, 0.f};
+    float acc[OB] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
       if (c * 64 + lane < chunks) {
@@ -95,22 +98,29 @@ __global__ void __launch_bounds__(256) readout_kernel(MetaView mv, int hidden, c
     for (int j = 0; j < OB; ++j) {
       const int k = kb + j;
       if (k >= o1) break;
+      lg[j] = ok[j] ? acc[j] : -INFINITY;
       if (!ok[j]) {
         if (lane == 0) {
           flag_error(mv.dev_error, E_OPTION);
-          probs[k] = -INFINITY;
+          if (!one_batch) probs[k] = -INFINITY;
         }
         continue;
       }
       const float znew = fmaxf(zmax, acc[j]);
       se = (zmax == -INFINITY ? 0.f : se * __expf(zmax - znew)) + __expf(acc[j] - znew);
       zmax = znew;
-      if (lane == 0) probs[k] = acc[j];
+      if (lane == 0 && !one_batch) probs[k] = acc[j];
     }
   }
   if (lane == 0) {
     const float inv = se > 0.f ? 1.f / se : 0.f;
-    for (int k = o0; k < o1; ++k) probs[k] = __expf(probs[k] - zmax) * inv;
+    if (one_batch) {
+#pragma unroll
+      for (int j = 0; j < OB; ++j)
+        if (o0 + j < o1) probs[o0 + j] = __expf(lg[j] - zmax) * inv;
+    } else {
+      for (int k = o0; k < o1; ++k) probs[k] = __expf(probs[k] - zmax) * inv;
+    }
   }
 }
 
