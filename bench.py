@@ -1,14 +1,19 @@
 """ForkAttention round benchmark on one MI355X.
 
-One timed step = one whole round of the hot path over a synthetic batch:
-host planning of the flat stream, the metadata upload (pinned H2D copy) and a
-graph replay that expands the metadata, runs the GDN layer (trunk call, then
-question call), rotates keys, runs the tree-masked attention layer(s) and the
-selective readout.  Inputs are resident in HBM before the timed region.
+One timed step = one whole round of the hot path over a synthetic batch: for
+every sub-round of the round (a round larger than the largest capacity is split
+at request boundaries), host planning of the flat stream, choice of the
+smallest captured capacity bucket, the metadata upload (pinned H2D copy) and the
+bucket's graph replay, which expands the metadata, runs the GDN layer (trunk
+call, then question call), rotates keys, runs the tree-masked attention
+layer(s) and the selective readout.  Payloads are resident in HBM before the
+timed region: every sub-round has a buffer set of its own, so the replays of a
+round are enqueued back to back.
 
-Default workload: short single-question rounds (R=64 requests, P~U[256,768],
-one question of 16..48 tokens each, 2-5 options; GDN 16 heads x 128, attention
-16 q / 4 kv heads x 256, hidden 2048, bf16 activations, fp32 GDN state).
+Default workload: the 64-question fan-out round (R=16 requests, P=8192, 64
+questions of 16..64 tokens each, 2-8 options; GDN 16 heads x 128, attention 16 q
+/ 4 kv heads x 256, hidden 2048, bf16 activations, fp32 GDN state): about 172k
+stream rows, run as three replays of the 65536-row bucket (6 + 6 + 4 requests).
 
 Prints one JSON line.  ``value`` is stream tokens per second of whole rounds
 (each round holds one GDN layer, one attention layer and the readout).
@@ -19,6 +24,8 @@ import argparse
 import gc
 import json
 import os
+import platform
+import subprocess
 import sys
 import time
 
@@ -39,7 +46,7 @@ KERNEL_SOURCES = {
     "attn_prepare_swa": ["attn_kernels.hip"], "attn_core_swa": ["attn_kernels.hip"],
     "readout": ["readout_kernels.hip"],
 }
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters_short_rounds.md")
+COUNTERS_FILES = {1: "hbm_counters_short_rounds.md", 3: "hbm_counters_question_fanout.md"}
 
 
 def source_digest(name: str) -> str:
@@ -51,12 +58,15 @@ def source_digest(name: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(name: str):
-    """HBM bytes per launch of `name` from the committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE,
-    scaled by the reference copy), or None when there is none or the kernel source changed since."""
-    if not os.path.exists(COUNTERS_FILE):
+def measured_traffic(name: str, config: int):
+    """HBM bytes per round of `name` (summed over the round's launches) from the committed rocprofv3
+    counter summary of this workload (FETCH_SIZE + WRITE_SIZE, scaled by the reference copy), or None when
+    there is none or the kernel source changed since."""
+    fn = COUNTERS_FILES.get(config)
+    path = os.path.join(ROOT, "profiles", fn) if fn else None
+    if not path or not os.path.exists(path):
         return None
-    with open(COUNTERS_FILE) as fh:
+    with open(path) as fh:
         for line in fh:
             cells = [c.strip() for c in line.strip().strip("|").split("|")]
             if len(cells) >= 5 and cells[0] == name:
@@ -72,21 +82,20 @@ def _round_up(x: int, m: int) -> int:
 
 
 def algorithmic_work(rnd):
-    """Algorithmic bytes / FLOPs per kernel of one round (what the method must move or compute)."""
+    """Algorithmic bytes / FLOPs per kernel of one (sub-)round (what the method must move or compute)."""
     s = rnd.shapes
     b = 2 if rnd.dtype == "bf16" else 4
     T = sum((r.P - r.m) + sum(r.q_len) for r in rnd.requests)
     R = len(rnd.requests)
     nq = sum(len(r.q_len) for r in rnd.requests)
-    # attention: visible pairs per q head; every row x at position t sees min(t + 1, W) keys
+
+    # attention: visible pairs per q head; a row at position t sees min(t + 1, W) keys (W = 0: t + 1)
     def pairs(W):
         tot = 0
         for r in rnd.requests:
-            ts = list(range(r.m, r.P)) + [r.P + u for L in r.q_len for u in range(L)]
-            for t in ts:
+            for t in list(range(r.m, r.P)) + [r.P + u for L in r.q_len for u in range(L)]:
                 tot += min(t + 1, W) if W > 0 else t + 1
         return tot
-    cache_rows = sum(r.m for r in rnd.requests)
     attn = {}
     for name, W in [("attn", 0)] + ([("swa", s.swa_window)] if s.swa_window > 0 else []):
         pr = pairs(W)
@@ -107,48 +116,120 @@ def algorithmic_work(rnd):
     gdn1 = q_rows * per_row + sum(1 for r in rnd.requests if r.q_len) * (state + window)
     n_opt = sum(sum(r.n_opt) for r in rnd.requests)
     ro = nq * s.hidden * b + n_opt * (s.hidden * b + 8) + 4 * (nq + 1)
-    return {"T": T, "attn": attn, "gdn0": gdn0, "gdn1": gdn1, "readout": ro, "cache_rows": cache_rows}
+    return {"T": T, "attn": attn, "gdn0": gdn0, "gdn1": gdn1, "readout": ro}
 
 
-def cpu_baseline(rnd, n_req: int):
-    """Time the oracle (as it stands) on the first n_req requests of the round, single-threaded."""
+def _host_cpu() -> str:
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for ln in out.splitlines():
+            if ln.startswith("Model name:"):
+                return ln.split(":", 1)[1].strip()
+    except Exception:  # noqa: BLE001
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(rnd, n_trunk_sample: int = 48):
+    """The oracle (as it stands, single BLAS thread) on a bounded sample of the round's first request:
+    its GDN over the whole trunk and its first question (per-token recurrence: the full cost of those rows),
+    its attention at ``n_trunk_sample`` trunk rows at evenly spaced positions plus every row of the
+    question, and the question's readout.  The trunk's attention time is scaled to all trunk rows by the
+    ratio of visible keys (the oracle's per-row attention cost is linear in them); value = sampled rows /
+    (measured GDN, question attention and readout time + scaled trunk attention time)."""
+    import numpy as np
     try:
         from threadpoolctl import threadpool_limits
     except Exception:  # noqa: BLE001
         threadpool_limits = None
-    from oracle import round as oround
-    sub = rnd.subset(list(range(n_req)))
+    from oracle.attention import prompt_attention
+    from oracle.gdn import gdn_prompt
+    from oracle.readout import option_probs
+    sub = rnd.subset([0])
+    r = sub.requests[0]
+    pl = sub.payload(0, keep=True)
     conv_w = sub.conv_w()
-    rows = sum((r.P - r.m) + sum(r.q_len) for r in sub.requests)
-    for j in range(n_req):
-        sub.payload(j, keep=True)
-    ctx = threadpool_limits(1) if threadpool_limits else None
-    t0 = time.perf_counter()
-    for j in range(n_req):
-        oround.run_request(sub, j, conv_w, "memo")
-    dt = time.perf_counter() - t0
-    if ctx is not None:
-        ctx.unregister() if hasattr(ctx, "unregister") else None
-    return {"value": rows / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n_req} of {len(rnd.requests)} requests ({rows} stream rows), memo mode "
-                      f"(trunk once, every question from a copy of the trunk state), fp64, all layers + readout; "
-                      f"{dt:.1f} s"}
+    sh = sub.shapes
+    tn = r.P - r.m
+    L = r.q_len[0] if r.q_len else 0
+    rows = np.arange(tn + L)
+    pos = np.concatenate([np.arange(r.m, r.P), np.arange(r.P, r.P + L)])
+    samp = sorted(set(np.linspace(0, tn - 1, min(n_trunk_sample, tn)).astype(int).tolist())) if tn else []
+    limiter = threadpool_limits(1) if threadpool_limits else None
+    try:
+        t0 = time.perf_counter()
+        gdn_prompt(pl["gdn_x"][rows], pl["alpha"][rows], pl["eta"][rows], conv_w, sh.H, sh.dk, sh.dv,
+                   pl.get("ckpt_window"), pl.get("ckpt_state"), sh.gdn_act)
+        t1 = time.perf_counter()
+        ck = (pl.get("kv_k"), pl.get("kv_v")) if r.m > 0 else (None, None)
+        prompt_attention(pl["attn_q"][rows], pl["attn_k"][rows], pl["attn_v"][rows], pos, sh.theta,
+                         cache_k=ck[0], cache_v=ck[1], rows=samp)
+        t2 = time.perf_counter()
+        prompt_attention(pl["attn_q"][rows], pl["attn_k"][rows], pl["attn_v"][rows], pos, sh.theta,
+                         cache_k=ck[0], cache_v=ck[1], rows=list(range(tn, tn + L)))
+        if L:
+            option_probs(pl["hidden"][tn + L - 1], pl["w_opt"][:r.n_opt[0]])
+        t3 = time.perf_counter()
+    finally:
+        if limiter is not None:
+            limiter.unregister()
+    vis_all = sum(t + 1 for t in range(r.m, r.P))
+    vis_samp = sum(int(pos[a]) + 1 for a in samp) or 1
+    t_trunk_attn = (t2 - t1) * vis_all / vis_samp
+    total = (t1 - t0) + t_trunk_attn + (t3 - t2)
+    return {"value": round((tn + L) / total, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"request 0 of the round ({tn} trunk rows) with its first question ({L} rows), memo order, "
+                       f"fp64, one BLAS thread: GDN over all {tn + L} rows {t1 - t0:.1f} s; attention at "
+                       f"{len(samp)} evenly spaced trunk rows {t2 - t1:.1f} s, scaled by visible keys to all "
+                       f"{tn} trunk rows = {t_trunk_attn:.1f} s (extrapolated); question attention + readout "
+                       f"{t3 - t2:.1f} s; host {os.cpu_count()} logical CPUs, {_host_cpu()}"),
+            "host_cpus": os.cpu_count()}
+
+
+def measured_peaks(torch):
+    """Device-to-device copy bandwidth and a large bf16 GEMM (the vendor library) in this job: practical
+    ceilings beside the published peaks."""
+    n = 1 << 30
+    a = torch.empty(n // 2, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(10):
+        b.copy_(a)
+    ev[1].record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * 10 / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    y = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    z = x @ y
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(10):
+        z = x @ y
+    ev[1].record()
+    torch.cuda.synchronize()
+    gemm = 2 * m ** 3 * 10 / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12
+    del x, y, z
+    return {"d2d_copy_GB/s": round(copy_gbs, 1), "bf16_gemm_8192_TFLOP/s": round(gemm, 1)}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-requests", type=int, default=6, help="requests of the oracle CPU sample (0: skip)")
-    ap.add_argument("--subround", type=int, default=None,
-                    help="for a workload over one capacity (question fan-out): which of its replays to time")
-    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--cpu-sample", type=int, default=48,
+                    help="trunk rows of the oracle's attention sample (0: skip the CPU baseline)")
+    ap.add_argument("--kernel-reps", type=int, default=5)
     ap.add_argument("--counters", action="store_true",
-                    help="counter pass: one launch of every kernel plus a 256 MiB device copy (for rocprofv3 --pmc "
-                         "FETCH_SIZE / WRITE_SIZE and the copy-kernel scale factor); prints no JSON")
+                    help="counter pass: one launch of every kernel per sub-round plus a 256 MiB device copy (for "
+                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE and the copy-kernel scale factor); prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the ForkAttention round runs on a single MI355X "
@@ -158,49 +239,50 @@ def main():
     import torch
 
     from tree_forked_hybrid_amd import flide as F
-    from tree_forked_hybrid_amd.runner import RoundBuffers, spec_for_round
+    from tree_forked_hybrid_amd.runner import BucketTable, bucket_capacities, spec_for_round
     from workloads import CONFIGS, make_round
 
     spec_cfg = CONFIGS[args.config]
     rnd = make_round(args.config, args.seed)
     T = sum((r.P - r.m) + sum(r.q_len) for r in rnd.requests)
-    sub_note = None
-    if T > rnd.t_max:
-        # a round over the capacity runs as several replays: time one of them (--subround)
-        first, eager = F.flide_split_round(rnd.requests, rnd.t_max)
-        k = args.subround
-        if args.subround is None or not 0 <= k < len(eager) or eager[k]:
-            print(f"this workload runs as {len(eager)} replays of <= {rnd.t_max} rows; pick one with --subround "
-                  f"0..{len(eager) - 1}", file=sys.stderr)
-            sys.exit(2)
-        rnd = rnd.subset(list(range(first[k], first[k + 1])))
-        T = sum((r.P - r.m) + sum(r.q_len) for r in rnd.requests)
-        sub_note = f"replay {k} of {len(eager)} (requests {first[k]}..{first[k + 1] - 1})"
-    R = len(rnd.requests)
-    nq = sum(len(r.q_len) for r in rnd.requests)
-    spec = spec_for_round(rnd, T_cap=_round_up(T, 4096), R_cap=_round_up(R, 64), Q_cap=_round_up(max(nq, 1), 64))
-    ctx = F.Context(0)
-    bufs = RoundBuffers(spec)
-    image = F.flide_plan_round(rnd.requests, bufs.caps)
-    placement = F.decode_image(image, bufs.caps)
-    bufs.fill(rnd, placement)
-    bid = F.flide_graph_capture(ctx, bufs.round_bufs())
-    caps = bufs.caps
+    first, eager = F.flide_split_round(rnd.requests, rnd.t_max)
+    if any(eager):
+        print("a request of this workload exceeds the largest capacity (eager path): not a benchmark round",
+              file=sys.stderr)
+        sys.exit(2)
+    subs = [rnd.subset(list(range(first[i], first[i + 1]))) for i in range(len(eager))]
+    R_cap = _round_up(max(len(s.requests) for s in subs), 8)
+    Q_cap = _round_up(max(max(sum(len(r.q_len) for r in s.requests) for s in subs), 1), 64)
+    opt_cap = max(sum(sum(r.n_opt) for r in s.requests) for s in subs)
+    caps_table = bucket_capacities(rnd.t_max, R_cap, Q_cap)
+    spec = spec_for_round(rnd, T_cap=rnd.t_max, R_cap=R_cap, Q_cap=Q_cap, opt_cap=opt_cap)
+    print(f"[bench] {spec_cfg.name}: {T} rows, {len(subs)} sub-round(s), table of {len(caps_table)} buckets "
+          f"(R_cap {R_cap}, Q_cap {Q_cap})", flush=True)
+    tables = []
+    for k, sub in enumerate(subs):  # one buffer set per sub-round: replays of a round go back to back
+        tab = BucketTable(spec, caps_table)
+        bid, img = tab.plan(sub.requests)
+        tab.bufs.fill(sub, F.decode_image(img, tab.caps_of(bid)))
+        tables.append(tab)
+        print(f"[bench] sub-round {k}: {len(sub.requests)} requests, bucket T_cap {tab.caps_of(bid).T_cap}",
+              flush=True)
+    sub_reqs = [s.requests for s in subs]
 
     def step():
-        img = F.flide_plan_round(rnd.requests, caps, image)
-        F.flide_graph_replay(ctx, bid, img)
+        for tab, reqs in zip(tables, sub_reqs):
+            tab.run(reqs)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    F.flide_check_device(ctx, caps, bufs.dev_meta)
-    # A serving loop keeps the collector out of the round's critical path: the setup heap is frozen
-    # and collection is paused while rounds are timed (a full collection costs tens of ms here).
+    for tab in tables:
+        tab.check()
+    # A serving loop keeps the collector out of the round's critical path: the setup heap is frozen and
+    # collection is paused while rounds are timed (a full collection costs tens of ms here).
     gc.collect()
     gc.freeze()
     gc.disable()
-    # Round latency: plan, upload and replay one round, then wait for it.
+    # Round latency: plan, upload and replay every sub-round of one round, then wait for it.
     lat = []
     for _ in range(args.steps):
         s0 = time.perf_counter()
@@ -208,9 +290,9 @@ def main():
         torch.cuda.synchronize()
         lat.append(time.perf_counter() - s0)
     # Throughput (the timed region): rounds back to back, as a serving loop runs them.  Each round is
-    # planned on the host while the device still runs the previous one; its metadata upload and graph
-    # replay are ordered after that round on the stream, and the replay's double-buffered pinned staging
-    # keeps a round's image intact until its copy has executed.
+    # planned on the host while the device still runs the previous one; its metadata uploads and graph
+    # replays are ordered after that round on the stream, and each bucket's double-buffered pinned staging
+    # keeps an image intact until its copy has executed.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -219,13 +301,45 @@ def main():
     t1 = time.perf_counter()
     gc.enable()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    F.flide_check_device(ctx, caps, bufs.dev_meta)
+    for tab in tables:
+        tab.check()
 
-    # per-kernel durations, measured with HIP events on the launch stream (the null stream)
-    bufs.upload(ctx, image)
-    kernels = {}
-
-    def timed(name, fn):
+    # Per-kernel durations: each entry point launched on its own on every sub-round's buffers and bucket,
+    # timed with HIP events on the launch stream (torch's current stream); summed over the round.
+    st = torch.cuda.current_stream()
+    launches = []  # (name, sub-round, fn)
+    for k, tab in enumerate(tables):
+        bid = tab.last[0]
+        caps, dm, b = tab.caps_of(bid), tab.dev_meta_of(bid), tab.bufs
+        F.flide_meta_upload(tab.ctx, caps, tab.last[1], dm, st)
+        ctx = tab.ctx
+        for phase, name in ((0, "fork_gdn_trunks"), (1, "fork_gdn_questions")):
+            launches.append((name, k, lambda ph=phase, ctx=ctx, caps=caps, dm=dm, b=b: F.flide_fork_gdn(
+                ctx, caps, dm, b.gdn_params, ph, b.x, b.conv_w, b.alpha, b.eta, b.state_pool, b.conv_pool,
+                b.spec.n_slots, b.o_gdn, stream=st)))
+        for l in range(b.n_attn):
+            sfx = "" if l == 0 else "_swa"
+            launches.append(("attn_prepare" + sfx, k, lambda l=l, ctx=ctx, caps=caps, dm=dm, b=b: F.flide_attn_prepare(
+                ctx, caps, dm, b.attn_params[l], b.k[l], b.v[l], b.ws[l], stream=st)))
+            launches.append(("attn_core" + sfx, k, lambda l=l, ctx=ctx, caps=caps, dm=dm, b=b: F.flide_attn_core(
+                ctx, caps, dm, b.attn_params[l], b.q[l], b.v[l], b.k_cache[l], b.v_cache[l], b.o_attn[l], b.ws[l],
+                stream=st)))
+        launches.append(("readout", k, lambda ctx=ctx, caps=caps, dm=dm, b=b: F.flide_readout(
+            ctx, caps, dm, b.ro_params, b.h, b.w_opt, b.opt_off, b.opt_id, max(1, b.spec.opt_cap), b.probs,
+            stream=st)))
+    if args.counters:
+        for _, _, fn in launches:
+            fn()
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)  # reference copy of known size: scales FETCH_SIZE / WRITE_SIZE
+        torch.cuda.synchronize()
+        print(f"counter pass done: {len(launches)} launches, copy {COPY_BYTES} bytes", flush=True)
+        for tab in tables:
+            tab.close()
+        return
+    kernels, launches_of = {}, {}
+    for name, k, fn in launches:
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         fn()
         torch.cuda.synchronize()
@@ -234,54 +348,29 @@ def main():
             fn()
         ev[1].record()
         torch.cuda.synchronize()
-        kernels[name] = ev[0].elapsed_time(ev[1]) * 1e3 / args.kernel_reps  # us
+        kernels[name] = kernels.get(name, 0.0) + ev[0].elapsed_time(ev[1]) * 1e3 / args.kernel_reps  # us
+        launches_of[name] = launches_of.get(name, 0) + 1
+    for tab in tables:
+        tab.check()
 
-    st = torch.cuda.current_stream()  # events and kernels on one stream
-    gp = bufs.gdn_params
-    launches = {}
-    for phase, name in ((0, "fork_gdn_trunks"), (1, "fork_gdn_questions")):
-        launches[name] = lambda ph=phase: F.flide_fork_gdn(ctx, caps, bufs.dev_meta, gp, ph, bufs.x, bufs.conv_w,
-                                                           bufs.alpha, bufs.eta, bufs.state_pool, bufs.conv_pool,
-                                                           spec.n_slots, bufs.o_gdn, stream=st)
-    for l in range(bufs.n_attn):
-        sfx = "" if l == 0 else "_swa"
-        launches["attn_prepare" + sfx] = lambda l=l: F.flide_attn_prepare(
-            ctx, caps, bufs.dev_meta, bufs.attn_params[l], bufs.k[l], bufs.v[l], bufs.ws[l], stream=st)
-        launches["attn_core" + sfx] = lambda l=l: F.flide_attn_core(
-            ctx, caps, bufs.dev_meta, bufs.attn_params[l], bufs.q[l], bufs.v[l], bufs.k_cache[l], bufs.v_cache[l],
-            bufs.o_attn[l], bufs.ws[l], stream=st)
-    launches["readout"] = lambda: F.flide_readout(ctx, caps, bufs.dev_meta, bufs.ro_params, bufs.h, bufs.w_opt,
-                                                  bufs.opt_off, bufs.opt_id, max(1, spec.opt_cap), bufs.probs,
-                                                  stream=st)
-    if args.counters:
-        for fn in launches.values():
-            fn()
-        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)  # reference copy of known size: scales FETCH_SIZE / WRITE_SIZE
-        torch.cuda.synchronize()
-        print(f"counter pass done: {len(launches)} kernels, copy {COPY_BYTES} bytes", flush=True)
-        ctx.close()
-        return
-    for name, fn in launches.items():
-        timed(name, fn)
-    torch.cuda.synchronize()
-
-    work = algorithmic_work(rnd)
+    works = [algorithmic_work(s) for s in subs]
+    tot = lambda f: sum(f(w) for w in works)  # noqa: E731
     rows = {
-        "fork_gdn_trunks": ("hbm", work["gdn0"], None),
-        "fork_gdn_questions": ("hbm", work["gdn1"], None),
-        "attn_prepare": ("hbm", work["attn"]["attn"]["prep_bytes"], None),
-        "attn_core": ("mfma", work["attn"]["attn"]["bytes"], work["attn"]["attn"]["flops"]),
-        "readout": ("hbm", work["readout"], None),
+        "fork_gdn_trunks": ("hbm", tot(lambda w: w["gdn0"]), None),
+        "fork_gdn_questions": ("hbm", tot(lambda w: w["gdn1"]), None),
+        "attn_prepare": ("hbm", tot(lambda w: w["attn"]["attn"]["prep_bytes"]), None),
+        "attn_core": ("mfma", tot(lambda w: w["attn"]["attn"]["bytes"]), tot(lambda w: w["attn"]["attn"]["flops"])),
+        "readout": ("hbm", tot(lambda w: w["readout"]), None),
     }
-    if "swa" in work["attn"]:
-        rows["attn_prepare_swa"] = ("hbm", work["attn"]["swa"]["prep_bytes"], None)
-        rows["attn_core_swa"] = ("mfma", work["attn"]["swa"]["bytes"], work["attn"]["swa"]["flops"])
+    if "swa" in works[0]["attn"]:
+        rows["attn_prepare_swa"] = ("hbm", tot(lambda w: w["attn"]["swa"]["prep_bytes"]), None)
+        rows["attn_core_swa"] = ("mfma", tot(lambda w: w["attn"]["swa"]["bytes"]),
+                                 tot(lambda w: w["attn"]["swa"]["flops"]))
     per_kernel = {}
     for name, us in kernels.items():
         bound, byts, flops = rows[name]
-        ent = {"us": round(us, 2), "GB/s": round(byts / (us * 1e-6) / 1e9, 1), "hbm_frac": None, "mfma_frac": None}
+        ent = {"us_per_round": round(us, 2), "launches_per_round": launches_of[name],
+               "GB/s": round(byts / (us * 1e-6) / 1e9, 1)}
         ent["hbm_frac"] = round(ent["GB/s"] / PEAK_HBM_GBS, 4)
         if flops:
             tf = flops / (us * 1e-6) / 1e12
@@ -293,24 +382,30 @@ def main():
     us = kernels[dom]
     if flops and rnd.dtype == "bf16":
         # the binding roof of a contraction is whichever of MFMA time and HBM time is larger
-        t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
-        t_hbm = byts / (PEAK_HBM_GBS * 1e9)
-        bound = "mfma" if t_mfma >= t_hbm else "hbm"
+        bound = "mfma" if flops / (PEAK_BF16_TFLOPS * 1e12) >= byts / (PEAK_HBM_GBS * 1e9) else "hbm"
+    traffic = measured_traffic(dom, args.config)
+    nl = launches_of[dom]
     if bound == "mfma":
         ach = flops / (us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom), "kernel": dom}
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
     else:
         ach = byts / (us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(dom), "kernel": dom}
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    roof.update({"traffic": None if traffic is None else round(traffic / nl), "kernel": dom,
+                 "launches_per_round": nl, "avg_launch_us": round(us / nl, 2),
+                 "algorithmic_per_launch": round((flops if bound == "mfma" else byts) / nl)})
 
-    cpu = None
-    if args.cpu_requests > 0:
-        cpu = cpu_baseline(rnd, min(args.cpu_requests, R))
+    peaks = measured_peaks(torch)
+    cpu = cpu_baseline(rnd, args.cpu_sample) if args.cpu_sample > 0 else None
 
     lat_ms = sorted(x * 1e3 for x in lat)
     value = T / (ms_per_step * 1e-3)
+    n_req = [len(s.requests) for s in subs]
+    sub_note = (f"whole round as {len(subs)} replays ({' + '.join(map(str, n_req))} requests) of the "
+                f"{'/'.join(str(t.caps_of(t.last[0]).T_cap) for t in tables)}-row buckets") if len(subs) > 1 else \
+        f"one replay of the {tables[0].caps_of(tables[0].last[0]).T_cap}-row bucket"
     rec = {
         "metric": "ForkAttention tokens/s per layer + round latency (ms); % MFMA / HBM roofline",
         "value": round(value, 1),
@@ -324,8 +419,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if rnd.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": spec_cfg.name + ": " + spec_cfg.description + (f"; {sub_note}" if sub_note else ""),
-                   "stream_rows": T, "requests": R, "questions": nq, "bucket_T_cap": caps.T_cap, "seed": args.seed},
+        "config": {"workload": f"{spec_cfg.name}: {spec_cfg.description}; {sub_note}",
+                   "stream_rows": T, "requests": len(rnd.requests),
+                   "questions": sum(len(r.q_len) for r in rnd.requests),
+                   "bucket_table_T_caps": [c.T_cap for c in caps_table], "seed": args.seed},
         "round_latency_ms": {"p10": round(lat_ms[len(lat_ms) // 10], 4), "median": round(lat_ms[len(lat_ms) // 2], 4),
                              "p90": round(lat_ms[(9 * len(lat_ms)) // 10], 4)},
         "per_layer_tokens_per_s": {
@@ -334,10 +431,15 @@ def main():
         },
         "kernels": per_kernel,
         "roofline": roof,
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
+    if "attn_core_swa" in kernels:
+        rec["per_layer_tokens_per_s"]["swa"] = round(T / ((kernels["attn_prepare_swa"] + kernels["attn_core_swa"])
+                                                          * 1e-6), 1)
     print(json.dumps(rec), flush=True)
-    ctx.close()
+    for tab in tables:
+        tab.close()
 
 
 if __name__ == "__main__":

@@ -63,9 +63,10 @@ typedef enum { FLIDE_F32 = 0, FLIDE_BF16 = 1 } flide_dtype;
 
 typedef struct flide_ctx flide_ctx;
 
-/* Static description of the status code (never NULL). */
+/* Infrastructure (no passage of the pages defines error reporting).
+ * Static description of the status code (never NULL). */
 const char* flide_status_string(int32_t status);
-/* Library version string (never NULL). */
+/* Infrastructure.  Library version string (never NULL). */
 const char* flide_version(void);
 
 /* ------------------------------------------------------------------------
@@ -153,11 +154,17 @@ typedef struct {
   int32_t reserved;
 } flide_meta_layout;
 
-/* Offsets and sizes of a metadata image for `caps` (host only, no GPU needed).
+/* Offsets and sizes of a metadata image for `caps` (host only, no GPU needed): the
+ * device buffers of segment lengths, positions, key ranges and state indices that
+ * each round rewrites before its graph replay ([ZH] §方法步骤详情 third step;
+ * [KO] §어떻게 쓰나).  out (host) is written on success only.
  * Errors: FLIDE_E_INVALID_ARG for NULL pointers or capacities < 1 or too large. */
 flide_status flide_meta_layout_for(const flide_caps* caps, flide_meta_layout* out);
 
-/* Stream rows T, segments and questions a round needs (host only).
+/* Stream rows T, segments and questions a round needs (host only): T is the
+ * padding-free stream length P - m + sum |q_i| summed over the requests, the
+ * P + sum |q_i| work of [KO] §어떻게 동작하나 (minus any checkpointed prefix).
+ * T, n_seg, n_qst (host, each may be NULL) are written on success only.
  * Errors: FLIDE_E_INVALID_ARG for an invalid request (m > P, |q| < 1, m > 0
  * without a checkpoint slot, negative sizes, ...).                            */
 flide_status flide_plan_sizes(const flide_request* reqs, int32_t R, int32_t* T, int32_t* n_seg,
@@ -185,16 +192,27 @@ flide_status flide_split_round(const flide_request* reqs, int32_t R, int32_t T_m
  * Context
  * ------------------------------------------------------------------------ */
 
-/* Create a context on HIP device `device` (makes it current on this thread).
- * Errors: FLIDE_E_INVALID_ARG (NULL out), FLIDE_E_HIP (no such device, or not gfx950). */
+/* Infrastructure (owner of the graph buckets of [KO] §어떻게 쓰나).
+ * Create a context on HIP device `device` (makes it current on this thread);
+ * *out (host) receives the library-owned handle, NULL on error.
+ * Errors: FLIDE_E_INVALID_ARG (NULL out), FLIDE_E_HIP (no such device),
+ * FLIDE_E_UNSUPPORTED (not gfx950). */
 flide_status flide_create(flide_ctx** out, int32_t device);
-/* Free graphs, pinned staging and rotary tables.  Never frees caller memory.
- * Synchronises the device first.  NULL is a no-op. */
+/* Infrastructure.  Free graphs, pinned staging and rotary tables.  Never frees
+ * caller memory.  Synchronises the device first.  NULL is a no-op. */
 void flide_destroy(flide_ctx* ctx);
-/* Message of the last failing call on this context ("" if none; never NULL). */
+/* Infrastructure.  Message of the last failing call on this context ("" if
+ * none; never NULL; owned by the context, valid until its next call). */
 const char* flide_last_error(const flide_ctx* ctx);
+/* Infrastructure.  The raw hipError_t of the last call on this context that
+ * returned FLIDE_E_HIP (0 = hipSuccess if none did; 0 for a NULL context).
+ * Calls that fail for other reasons leave it unchanged. */
+int32_t flide_last_hip_error(const flide_ctx* ctx);
 
-/* Upload a metadata image and expand the per-row arrays on the device.
+/* Per-round metadata write ([ZH] §方法步骤详情 third step: each round only
+ * rewrites the device buffers of segment lengths, positions, key ranges and
+ * state indices; [ZH] §方法步骤详情 first step: every row carries (j, c, t)).
+ * Upload a metadata image and expand the per-row arrays on the device.
  * image (host): written by flide_plan_round for `caps`; dev_meta (device):
  * layout.dev_words int32 words.  The image is copied into library-owned pinned
  * staging before the call returns, so the caller may reuse `image` at once.
@@ -212,8 +230,8 @@ flide_status flide_meta_upload(flide_ctx* ctx, const flide_caps* caps, const int
  * positions (rotate-half pairs (i, i + d/2), angle t * theta^(-2i/d), fp64 host
  * table stored as fp32).  Grouped-query heads: q head h reads kv head
  * h / (Hq / Hkv).  Scores scaled by 1/sqrt(d); fp32 softmax and accumulation.
- *  Hq, Hkv, d   heads and head size; Hq % Hkv == 0.  bf16: d == 256 or 128
- *               (MFMA path); f32: any even d <= 256.
+ *  Hq, Hkv, d   heads and head size; Hq % Hkv == 0; d a multiple of 8 in
+ *               [8, 256] (bf16 with d == 128 or 256 runs on the MFMA path).
  *  window       0 = full attention, else W >= 1
  *  theta        rotary base
  *  max_pos      exclusive bound on every position of the rounds run (rotary table size)
@@ -231,8 +249,9 @@ typedef struct {
   int32_t deterministic;
 } flide_attn_params;
 
-/* Bytes of the workspace flide_fork_attn needs for `caps` (rotated keys and, on the
- * bf16 MFMA path, transposed values).  Zero-fill the workspace once when allocating it:
+/* Infrastructure (sizes the scratch of the rotation of [ZH] §方法步骤详情).
+ * Bytes of the workspace flide_fork_attn needs for `caps` (rotated keys and, on the
+ * bf16 MFMA path, transposed values); *bytes (host) written on success.  Zero-fill the workspace once when allocating it:
  * columns between segments are read under a zero mask and must hold finite values. */
 flide_status flide_attn_workspace_bytes(const flide_caps* caps, const flide_attn_params* p, int64_t* bytes);
 
@@ -311,7 +330,8 @@ flide_status flide_attn_core(flide_ctx* ctx, const flide_caps* caps, const int32
  * and before the workspace is reused.  p->cache_rows must be >= every save_m;
  * a slot or position outside the cache sets the device error word (read by
  * flide_check_device).  The GDN half of the checkpoint is written by
- * flide_fork_gdn phase 0.
+ * flide_fork_gdn phase 0.  Whole rounds (flide_graph_capture, flide_round_eager)
+ * run this step themselves after each attention layer that has a K/V cache.
  * Errors: FLIDE_E_INVALID_ARG (NULL buffers, no cache), FLIDE_E_UNSUPPORTED, FLIDE_E_HIP. */
 flide_status flide_attn_save_kv(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
                                 const flide_attn_params* p, const void* v, const void* workspace, void* k_cache,
@@ -380,22 +400,35 @@ typedef struct {
 } flide_round_bufs;
 
 /* Capture the whole round (metadata expansion, GDN phases 0 and 1, attention
- * layers, readout) into a HIP graph for capacity bufs->caps.  Launch shapes
+ * layers, the checkpoint K/V of requests with save_m > 0 when the layer has a
+ * K/V cache, readout) into a HIP graph for capacity bufs->caps.  Launch shapes
  * depend only on the capacity; kernels read their work from the metadata.
  * *bucket_id receives the bucket's id.  Errors: FLIDE_E_INVALID_ARG,
  * FLIDE_E_UNSUPPORTED, FLIDE_E_HIP.                                           */
 flide_status flide_graph_capture(flide_ctx* ctx, const flide_round_bufs* bufs, void* stream, int32_t* bucket_id);
-/* Smallest captured bucket whose capacity holds (T, R, n_q); FLIDE_E_CAPACITY if none. */
+/* Bucket choice ([KO] §어떻게 쓰나: the smallest captured graph that fits the
+ * round).  Smallest live captured bucket whose capacity holds (T, R, n_q);
+ * *bucket_id (host) written on success.  FLIDE_E_CAPACITY if none. */
 flide_status flide_select_bucket(const flide_ctx* ctx, int32_t T, int32_t R, int32_t n_q, int32_t* bucket_id);
-/* Upload `image` (host, planned for the bucket's caps) into the bucket's
- * metadata through double-buffered pinned staging, then launch the graph. */
+/* Graph replay ([ZH] §核心方法: rewrite the buffers, replay the same graph).
+ * Upload `image` (host, planned for the bucket's caps) into the bucket's
+ * metadata through double-buffered pinned staging, then launch the graph.
+ * Errors: FLIDE_E_INVALID_ARG (no such or released bucket, NULL image),
+ * FLIDE_E_CAPACITY (image planned for larger caps), FLIDE_E_HIP. */
 flide_status flide_graph_replay(flide_ctx* ctx, int32_t bucket_id, const int32_t* image, void* stream);
+/* Infrastructure (the capacity buckets of [KO] §어떻게 쓰나 are captured at
+ * init; a caller that frees a bucket's buffers releases its graph first).
+ * Destroy bucket `bucket_id`'s graph and staging after the device is idle; the
+ * id is never reused, and flide_graph_replay / flide_select_bucket skip it.
+ * Errors: FLIDE_E_INVALID_ARG (no such or already released bucket), FLIDE_E_HIP. */
+flide_status flide_graph_release(flide_ctx* ctx, int32_t bucket_id);
 /* The same kernel sequence launched one by one (no graph), e.g. for a single
  * request above the largest capacity ([KO] §어떻게 쓰나).                      */
 flide_status flide_round_eager(flide_ctx* ctx, const flide_round_bufs* bufs, const int32_t* image, void* stream);
 
-/* Synchronise `stream`, read and clear the device error word of dev_meta.
- * Returns FLIDE_E_DEVICE (with a message) if a kernel flagged bad metadata.  */
+/* Infrastructure.  Synchronise `stream`, read and clear the device error word
+ * of dev_meta (device).  Returns FLIDE_E_DEVICE (with a message) if a kernel
+ * flagged bad metadata, FLIDE_E_HIP if the stream reports an error.          */
 flide_status flide_check_device(flide_ctx* ctx, const flide_caps* caps, int32_t* dev_meta, void* stream);
 
 #ifdef __cplusplus

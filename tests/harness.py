@@ -60,20 +60,50 @@ def run_gpu(rnd, ctx, mode: str = "direct", spec=None, bufs=None, repeats: int =
     img = F.flide_plan_round(rnd.requests, bufs.caps)
     print(f"[gpu] mode={mode} T={lay['T']} R={lay['R']} n_q={lay['n_qst']} caps=({bufs.caps.T_cap},"
           f"{bufs.caps.R_cap},{bufs.caps.Q_cap}) dtype={rnd.dtype}", flush=True)
+    bid = None
+    if mode == "graph":
+        bid = F.flide_graph_capture(ctx, bufs.round_bufs())
     for _ in range(repeats):
         if mode == "direct":
             bufs.upload(ctx, img)
             bufs.run_layers(ctx)
         elif mode == "graph":
-            bid = F.flide_graph_capture(ctx, bufs.round_bufs())
             F.flide_graph_replay(ctx, bid, img)
         elif mode == "eager":
             F.flide_round_eager(ctx, bufs.round_bufs(), img)
         else:
             raise ValueError(mode)
     torch.cuda.synchronize()
+    if bid is not None:  # the graph holds the buffers' addresses: release it before they can be freed
+        F.flide_graph_release(ctx, bid)
     F.flide_check_device(ctx, bufs.caps, bufs.dev_meta)
     return bufs, lay
+
+
+def run_split(rnd, tables, t_max: Optional[int] = None):
+    """Run ``rnd`` through bucket tables: split at request boundaries for the tables' largest capacity (or
+    ``t_max``), sub-round k filled into table k mod len(tables) (placement by the oracle's layout) and all
+    sub-rounds replayed back to back, each in the smallest bucket that holds it.  Tables must not be reused
+    within one call (len(tables) >= number of sub-rounds).  Returns [(sub-round, table, layout)]."""
+    import torch
+    from tree_forked_hybrid_amd import flide as F
+    t_max = t_max or max(c.T_cap for t in tables for c, _, _ in t.buckets.values())
+    first, eager = F.flide_split_round(rnd.requests, t_max)
+    assert not any(eager) and len(eager) <= len(tables), (eager, len(tables))
+    out = []
+    for k in range(len(eager)):
+        sub = rnd.subset(list(range(first[k], first[k + 1])))
+        lay = olayout.build_layout(sub.requests)
+        tables[k].bufs.fill(sub, lay)
+        out.append((sub, tables[k], lay))
+    for sub, tab, _ in out:
+        bid = tab.run(sub.requests)
+        print(f"[gpu] split sub-round: {len(sub.requests)} requests, T={tab.last[1][tab.bufs.layout.hdr]} "
+              f"bucket T_cap={tab.caps_of(bid).T_cap}", flush=True)
+    torch.cuda.synchronize()
+    for _, tab, _ in out:
+        tab.check()
+    return out
 
 
 def outputs(bufs) -> Dict[str, np.ndarray]:

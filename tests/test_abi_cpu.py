@@ -39,6 +39,16 @@ def test_library_exports_every_declared_function():
     assert sorted(F.exported_names()) == declared
 
 
+def test_error_queries_without_a_context():
+    """The error queries answer for a NULL context (no GPU needed): no message, no HIP error; entry points
+    that need a context refuse NULL before touching anything."""
+    lib = F.load_library()
+    assert F.flide_last_hip_error(None) == 0
+    assert lib.flide_last_error(None) == b""
+    assert lib.flide_graph_release(None, 0) == F.FLIDE_E_INVALID_ARG
+    assert lib.flide_select_bucket(None, 1, 1, 0, None) == F.FLIDE_E_INVALID_ARG
+
+
 def test_status_strings_and_version():
     lib = F.load_library()
     for s in range(7):

@@ -40,6 +40,7 @@ struct Bucket {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   Staging st;
+  bool live = true;  // false once released: the id is never reused, replays of it are rejected
 };
 
 }  // namespace
@@ -47,6 +48,7 @@ struct Bucket {
 struct flide_ctx {
   int device = 0;
   std::string err;
+  int hip_err = 0;  // raw hipError_t behind the last FLIDE_E_HIP
   std::vector<RopeTable> ropes;
   std::vector<Bucket*> buckets;
   Staging direct;
@@ -60,11 +62,15 @@ flide_status fail(flide_ctx* ctx, flide_status st, const std::string& msg) {
   return st;
 }
 
-#define FLIDE_HIP(ctx, call)                                                                          \
-  do {                                                                                                \
-    hipError_t e_ = (call);                                                                           \
-    if (e_ != hipSuccess)                                                                             \
-      return fail(ctx, FLIDE_E_HIP, std::string(#call) + ": " + hipGetErrorString(e_));                \
+flide_status fail_hip(flide_ctx* ctx, hipError_t e, const std::string& what) {
+  if (ctx) ctx->hip_err = int(e);
+  return fail(ctx, FLIDE_E_HIP, what + ": " + hipGetErrorString(e));
+}
+
+#define FLIDE_HIP(ctx, call)                              \
+  do {                                                    \
+    hipError_t e_ = (call);                               \
+    if (e_ != hipSuccess) return fail_hip(ctx, e_, #call); \
   } while (0)
 
 #define FLIDE_TRY(expr)                     \
@@ -74,7 +80,7 @@ flide_status fail(flide_ctx* ctx, flide_status st, const std::string& msg) {
   } while (0)
 
 flide_status launched(flide_ctx* ctx, int rc, const char* what) {
-  if (rc != 0) return fail(ctx, FLIDE_E_HIP, std::string(what) + ": " + hipGetErrorString(hipError_t(rc)));
+  if (rc != 0) return fail_hip(ctx, hipError_t(rc), what);
   return FLIDE_OK;
 }
 
@@ -108,6 +114,15 @@ void staging_free(Staging& st) {
     st.done[i] = nullptr;
   }
   st.words = 0;
+}
+
+void bucket_free(Bucket* b) {
+  if (b->exec) (void)hipGraphExecDestroy(b->exec);
+  if (b->graph) (void)hipGraphDestroy(b->graph);
+  b->exec = nullptr;
+  b->graph = nullptr;
+  staging_free(b->st);
+  b->live = false;
 }
 
 // Copy `words` of `image` into the next pinned buffer (waiting until its
@@ -159,7 +174,7 @@ flide_status ensure_rope(flide_ctx* ctx, double theta, int d, int max_pos, RopeA
   hipError_t e = hipMemcpy(dev, h.data(), h.size() * sizeof(float), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(dev);
-    return fail(ctx, FLIDE_E_HIP, std::string("hipMemcpy(rope table): ") + hipGetErrorString(e));
+    return fail_hip(ctx, e, "hipMemcpy(rope table)");
   }
   ctx->ropes.push_back({theta, d, max_pos, dev});
   out->table = dev;
@@ -187,6 +202,9 @@ flide_status check_gdn(flide_ctx* ctx, const flide_gdn_params* p, int32_t n_slot
   auto ok_dim = [](int v) { return v == 16 || v == 32 || v == 64 || v == 128; };
   if (p->H < 1 || !ok_dim(p->dk) || !ok_dim(p->dv))
     return fail(ctx, FLIDE_E_UNSUPPORTED, "GDN needs H >= 1 and dk, dv in {16, 32, 64, 128}");
+  // the per-token kernel covers value blocks of min(dv, 32) channels for dk >= value block
+  if (p->dk < (p->dv >= 32 ? 32 : p->dv))
+    return fail(ctx, FLIDE_E_UNSUPPORTED, "GDN needs dk >= min(dv, 32)");
   if (p->conv_k < 1 || p->conv_k > 4) return fail(ctx, FLIDE_E_UNSUPPORTED, "conv width must be 1..4");
   if (p->act != 0 && p->act != 1) return fail(ctx, FLIDE_E_INVALID_ARG, "act must be 0 (none) or 1 (SiLU)");
   if (p->dtype != FLIDE_F32 && p->dtype != FLIDE_BF16) return fail(ctx, FLIDE_E_UNSUPPORTED, "dtype must be f32 or bf16");
@@ -260,9 +278,18 @@ flide_status enqueue_round(flide_ctx* ctx, const flide_round_bufs* b, hipStream_
                         b->n_slots, b->o_gdn, stream));
   FLIDE_TRY(enqueue_gdn(ctx, mv, b->gdn, 1, b->x, b->conv_w, b->alpha, b->eta, b->state_pool, b->conv_pool,
                         b->n_slots, b->o_gdn, stream));
-  for (int l = 0; l < b->n_attn; ++l)
-    FLIDE_TRY(enqueue_attn(ctx, mv, b->attn[l], b->q[l], b->k[l], b->v[l], b->k_cache[l], b->v_cache[l],
-                           b->o_attn[l], b->attn_ws[l], stream));
+  for (int l = 0; l < b->n_attn; ++l) {
+    const flide_attn_params& ap = b->attn[l];
+    FLIDE_TRY(enqueue_attn(ctx, mv, ap, b->q[l], b->k[l], b->v[l], b->k_cache[l], b->v_cache[l], b->o_attn[l],
+                           b->attn_ws[l], stream));
+    // interior checkpoints of the round (requests with save_m > 0): their K/V go to the cache slot
+    // from the workspace the prepare step just wrote; requests without one exit at once
+    if (ap.cache_rows > 0 && b->k_cache[l] && b->v_cache[l])
+      FLIDE_TRY(launched(ctx,
+                         launch_attn_save_kv(mv, ap, b->v[l], b->attn_ws[l], const_cast<void*>(b->k_cache[l]),
+                                             const_cast<void*>(b->v_cache[l]), stream),
+                         "attn_save_kv"));
+  }
   if (!b->h || !b->w_opt || !b->opt_off || !b->opt_id || !b->probs)
     return fail(ctx, FLIDE_E_INVALID_ARG, "readout buffer is NULL");
   FLIDE_TRY(launched(ctx, launch_readout(mv, b->ro, b->h, b->w_opt, b->opt_off, b->opt_id, b->n_opt_rows,
@@ -315,9 +342,7 @@ void flide_destroy(flide_ctx* ctx) {
   (void)hipSetDevice(ctx->device);
   (void)hipDeviceSynchronize();
   for (Bucket* b : ctx->buckets) {
-    if (b->exec) (void)hipGraphExecDestroy(b->exec);
-    if (b->graph) (void)hipGraphDestroy(b->graph);
-    staging_free(b->st);
+    bucket_free(b);
     delete b;
   }
   staging_free(ctx->direct);
@@ -327,6 +352,8 @@ void flide_destroy(flide_ctx* ctx) {
 }
 
 const char* flide_last_error(const flide_ctx* ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+int32_t flide_last_hip_error(const flide_ctx* ctx) { return ctx ? ctx->hip_err : 0; }
 
 flide_status flide_meta_upload(flide_ctx* ctx, const flide_caps* caps, const int32_t* image, int32_t* dev_meta,
                                void* stream) {
@@ -467,7 +494,7 @@ flide_status flide_graph_capture(flide_ctx* ctx, const flide_round_bufs* bufs, v
     hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) {
       delete b;
-      return fail(ctx, FLIDE_E_HIP, std::string("hipStreamBeginCapture: ") + hipGetErrorString(e));
+      return fail_hip(ctx, e, "hipStreamBeginCapture");
     }
     flide_status st = enqueue_round(ctx, bufs, cs);
     hipGraph_t g = nullptr;
@@ -476,14 +503,14 @@ flide_status flide_graph_capture(flide_ctx* ctx, const flide_round_bufs* bufs, v
       if (g) (void)hipGraphDestroy(g);
       delete b;
       if (st != FLIDE_OK) return st;
-      return fail(ctx, FLIDE_E_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+      return fail_hip(ctx, e, "hipStreamEndCapture");
     }
     b->graph = g;
     e = hipGraphInstantiate(&b->exec, g, nullptr, nullptr, 0);
     if (e != hipSuccess) {
       (void)hipGraphDestroy(g);
       delete b;
-      return fail(ctx, FLIDE_E_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+      return fail_hip(ctx, e, "hipGraphInstantiate");
     }
     st = staging_init(ctx, b->st, b->L.host_words);
     if (st != FLIDE_OK) {
@@ -504,6 +531,7 @@ flide_status flide_select_bucket(const flide_ctx* ctx, int32_t T, int32_t R, int
   if (!ctx || !bucket_id) return FLIDE_E_INVALID_ARG;
   int best = -1;
   for (size_t i = 0; i < ctx->buckets.size(); ++i) {
+    if (!ctx->buckets[i]->live) continue;
     const flide_caps& c = ctx->buckets[i]->bufs.caps;
     if (c.T_cap >= T && c.R_cap >= R && c.Q_cap >= n_q) {
       if (best < 0 || c.T_cap < ctx->buckets[size_t(best)]->bufs.caps.T_cap) best = int(i);
@@ -517,8 +545,8 @@ flide_status flide_select_bucket(const flide_ctx* ctx, int32_t T, int32_t R, int
 flide_status flide_graph_replay(flide_ctx* ctx, int32_t bucket_id, const int32_t* image, void* stream) {
   if (!ctx) return FLIDE_E_INVALID_ARG;
   try {
-    if (bucket_id < 0 || size_t(bucket_id) >= ctx->buckets.size())
-      return fail(ctx, FLIDE_E_INVALID_ARG, "no such bucket");
+    if (bucket_id < 0 || size_t(bucket_id) >= ctx->buckets.size() || !ctx->buckets[size_t(bucket_id)]->live)
+      return fail(ctx, FLIDE_E_INVALID_ARG, "no such bucket (never captured, or released)");
     if (!image) return fail(ctx, FLIDE_E_INVALID_ARG, "image is NULL");
     Bucket* b = ctx->buckets[size_t(bucket_id)];
     FLIDE_TRY(check_image(ctx, b->bufs.caps, b->L, image));
@@ -528,6 +556,21 @@ flide_status flide_graph_replay(flide_ctx* ctx, int32_t bucket_id, const int32_t
     return FLIDE_OK;
   } catch (...) {
     return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_graph_replay");
+  }
+}
+
+flide_status flide_graph_release(flide_ctx* ctx, int32_t bucket_id) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    if (bucket_id < 0 || size_t(bucket_id) >= ctx->buckets.size() || !ctx->buckets[size_t(bucket_id)]->live)
+      return fail(ctx, FLIDE_E_INVALID_ARG, "no such bucket (never captured, or released)");
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    // a replay still in flight holds the graph and the staging: wait for the device first
+    FLIDE_HIP(ctx, hipDeviceSynchronize());
+    bucket_free(ctx->buckets[size_t(bucket_id)]);
+    return FLIDE_OK;
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_graph_release");
   }
 }
 

@@ -59,6 +59,13 @@ constexpr int RAW_COPIES = ((CK + 3) * RAW_STRIDE + 1023) / 1024;  // 1 KB direc
 __device__ __forceinline__ f4v mma16(h4v a, h4v b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
 __device__ __forceinline__ f4v mma32(h8v a, h8v b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
+// Wait states between an MFMA and the first VALU read of its accumulator, issued explicitly.  With the
+// wait states the compiler chose for a bf16 pack (v_cvt_pk_bf16_f32) eight slots after the last
+// 16x16x16 MFMA of an output block, that pack read the accumulator before the MFMA had written it (the
+// first two of the four rows a lane stores came out stale; measured on MI355X); 19 slots cover the
+// longest MFMA of the kernel.
+__device__ __forceinline__ void mfma_read_fence(f4v& v) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(v)); }
+
 __device__ __forceinline__ h4v to_h4(f4v v) { return h4v{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]}; }
 __device__ __forceinline__ h8v cat8(h4v a, h4v b) { return h8v{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
 __device__ __forceinline__ h4v lds4(const _Float16* p) { return *reinterpret_cast<const h4v*>(p); }
@@ -192,21 +199,36 @@ __device__ __forceinline__ void lds_copy(__amdgpu_buffer_rsrc_t r, void* dst, in
 
 // Direct-to-LDS copies for the chunk starting at segment row cc: raw rows cc - 3 .. cc + 63 of the
 // head's q, k and v channels (rows outside the segment read as zero), and (wave 0) alpha, eta of rows
-// cc .. cc + 63.  head_b = byte offset of the head's q channels in a raw row, sect_b = bytes between
-// the q, k and v sections, rowb = bytes per raw row, hstride = bytes between rows of alpha / eta.
-__device__ __forceinline__ void issue_chunk_loads(ChunkIn& I, __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t ar,
-                                                  __amdgpu_buffer_rsrc_t er, int cc, int w, int l, int rowb,
-                                                  int head_b, int sect_b, int hstride) {
+// cc .. cc + 63.  xs, as, es point at the segment's first raw row and its first alpha / eta entry of
+// the head; head_b = byte offset of the head's q channels in a raw row, sect_b = bytes between the q, k
+// and v sections, rowb = bytes per raw row, hstride = bytes between rows of alpha / eta.  Every buffer
+// resource is based at the chunk (the raw one three rows before it, or at the segment start for the
+// first chunk, whose rows -3 .. -1 then fall below the resource and read as zero), so no offset grows
+// with the segment's length or the stream's capacity.
+__device__ __forceinline__ void issue_chunk_loads(ChunkIn& I, const bf16_t* xs, const float* as, const float* es,
+                                                  int len, int cc, int w, int l, int64_t rowb, int head_b, int sect_b,
+                                                  int hstride) {
+  const int nrow = min(len - cc, CK);  // >= 1
   if (w == 0) {
-    lds_copy<4>(ar, I.alpha, (cc + l) * hstride);
-    lds_copy<4>(er, I.eta, (cc + l) * hstride);
+    const int64_t eoff = int64_t(cc) * hstride / 4;
+    const int bytes = ((nrow - 1) * hstride / 4 + 1) * 4;
+    const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc((void*)(as + eoff), 0, bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc((void*)(es + eoff), 0, bytes, 0x00020000);
+    lds_copy<4>(ar, I.alpha, l * hstride);
+    lds_copy<4>(er, I.eta, l * hstride);
   }
+  const int base_row = cc == 0 ? 0 : cc - 3;  // first raw row inside the resource
+  const int nraw = min(len - base_row, CK + 3);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const unsigned char*>(xs) + int64_t(base_row) * rowb), 0, int(nraw * rowb), 0x00020000);
+  const int rb32 = int(rowb);
   for (int cp = w; cp < RAW_COPIES; cp += NT / 64) {
     const int byte = cp * 1024 + 16 * l;
     const int row = byte / RAW_STRIDE, col = byte - row * RAW_STRIDE;
     const int chb = (col >> 8) * sect_b + head_b + (col & 255);
-    // padding bytes and rows past the tile: zero fill (never read)
-    const int voff = row < CK + 3 && col < RAW_ROW ? (cc - 3 + row) * rowb + chb : 0x7FFFFFF0;
+    // padding bytes and rows past the tile: zero fill (never read); rows before the segment have a
+    // negative offset, which the hardware takes as a huge unsigned one: outside the resource, zero
+    const int voff = row < CK + 3 && col < RAW_ROW ? (cc - 3 + row - base_row) * rb32 + chb : 0x7FFFFFF0;
     lds_copy<16>(xr, I.raw + cp * 1024, voff);
   }
 }
@@ -310,8 +332,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
   // (K - 1 rows before the segment).  A row outside either reads as zero (out-of-range buffer
   // loads return 0; a negative byte offset wraps past the end), which is the conv's zero padding.
   const int rowb = int(C) * 2;  // bytes per raw row
-  const __amdgpu_buffer_rsrc_t xr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(x + int64_t(row0) * C), 0, len * rowb, 0x00020000);
+  const bf16_t* const xs = x + int64_t(row0) * C;
   const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(hist != nullptr ? hist : x), 0, hist != nullptr ? (K - 1) * rowb : 0, 0x00020000);
   const int hoff = (K - 1) * rowb;  // byte offset of segment row 0 in the history window's row numbering
@@ -352,18 +373,11 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
 
   // The copies of the next chunk are issued once the current chunk's conv is done with the tile; the
   // first chunk's history rows are patched in at its top.
-  const __amdgpu_buffer_rsrc_t ar =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(alpha + int64_t(row0) * H + h), 0, len > 0 ? ((len - 1) * H + 1) * 4 : 0,
-                                        0x00020000);
-  const __amdgpu_buffer_rsrc_t er =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(eta + int64_t(row0) * H + h), 0, len > 0 ? ((len - 1) * H + 1) * 4 : 0,
-                                        0x00020000);
+  const float* const as = alpha + int64_t(row0) * H + h;
+  const float* const es = eta + int64_t(row0) * H + h;
   const int head_b = h * DK * 2, sect_b = H * DK * 2;
-  // outputs of the segment's rows [0, len): stores past the segment fall outside the resource
   const int rowo = H * DV * 2;  // bytes per output row
-  const __amdgpu_buffer_rsrc_t orr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(o + int64_t(row0) * H * DV), 0, len * rowo, 0x00020000);
-  if (len > 0) issue_chunk_loads(I, xr, ar, er, 0, w, l, rowb, head_b, sect_b, H * 4);
+  if (len > 0) issue_chunk_loads(I, xs, as, es, len, 0, w, l, rowb, head_b, sect_b, H * 4);
   // rows -3 .. -1 of the first chunk: the conv history window (K - 1 rows; older rows stay zero), loaded
   // beside the first chunk's copies and patched into the tile once those have landed
   constexpr int HIST_THREADS = 3 * RAW_ROW / 16;
@@ -494,7 +508,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
       }
     }
     lds_barrier();
-    if (c0 + CK < len) issue_chunk_loads(I, xr, ar, er, c0 + CK, w, l, rowb, head_b, sect_b, H * 4);
+    if (c0 + CK < len) issue_chunk_loads(I, xs, as, es, len, c0 + CK, w, l, rowb, head_b, sect_b, H * 4);
     // ---- Gram blocks, held in registers until every wave is done with the lo tiles.  Waves 4-7 take
     // two P blocks and one strictly lower A block each; waves 0-3 one remaining block and, one each,
     // the diagonal A blocks and their inverses: the substitution chain runs on the older wave of each
@@ -572,10 +586,15 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
       for (int p2 = 0; 2 * p2 + 1 < rb; ++p2)
         acc = mma32(lds8(am + 16 * rb * CK + pair_off(p2)), cat8(uh[2 * p2], uh[2 * p2 + 1]), acc);
       if (rb & 1) acc = mma16(lds4(am + 16 * rb * CK + half_off(rb - 1)), uh[rb - 1], acc);
+      if (rb > 0) mfma_read_fence(acc);
       u[rb] = mma16(lds4(&L.tinv[rb][r16][4 * g4]), to_h4(acc), f4v{0.f, 0.f, 0.f, 0.f});
+      mfma_read_fence(u[rb]);
       uh[rb] = to_h4(u[rb]);
     }
     // ---- outputs O = e^g Q S0^T + P U ----
+    // rows of this chunk only: stores past the segment fall outside the resource
+    const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(o + (int64_t(row0) + c0) * H * DV), 0, n * rowo, 0x00020000);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       f4v acc = *reinterpret_cast<const f4v*>(&L.eg[16 * rb + 4 * g4]) * qs[rb];
@@ -583,8 +602,9 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
       for (int p2 = 0; 2 * p2 + 1 <= rb; ++p2)
         acc = mma32(lds8(pm + 16 * rb * CK + pair_off(p2)), cat8(uh[2 * p2], uh[2 * p2 + 1]), acc);
       if ((rb & 1) == 0) acc = mma16(lds4(pm + 16 * rb * CK + half_off(rb)), uh[rb], acc);
+      mfma_read_fence(acc);
       const uint32_t p01 = pack_bf16x2(acc[0], acc[1]), p23 = pack_bf16x2(acc[2], acc[3]);
-      const int ob = (c0 + 16 * rb + 4 * g4) * rowo + (h * DV + ncol) * 2;  // row 16 rb + 4 g4 of this chunk
+      const int ob = (16 * rb + 4 * g4) * rowo + (h * DV + ncol) * 2;  // row 16 rb + 4 g4 of this chunk
       __builtin_amdgcn_raw_buffer_store_b16((unsigned short)p01, orr, ob, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(p01 >> 16), orr, ob + rowo, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b16((unsigned short)p23, orr, ob + 2 * rowo, 0, 0);
@@ -650,9 +670,8 @@ bool gdn_uses_chunk(const flide_gdn_params& p) { return p.dtype == FLIDE_BF16 &&
 int launch_gdn(const MetaView& mv, const flide_gdn_params& p, int phase, const void* x, const float* conv_w,
                const float* alpha, const float* eta, float* state_pool, void* conv_pool, int32_t n_slots, void* o,
                void* stream) {
-  // the chunk kernel addresses a segment's raw rows with 32-bit buffer offsets
-  const bool offsets_fit = int64_t(mv.T_cap + CK) * p.H * (2 * DK + DV) * 2 < (int64_t(1) << 31);
-  if (!gdn_uses_chunk(p) || !offsets_fit)
+  // (buffer offsets of the chunk kernel are relative to each chunk: any capacity and segment length)
+  if (!gdn_uses_chunk(p))
     return launch_gdn_plain(mv, p, phase, x, conv_w, alpha, eta, state_pool, conv_pool, n_slots, o, stream);
   dim3 grid(phase == 0 ? mv.R_cap : (mv.Q_cap > 0 ? mv.Q_cap : 1), p.H);
   auto kern = phase == 0 ? (p.act == 1 ? gdn_chunk_kernel<0, 1> : gdn_chunk_kernel<0, 0>)

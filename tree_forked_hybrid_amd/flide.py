@@ -97,6 +97,7 @@ _SIGNATURES = {
     "flide_create": (C.c_int, [C.POINTER(_VP), C.c_int32]),
     "flide_destroy": (None, [_VP]),
     "flide_last_error": (C.c_char_p, [_VP]),
+    "flide_last_hip_error": (C.c_int32, [_VP]),
     "flide_meta_upload": (C.c_int, [_VP, C.POINTER(flide_caps), C.POINTER(C.c_int32), _VP, _VP]),
     "flide_attn_workspace_bytes": (C.c_int, [C.POINTER(flide_caps), C.POINTER(flide_attn_params),
                                              C.POINTER(C.c_int64)]),
@@ -115,6 +116,7 @@ _SIGNATURES = {
     "flide_graph_capture": (C.c_int, [_VP, C.POINTER(flide_round_bufs), _VP, C.POINTER(C.c_int32)]),
     "flide_select_bucket": (C.c_int, [_VP, C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32)]),
     "flide_graph_replay": (C.c_int, [_VP, C.c_int32, C.POINTER(C.c_int32), _VP]),
+    "flide_graph_release": (C.c_int, [_VP, C.c_int32]),
     "flide_round_eager": (C.c_int, [_VP, C.POINTER(flide_round_bufs), C.POINTER(C.c_int32), _VP]),
     "flide_check_device": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, _VP]),
 }
@@ -385,6 +387,14 @@ def flide_graph_replay(ctx: Context, bucket_id: int, image: np.ndarray, stream=N
     image = np.ascontiguousarray(image, dtype=np.int32)
     _check(load_library().flide_graph_replay(ctx.handle, int(bucket_id), image.ctypes.data_as(C.POINTER(C.c_int32)),
                                              _stream(stream)), "flide_graph_replay", ctx.handle)
+
+
+def flide_graph_release(ctx: Context, bucket_id: int) -> None:
+    _check(load_library().flide_graph_release(ctx.handle, int(bucket_id)), "flide_graph_release", ctx.handle)
+
+
+def flide_last_hip_error(ctx: Optional[Context]) -> int:
+    return int(load_library().flide_last_hip_error(ctx.handle if ctx is not None else None))
 
 
 def flide_round_eager(ctx: Context, bufs: flide_round_bufs, image: np.ndarray, stream=None) -> None:

@@ -8,6 +8,7 @@ computation happens in libflide.so's kernels.
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Dict, List, Optional, Sequence
 
@@ -15,6 +16,8 @@ import numpy as np
 import torch
 
 from . import flide as F
+
+__all__ = ["RoundSpec", "RoundBuffers", "spec_for_round", "bucket_capacities", "BucketTable", "SplitExecutor"]
 
 
 def _torch_dtype(dtype: str):
@@ -106,7 +109,9 @@ class RoundBuffers:
         names = ["attn_q", "attn_k", "attn_v"] + (["swa_q", "swa_k", "swa_v"] if self.n_attn == 2 else []) + \
                 ["gdn_x", "alpha", "eta", "hidden"]
         host = {}
-        pls = [rnd.payload(j) for j in range(len(rnd.requests))]   # generated once per request
+        # generated once per request; requests have generators of their own, so they are drawn in parallel
+        with ThreadPoolExecutor(max_workers=max(1, min(8, len(rnd.requests)))) as ex:
+            pls = list(ex.map(rnd.payload, range(len(rnd.requests))))
         rows_idx = np.empty(T, np.int64)
         at = 0
         for j in range(len(rnd.requests)):
@@ -174,11 +179,21 @@ class RoundBuffers:
 
     # ------------------------------------------------------------------ C structure
     def round_bufs(self) -> F.flide_round_bufs:
-        if self._struct is not None:
-            return self._struct
+        if self._struct is None:
+            self._struct = self.round_bufs_for(self.caps, self.dev_meta)
+        return self._struct
+
+    def round_bufs_for(self, caps: F.flide_caps, dev_meta) -> F.flide_round_bufs:
+        """The round structure over these buffers for a capacity at most theirs (a smaller bucket uses the
+        first rows of every tensor) with its own metadata buffer ``dev_meta``."""
+        if caps.T_cap > self.caps.T_cap or caps.R_cap > self.caps.R_cap or caps.Q_cap > self.caps.Q_cap:
+            raise ValueError("bucket capacity above the buffers' capacity")
+        for l in range(self.n_attn):
+            if F.flide_attn_workspace_bytes(caps, self.attn_params[l]) > self.ws[l].numel():
+                raise ValueError("attention workspace too small for the bucket")
         b = F.flide_round_bufs()
-        b.caps = self.caps
-        b.dev_meta = self.dev_meta.data_ptr()
+        b.caps = caps
+        b.dev_meta = dev_meta.data_ptr() if hasattr(dev_meta, "data_ptr") else int(dev_meta)
         b.n_attn = self.n_attn
         for l in range(self.n_attn):
             b.attn[l] = self.attn_params[l]
@@ -205,7 +220,6 @@ class RoundBuffers:
         b.opt_id = self.opt_id.data_ptr()
         b.n_opt_rows = max(1, self.spec.opt_cap)
         b.probs = self.probs.data_ptr()
-        self._struct = b
         return b
 
     # ------------------------------------------------------------------ direct kernel calls
@@ -249,3 +263,104 @@ def spec_for_round(rnd, T_cap: Optional[int] = None, R_cap: Optional[int] = None
     max_pos = max([r.P + (max(r.q_len) if r.q_len else 0) for r in rnd.requests] + [1])
     return RoundSpec(rnd.shapes, rnd.dtype, T_cap or max(T, 1), R_cap or max(R, 1), Q_cap if Q_cap is not None else Q,
                      max(slots + [0]) + 1, opt_cap or max(n_opt, 1), max_m, max_pos)
+
+
+def bucket_capacities(t_max: int, R_cap: int, Q_cap: int, t_min: int = 2048) -> List[F.flide_caps]:
+    """Capacity table: T_cap = t_min, 1.5 t_min, 2 t_min, 3 t_min, ... up to t_max (powers of two and
+    1.5 times powers of two), each holding R_cap requests and Q_cap questions."""
+    out, t = [], t_min
+    while t < t_max:
+        out.append(t)
+        if t + t // 2 < t_max:
+            out.append(t + t // 2)
+        t *= 2
+    out.append(t_max)
+    return [F.caps_of(t, R_cap, Q_cap) for t in sorted(set(out))]
+
+
+class BucketTable:
+    """One set of round buffers at the largest capacity and a captured graph per capacity of ``caps``
+    (flat-graph execution with capacity buckets: the Korean summary §어떻게 쓰나).  Every bucket's graph
+    reads and writes the same tensors (a bucket uses their first rows) and has a metadata buffer of its
+    own.  The table owns a context of its own, so ``flide_select_bucket`` chooses among this table's
+    buckets; several tables let the sub-rounds of a split round be replayed back to back, each on its
+    own buffers."""
+
+    def __init__(self, spec: RoundSpec, caps: Sequence[F.flide_caps], device: int = 0):
+        self.ctx = F.Context(device)
+        big = max(caps, key=lambda c: c.T_cap)
+        self.bufs = RoundBuffers(RoundSpec(**{**spec.__dict__, "T_cap": big.T_cap,
+                                              "R_cap": max(c.R_cap for c in caps),
+                                              "Q_cap": max(c.Q_cap for c in caps)}))
+        # one workspace per layer, sized for the largest bucket
+        for l in range(self.bufs.n_attn):
+            need = max(F.flide_attn_workspace_bytes(c, self.bufs.attn_params[l]) for c in caps)
+            if need > self.bufs.ws[l].numel():
+                self.bufs.ws[l] = torch.zeros(need, dtype=torch.uint8, device=self.bufs.device)
+        self.buckets: Dict[int, tuple] = {}   # bucket id -> (caps, dev_meta, host image)
+        for c in sorted(caps, key=lambda c: c.T_cap):
+            L = F.flide_meta_layout_for(c)
+            dev_meta = torch.zeros(L.dev_words, dtype=torch.int32, device=self.bufs.device)
+            bid = F.flide_graph_capture(self.ctx, self.bufs.round_bufs_for(c, dev_meta))
+            self.buckets[bid] = (c, dev_meta, np.zeros(L.host_words, np.int32))
+        self.last = None  # (bucket id, image) of the last round run
+
+    def select(self, requests) -> int:
+        T, _, nq = F.flide_plan_sizes(requests)
+        return F.flide_select_bucket(self.ctx, T, len(requests), nq)
+
+    def plan(self, requests, bid: Optional[int] = None):
+        """(bucket id, metadata image) of a round: the smallest bucket that holds it, unless given."""
+        if bid is None:
+            bid = self.select(requests)
+        caps, _, img = self.buckets[bid]
+        return bid, F.flide_plan_round(requests, caps, img)
+
+    def run(self, requests, stream=None, bid: Optional[int] = None) -> int:
+        """Plan the round for its bucket, upload the metadata and replay the bucket's graph."""
+        bid, img = self.plan(requests, bid)
+        F.flide_graph_replay(self.ctx, bid, img, stream)
+        self.last = (bid, img)
+        return bid
+
+    def caps_of(self, bid: int) -> F.flide_caps:
+        return self.buckets[bid][0]
+
+    def dev_meta_of(self, bid: int):
+        return self.buckets[bid][1]
+
+    def check(self, bid: Optional[int] = None) -> None:
+        bid = self.last[0] if bid is None else bid
+        F.flide_check_device(self.ctx, self.caps_of(bid), self.dev_meta_of(bid))
+
+    def close(self) -> None:
+        if self.ctx.handle:
+            torch.cuda.synchronize()
+            for bid in list(self.buckets):
+                F.flide_graph_release(self.ctx, bid)
+            self.buckets.clear()
+            self.ctx.close()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+class SplitExecutor:
+    """A round over the largest capacity split at request boundaries (``flide_split_round``, the Korean
+    summary §어떻게 쓰나): sub-round i runs in bucket table i mod n of ``tables``, so consecutive replays
+    use different buffers and are enqueued back to back; a request longer than every capacity runs
+    eagerly (``flide_round_eager``) in buffers of its own size."""
+
+    def __init__(self, tables: Sequence[BucketTable]):
+        self.tables = list(tables)
+        self.t_max = max(c.T_cap for t in self.tables for c, _, _ in t.buckets.values())
+
+    def split(self, requests):
+        first, eager = F.flide_split_round(requests, self.t_max)
+        return [(first[i], first[i + 1], eager[i]) for i in range(len(eager))]
+
+    def table_of(self, k: int) -> BucketTable:
+        return self.tables[k % len(self.tables)]
