@@ -269,6 +269,22 @@ flide_status flide_fork_attn(flide_ctx* ctx, const flide_caps* caps, const int32
                              const flide_attn_params* p, const void* q, const void* k, const void* v,
                              const void* k_cache, const void* v_cache, void* o, void* workspace, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving loops or
+ * harnesses that forbid hipMalloc): flide_fork_attn without the workspace argument.  The rotated keys
+ * and transposed values go to a device array of this library, one per GPU, that holds 64 MiB of
+ * workspace (flide_attn_workspace_bytes(caps, p) must not exceed it: about 16k stream rows at 4 kv
+ * heads of 256) plus a 16 MiB rotary-table region (max_pos * d * 4 bytes), used when the context
+ * holds no table for (theta, d, max_pos) yet; writing that region the first time waits for `stream`.
+ * The array is set up by flide_create and kept until the process ends.  Every call on one GPU shares
+ * it and it keeps the last call's contents: calls that overlap on one GPU (other streams, other
+ * threads, other contexts) race.  Nothing is allocated on the device.  Arguments and layouts as
+ * flide_fork_attn; results are bit-identical to it.
+ * Errors: FLIDE_E_CAPACITY (workspace or table above the array's size; nothing is launched), and as
+ * flide_fork_attn. */
+flide_status flide_fork_attn_noalloc(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
+                                     const flide_attn_params* p, const void* q, const void* k, const void* v,
+                                     const void* k_cache, const void* v_cache, void* o, void* stream);
+
 /* Gated DeltaNet layer, two calls ([ZH] §前置知识 and §方法步骤详情; [KO]
  * §무엇과 다른가): causal depthwise conv over the raw q|k|v channels (width
  * conv_k, tap conv_k-1 multiplies the current row, no bias), optional SiLU,

@@ -26,6 +26,7 @@ SOURCES = [
     "gdn_kernels.hip",
     "gdn_chunk_kernels.hip",
     "readout_kernels.hip",
+    "noalloc.hip",
 ]
 HEADERS = ["flide_internal.hpp", "device_common.hpp"]
 

@@ -151,14 +151,7 @@ flide_status check_image(flide_ctx* ctx, const flide_caps& caps, const flide_met
 
 // Rotary table [max_pos, d/2, 2] of (cos, sin) for angle t * theta^(-2i/d),
 // evaluated in fp64 on the host and stored as fp32.
-flide_status ensure_rope(flide_ctx* ctx, double theta, int d, int max_pos, RopeArgs* out) {
-  for (auto& t : ctx->ropes) {
-    if (t.theta == theta && t.d == d && t.max_pos >= max_pos) {
-      out->table = t.dev;
-      out->max_pos = t.max_pos;
-      return FLIDE_OK;
-    }
-  }
+std::vector<float> rope_table_host(double theta, int d, int max_pos) {
   const int half = d / 2;
   std::vector<float> h(size_t(max_pos) * half * 2);
   for (int i = 0; i < half; ++i) {
@@ -169,6 +162,24 @@ flide_status ensure_rope(flide_ctx* ctx, double theta, int d, int max_pos, RopeA
       h[(size_t(p) * half + i) * 2 + 1] = float(std::sin(a));
     }
   }
+  return h;
+}
+
+// A table of this context that covers (theta, d, max_pos), if any.
+bool find_rope(const flide_ctx* ctx, double theta, int d, int max_pos, RopeArgs* out) {
+  for (auto& t : ctx->ropes) {
+    if (t.theta == theta && t.d == d && t.max_pos >= max_pos) {
+      out->table = t.dev;
+      out->max_pos = t.max_pos;
+      return true;
+    }
+  }
+  return false;
+}
+
+flide_status ensure_rope(flide_ctx* ctx, double theta, int d, int max_pos, RopeArgs* out) {
+  if (find_rope(ctx, theta, d, max_pos, out)) return FLIDE_OK;
+  std::vector<float> h = rope_table_host(theta, d, max_pos);
   float* dev = nullptr;
   FLIDE_HIP(ctx, hipMalloc((void**)&dev, h.size() * sizeof(float)));
   hipError_t e = hipMemcpy(dev, h.data(), h.size() * sizeof(float), hipMemcpyHostToDevice);
@@ -252,6 +263,19 @@ flide_status enqueue_attn_core(flide_ctx* ctx, const MetaView& mv, const flide_a
                   "attn_core");
 }
 
+// The attention layer over a given rotary table (no table is built here: nothing is allocated).
+flide_status enqueue_attn_with(flide_ctx* ctx, const MetaView& mv, const flide_attn_params& p, const RopeArgs& rope,
+                               const void* q, const void* k, const void* v, const void* kc, const void* vc, void* o,
+                               void* ws, hipStream_t stream) {
+  if (!q || !k || !v || !o || !ws) return fail(ctx, FLIDE_E_INVALID_ARG, "attention buffer is NULL");
+  if (p.cache_rows > 0 && (!kc || !vc || p.cache_slots < 1))
+    return fail(ctx, FLIDE_E_INVALID_ARG, "K/V cache shape given without cache buffers");
+  FLIDE_TRY(launched(ctx, launch_attn_prepare(mv, p, rope, k, v, ws, stream), "attn_prepare"));
+  return launched(ctx, launch_attn_core(mv, p, rope, q, v, p.cache_rows > 0 ? kc : nullptr,
+                                        p.cache_rows > 0 ? vc : nullptr, o, ws, stream),
+                  "attn_core");
+}
+
 flide_status enqueue_attn(flide_ctx* ctx, const MetaView& mv, const flide_attn_params& p, const void* q,
                           const void* k, const void* v, const void* kc, const void* vc, void* o, void* ws,
                           hipStream_t stream) {
@@ -324,6 +348,8 @@ flide_status flide_create(flide_ctx** out, int32_t device) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, device) != hipSuccess) return FLIDE_E_HIP;
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return FLIDE_E_UNSUPPORTED;
+    // the allocation-free entry point's device scratch: its address on this GPU, taken once
+    if (noalloc_scratch_init(device) != int(hipSuccess)) return FLIDE_E_HIP;
     flide_ctx* ctx = new flide_ctx();
     ctx->device = device;
     if (hipStreamCreateWithFlags(&ctx->capture_stream, hipStreamNonBlocking) != hipSuccess) {
@@ -391,6 +417,51 @@ flide_status flide_fork_attn(flide_ctx* ctx, const flide_caps* caps, const int32
     return enqueue_attn(ctx, mv, *p, q, k, v, k_cache, v_cache, o, workspace, (hipStream_t)stream);
   } catch (...) {
     return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_fork_attn");
+  }
+}
+
+flide_status flide_fork_attn_noalloc(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta,
+                                     const flide_attn_params* p, const void* q, const void* k, const void* v,
+                                     const void* k_cache, const void* v_cache, void* o, void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    FLIDE_TRY(check_attn(ctx, p));
+    MetaView mv;
+    FLIDE_TRY(view_of(ctx, caps, dev_meta, &mv));
+    const int64_t need = attn_workspace_bytes(*caps, *p);
+    if (need > kNoAllocWorkspaceBytes)
+      return fail(ctx, FLIDE_E_CAPACITY,
+                  "flide_fork_attn_noalloc: these capacities need " + std::to_string(need) +
+                      " bytes of attention workspace; the library's scratch holds " +
+                      std::to_string(kNoAllocWorkspaceBytes) + " (use flide_fork_attn with a workspace)");
+    void* ws = noalloc_workspace(ctx->device);
+    if (!ws) return fail(ctx, FLIDE_E_INTERNAL, "device scratch was not set up");
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    RopeArgs rope;
+    if (!find_rope(ctx, p->theta, p->d, p->max_pos, &rope)) {
+      // no table of this context covers the call: use the scratch's table region, written from the same
+      // host fp64 evaluation as every other table when it does not already hold these parameters
+      const int64_t tbytes = int64_t(p->max_pos) * p->d * 4;
+      if (tbytes > kNoAllocTableBytes)
+        return fail(ctx, FLIDE_E_CAPACITY,
+                    "flide_fork_attn_noalloc: a rotary table of " + std::to_string(tbytes) +
+                        " bytes does not fit the library's scratch (" + std::to_string(kNoAllocTableBytes) + ")");
+      bool holds = false;
+      float* table = noalloc_table(ctx->device, p->theta, p->d, p->max_pos, &holds, false);
+      if (!table) return fail(ctx, FLIDE_E_INTERNAL, "device scratch was not set up");
+      if (!holds) {
+        std::vector<float> h = rope_table_host(p->theta, p->d, p->max_pos);
+        FLIDE_HIP(ctx, hipMemcpyAsync(table, h.data(), h.size() * sizeof(float), hipMemcpyHostToDevice,
+                                      (hipStream_t)stream));
+        FLIDE_HIP(ctx, hipStreamSynchronize((hipStream_t)stream));  // the host copy is freed on return
+        noalloc_table(ctx->device, p->theta, p->d, p->max_pos, &holds, true);
+      }
+      rope.table = table;
+      rope.max_pos = p->max_pos;
+    }
+    return enqueue_attn_with(ctx, mv, *p, rope, q, k, v, k_cache, v_cache, o, ws, (hipStream_t)stream);
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_fork_attn_noalloc");
   }
 }
 

@@ -21,6 +21,14 @@ enum TileDesc { TD_SEG, TD_ROW0, TD_NROWS, TD_QPOS0, TD_M, TD_P, TD_CKPT, TD_QUE
 constexpr int kHdrWords = 64;
 constexpr int32_t kMagic = 0x464C4944;  // 'FLID'
 
+// Device scratch of the allocation-free attention entry point (one array per GPU, in noalloc.hip).
+constexpr int64_t kNoAllocWorkspaceBytes = int64_t(64) << 20;  // attention workspace
+constexpr int64_t kNoAllocTableBytes = int64_t(16) << 20;      // rotary table: max_pos * d * 4 bytes
+// Takes the array's device address on `device` (current) once and clears it; hipError_t as int.
+int noalloc_scratch_init(int device);
+void* noalloc_workspace(int device);
+float* noalloc_table(int device, double theta, int d, int max_pos, bool* holds, bool claim);
+
 // Header fields.
 enum : int {
   H_T = 0,

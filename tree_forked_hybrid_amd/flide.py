@@ -103,6 +103,8 @@ _SIGNATURES = {
                                              C.POINTER(C.c_int64)]),
     "flide_fork_attn": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.POINTER(flide_attn_params), _VP, _VP, _VP,
                                   _VP, _VP, _VP, _VP, _VP]),
+    "flide_fork_attn_noalloc": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.POINTER(flide_attn_params), _VP, _VP,
+                                          _VP, _VP, _VP, _VP, _VP]),
     "flide_attn_prepare": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.POINTER(flide_attn_params), _VP, _VP, _VP,
                                      _VP]),
     "flide_attn_save_kv": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.POINTER(flide_attn_params), _VP, _VP, _VP,
@@ -333,6 +335,13 @@ def flide_fork_attn(ctx: Context, caps: flide_caps, dev_meta, p: flide_attn_para
     _check(load_library().flide_fork_attn(ctx.handle, C.byref(caps), _ptr(dev_meta), C.byref(p), _ptr(q), _ptr(k),
                                           _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(workspace),
                                           _stream(stream)), "flide_fork_attn", ctx.handle)
+
+
+def flide_fork_attn_noalloc(ctx: Context, caps: flide_caps, dev_meta, p: flide_attn_params, q, k, v, k_cache,
+                            v_cache, o, stream=None) -> None:
+    _check(load_library().flide_fork_attn_noalloc(ctx.handle, C.byref(caps), _ptr(dev_meta), C.byref(p), _ptr(q),
+                                                  _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(o),
+                                                  _stream(stream)), "flide_fork_attn_noalloc", ctx.handle)
 
 
 def flide_attn_prepare(ctx: Context, caps: flide_caps, dev_meta, p: flide_attn_params, k, v, workspace,
