@@ -189,6 +189,47 @@ flide_status flide_split_round(const flide_request* reqs, int32_t R, int32_t T_m
                                int32_t* n_sub, uint8_t* eager);
 
 /* ------------------------------------------------------------------------
+ * Prefix-match checkpoint store (host only, no GPU needed)
+ * ------------------------------------------------------------------------
+ * A request may resume at m from a checkpoint only if its tokens match the
+ * checkpoint's up to m ([KO] §어떻게 쓰나).  The library never sees tokens: the
+ * caller names a prefix by a 64-bit digest of its first m tokens (any hash it
+ * likes; equal digests are taken as equal prefixes).  The store manages the
+ * pool slots [first_slot, first_slot + n_slots) of the state, conv and K/V
+ * pools: it maps (m, digest) to the slot holding that checkpoint, hands out
+ * slots for new checkpoints (free ones first, else evicting the least
+ * recently used committed entry that no round holds), and keeps a reference
+ * count per slot so that a slot a round reads or writes is never evicted.
+ * Not thread safe: one host thread at a time per store.
+ */
+typedef struct flide_ckpt_store flide_ckpt_store;
+
+/* *out (host) receives a store of n_slots slots numbered from first_slot.
+ * Errors: FLIDE_E_INVALID_ARG (NULL out, first_slot < 0, n_slots < 1). */
+flide_status flide_store_create(flide_ckpt_store** out, int32_t first_slot, int32_t n_slots);
+/* Free the store (never touches device memory).  NULL is a no-op. */
+void flide_store_destroy(flide_ckpt_store* store);
+/* Longest committed checkpoint among the caller's n candidates (positions[i] >= 1, the digest of its
+ * tokens 0..positions[i]-1 in digests[i]; host arrays).  On a hit *m_out / *slot_out receive the
+ * position and slot and the slot's reference count grows by one (release it once the round that
+ * resumes from it has completed); on a miss 0 and -1.  Errors: FLIDE_E_INVALID_ARG. */
+flide_status flide_store_lookup(flide_ckpt_store* store, int32_t n, const int32_t* positions,
+                                const uint64_t* digests, int32_t* m_out, int32_t* slot_out);
+/* A slot for a new checkpoint of prefix (m, digest), to pass as a request's save_slot with save_m = m
+ * (or as out_slot for the trunk's end, m = P).  The entry holds one reference and stays invisible to
+ * lookups until flide_store_commit.  Errors: FLIDE_E_INVALID_ARG (m < 1, or the prefix is already
+ * stored or reserved), FLIDE_E_CAPACITY (every slot is held by a round). */
+flide_status flide_store_reserve(flide_ckpt_store* store, int32_t m, uint64_t digest, int32_t* slot_out);
+/* Make a reserved slot visible to lookups: call it once the round that writes the checkpoint has
+ * completed on the device.  Errors: FLIDE_E_INVALID_ARG (not a reserved slot of this store). */
+flide_status flide_store_commit(flide_ckpt_store* store, int32_t slot);
+/* Drop one reference of a slot returned by lookup or reserve.  A reservation released before its
+ * commit frees the slot.  Errors: FLIDE_E_INVALID_ARG (not a held slot of this store). */
+flide_status flide_store_release(flide_ckpt_store* store, int32_t slot);
+/* stats (host, 7 entries): slots, used, committed, held, hits, misses, evictions. */
+flide_status flide_store_stats(const flide_ckpt_store* store, int64_t* stats);
+
+/* ------------------------------------------------------------------------
  * Context
  * ------------------------------------------------------------------------ */
 

@@ -361,6 +361,48 @@ def test_graph_round_writes_checkpoint_kv(ctx):
         np.testing.assert_array_equal(gb[key][rows_b], ga[key][rows_a], err_msg=key)
 
 
+def test_checkpoint_store_round_trip(ctx):
+    """Prefix-match checkpoint store with real rounds: a round writes a checkpoint at position 256 into the
+    slot the store reserves (graph mode, which writes the K/V itself) and commits it after the round has
+    completed; a later round whose first 256 tokens match (same digests) looks it up among candidates every
+    64 positions, resumes there and reproduces the uncut round's later rows bit for bit; a request with a
+    different prefix gets no checkpoint."""
+    import torch
+    from tree_forked_hybrid_amd import flide as F
+    store = F.CheckpointStore(8, 2)
+    digest = lambda rid, m: (rid * 1000003 + m * 7919) & ((1 << 63) - 1)  # the caller's prefix digest
+    base = make_round(1, 0, requests=[0])
+    r0 = base.requests[0]
+    sm = 256
+    slot = store.reserve(sm, digest(0, sm))
+    ra = dataclasses.replace(base, requests=[dataclasses.replace(r0, save_m=sm, save_slot=slot)])
+    ba, la = harness.run_gpu(ra, ctx, "graph")
+    store.commit(slot)
+    store.release(slot)
+    cands = list(range(64, r0.P, 64))
+    m, s = store.lookup(cands, [digest(0, p) for p in cands])
+    assert (m, s) == (sm, slot)
+    assert store.lookup(cands, [digest(1, p) for p in cands]) == (0, -1)
+    ga = harness.outputs(ba)
+    row_keys = ("attn_q", "attn_k", "attn_v", "gdn_x", "alpha", "eta", "hidden")
+    pb = {k: (np.asarray(v)[m:] if k in row_keys else v) for k, v in ra.payload(0).items()}
+    torch.cuda.synchronize()
+    pb["ckpt_state"] = ba.state_pool[s].cpu().numpy()
+    pb["ckpt_window"] = ba.conv_pool[s].float().cpu().numpy()
+    pb["kv_k"] = ba.k_cache[0][s, :m].float().cpu().numpy()
+    pb["kv_v"] = np.transpose(ba.v_cache[0][s, :, :, :m].float().cpu().numpy(), (2, 0, 1))
+    rb = dataclasses.replace(base, requests=[dataclasses.replace(r0, m=m, ckpt_slot=s)], _cache={0: pb})
+    bb, lb = harness.run_gpu(rb, ctx, "graph")
+    store.release(s)
+    gb = harness.outputs(bb)
+    rows_a = harness.stream_rows(ra, la, 0)[m:]
+    rows_b = harness.stream_rows(rb, lb, 0)
+    for key in ("gdn_o", "attn_o"):
+        np.testing.assert_array_equal(gb[key][rows_b], ga[key][rows_a], err_msg=key)
+    assert store.stats()["hits"] == 1 and store.stats()["held"] == 0
+    store.close()
+
+
 def test_parameter_checks_match_the_kernels(ctx):
     """A GDN shape the per-token kernel has no instance for is rejected before anything is launched."""
     import torch

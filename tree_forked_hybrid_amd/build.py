@@ -20,6 +20,7 @@ INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 
 SOURCES = [
     "plan.cpp",
+    "store.cpp",
     "api.cpp",
     "meta_kernels.hip",
     "attn_kernels.hip",

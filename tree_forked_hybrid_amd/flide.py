@@ -94,6 +94,14 @@ _SIGNATURES = {
                                    C.POINTER(C.c_int32), C.c_int64]),
     "flide_split_round": (C.c_int, [C.POINTER(flide_request), C.c_int32, C.c_int32, C.POINTER(C.c_int32),
                                     C.POINTER(C.c_int32), C.POINTER(C.c_uint8)]),
+    "flide_store_create": (C.c_int, [C.POINTER(_VP), C.c_int32, C.c_int32]),
+    "flide_store_destroy": (None, [_VP]),
+    "flide_store_lookup": (C.c_int, [_VP, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_uint64),
+                                     C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
+    "flide_store_reserve": (C.c_int, [_VP, C.c_int32, C.c_uint64, C.POINTER(C.c_int32)]),
+    "flide_store_commit": (C.c_int, [_VP, C.c_int32]),
+    "flide_store_release": (C.c_int, [_VP, C.c_int32]),
+    "flide_store_stats": (C.c_int, [_VP, C.POINTER(C.c_int64)]),
     "flide_create": (C.c_int, [C.POINTER(_VP), C.c_int32]),
     "flide_destroy": (None, [_VP]),
     "flide_last_error": (C.c_char_p, [_VP]),
@@ -283,6 +291,57 @@ def decode_image(image: np.ndarray, caps: flide_caps) -> dict:
     out["tile_row0"] = image[L.tile_row0:L.tile_row0 + n_tiles].copy()
     out["gdn_order"] = image[L.gdn_order:L.gdn_order + n_seg].copy()
     return out
+
+
+# ----------------------------------------------------------------------------- checkpoint store
+
+class CheckpointStore:
+    """A flide_ckpt_store over pool slots [first_slot, first_slot + n_slots) (host only)."""
+
+    def __init__(self, first_slot: int, n_slots: int):
+        h = C.c_void_p()
+        _check(load_library().flide_store_create(C.byref(h), int(first_slot), int(n_slots)), "flide_store_create")
+        self.handle = h.value
+
+    def close(self) -> None:
+        if self.handle:
+            load_library().flide_store_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001
+            pass
+
+    def lookup(self, positions: Sequence[int], digests: Sequence[int]) -> Tuple[int, int]:
+        """(m, slot) of the longest committed prefix among the candidates, (0, -1) if none."""
+        n = len(positions)
+        pos = np.ascontiguousarray(positions, np.int32)
+        dig = np.ascontiguousarray(np.asarray(digests, dtype=np.uint64))
+        m, slot = C.c_int32(), C.c_int32()
+        _check(load_library().flide_store_lookup(self.handle, n, pos.ctypes.data_as(C.POINTER(C.c_int32)),
+                                                 dig.ctypes.data_as(C.POINTER(C.c_uint64)), C.byref(m),
+                                                 C.byref(slot)), "flide_store_lookup")
+        return m.value, slot.value
+
+    def reserve(self, m: int, digest: int) -> int:
+        slot = C.c_int32()
+        _check(load_library().flide_store_reserve(self.handle, int(m), C.c_uint64(int(digest)), C.byref(slot)),
+               "flide_store_reserve")
+        return slot.value
+
+    def commit(self, slot: int) -> None:
+        _check(load_library().flide_store_commit(self.handle, int(slot)), "flide_store_commit")
+
+    def release(self, slot: int) -> None:
+        _check(load_library().flide_store_release(self.handle, int(slot)), "flide_store_release")
+
+    def stats(self) -> dict:
+        out = (C.c_int64 * 7)()
+        _check(load_library().flide_store_stats(self.handle, out), "flide_store_stats")
+        keys = ("slots", "used", "committed", "held", "hits", "misses", "evictions")
+        return {k: int(out[i]) for i, k in enumerate(keys)}
 
 
 # ----------------------------------------------------------------------------- context + kernels
