@@ -25,8 +25,10 @@ Modules:
   gdn        — causal depthwise conv, L2 norm and the per-token gated delta rule
   readout    — option probabilities, Eq. (1)
   round      — a whole round, isolated-prompt ("isolated") or trunk-once ("memo")
+  stack      — a multi-layer hybrid stack (pre-norm residual blocks around the token mixers) over the
+               same isolated prompts, with the readout on question-final rows
 
 Parity status: every function here is pinned by the CPU tests named in its
 docstring; none is "parity unpinned".
 """
-from . import attention, gdn, layout, readout, round  # noqa: F401
+from . import attention, gdn, layout, readout, round, stack  # noqa: F401

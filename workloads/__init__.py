@@ -14,4 +14,8 @@ from .synth import (  # noqa: F401
     custom_round,
     make_round,
     rows_of,
+    LAYER_KINDS,
+    Stack,
+    StackShapes,
+    make_stack,
 )

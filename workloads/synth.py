@@ -34,6 +34,7 @@ TENSOR_IDS = {
     "ckpt_state": 13, "ckpt_window": 14,
     "kv_k": 15, "kv_v": 16, "swa_kv_k": 17, "swa_kv_v": 18,
     "opt_perm": 19,
+    "stack_x": 20, "stack_w": 21, "stack_opt": 22,
 }
 
 
@@ -265,3 +266,120 @@ def custom_round(shapes: LayerShapes, dtype: str, requests: Sequence[Request], b
     """Round with a hand-written structure (edge cases, probes)."""
     reqs = list(requests)
     return Round(base, dtype, shapes, reqs, list(range(len(reqs))), t_max)
+
+
+# ----------------------------------------------------------------------------------------------------
+# Multi-layer synthetic hybrid stacks: seeded random weights of a pre-norm residual stack whose token
+# mixers are Gated DeltaNet, full-attention and sliding-window attention layers, each followed by a
+# SwiGLU MLP.  Only random draws (and bf16 rounding) live here; what the stack computes is written in
+# the oracle and in the HIP kernels.
+# ----------------------------------------------------------------------------------------------------
+
+LAYER_KINDS = ("gdn", "attn", "swa")
+
+
+@dataclass(frozen=True)
+class StackShapes:
+    Dm: int                     # model width (multiple of 32)
+    F: int                      # MLP width (multiple of 32)
+    layers: tuple               # kinds of the token mixers, in order
+    H: int                      # GDN heads
+    dk: int
+    dv: int
+    conv_k: int
+    Hq: int                     # attention heads
+    Hkv: int
+    d: int
+    theta: float
+    window: int                 # window of the "swa" layers
+
+    @property
+    def gdn_channels(self) -> int:
+        return self.H * (2 * self.dk + self.dv)
+
+
+@dataclass
+class Stack:
+    """A seeded stack and a round of requests whose rows are its input embeddings."""
+    base: int
+    dtype: str                  # "f32" or "bf16": storage type of weights and activations
+    shapes: StackShapes
+    requests: List[Request]
+    _w: Optional[dict] = field(default=None, repr=False)
+    _cache: Dict[int, dict] = field(default_factory=dict, repr=False)
+
+    def _act(self, x: np.ndarray) -> np.ndarray:
+        return bf16_round(x) if self.dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
+
+    def weights(self) -> dict:
+        """Per layer: ``norm1``, ``norm2`` gains [Dm] (fp32); mixer projections stored [out, in]; ``gate_up``
+        [2F, Dm] (gate rows, then up rows) and ``down`` [Dm, F].  GDN layers: ``w_x`` [C, Dm] (q | k | v
+        channels), ``w_ab`` [2H, Dm] and ``b_ab`` [2H] (alpha, then eta pre-activations), ``conv_w`` [C, K]
+        (fp32), ``w_o`` [Dm, H dv].  Attention layers: ``w_q`` [Hq d, Dm], ``w_k``, ``w_v`` [Hkv d, Dm],
+        ``w_o`` [Dm, Hq d].  Also ``norm_f`` [Dm], the final norm before the readout."""
+        if self._w is not None:
+            return self._w
+        s = self.shapes
+        out = {"layers": []}
+
+        def normal(shape, scale, *ids):
+            z = _rng(self.base, "stack_w", *ids).standard_normal(shape) * scale
+            return z.astype(np.float32)
+
+        for li, kind in enumerate(s.layers):
+            if kind not in LAYER_KINDS:
+                raise ValueError(kind)
+            L = {"kind": kind}
+            L["norm1"] = (1.0 + normal((s.Dm,), 0.1, li, 0)).astype(np.float32)
+            L["norm2"] = (1.0 + normal((s.Dm,), 0.1, li, 1)).astype(np.float32)
+            L["gate_up"] = self._act(normal((2 * s.F, s.Dm), 1.0 / np.sqrt(s.Dm), li, 2))
+            L["down"] = self._act(normal((s.Dm, s.F), 0.5 / np.sqrt(s.F), li, 3))
+            if kind == "gdn":
+                C = s.gdn_channels
+                L["w_x"] = self._act(normal((C, s.Dm), 1.0 / np.sqrt(s.Dm), li, 4))
+                # alpha = sigmoid(N(2, 0.5)) and eta = sigmoid(N(0, 1)) for unit-variance normalised inputs
+                w_a = normal((s.H, s.Dm), 0.5 / np.sqrt(s.Dm), li, 5)
+                w_e = normal((s.H, s.Dm), 1.0 / np.sqrt(s.Dm), li, 6)
+                L["w_ab"] = self._act(np.concatenate([w_a, w_e], axis=0))
+                L["b_ab"] = np.concatenate([np.full(s.H, 2.0), np.zeros(s.H)]).astype(np.float32)
+                L["conv_w"] = normal((C, s.conv_k), 1.0 / np.sqrt(s.conv_k), li, 7)
+                L["w_o"] = self._act(normal((s.Dm, s.H * s.dv), 0.5 / np.sqrt(s.H * s.dv), li, 8))
+            else:
+                L["w_q"] = self._act(normal((s.Hq * s.d, s.Dm), 1.0 / np.sqrt(s.Dm), li, 9))
+                L["w_k"] = self._act(normal((s.Hkv * s.d, s.Dm), 1.0 / np.sqrt(s.Dm), li, 10))
+                L["w_v"] = self._act(normal((s.Hkv * s.d, s.Dm), 1.0 / np.sqrt(s.Dm), li, 11))
+                L["w_o"] = self._act(normal((s.Dm, s.Hq * s.d), 0.5 / np.sqrt(s.Hq * s.d), li, 12))
+            out["layers"].append(L)
+        out["norm_f"] = (1.0 + normal((s.Dm,), 0.1, 999, 0)).astype(np.float32)
+        self._w = out
+        return out
+
+    def payload(self, j: int) -> dict:
+        """Request j: input embeddings ``x0`` [rows, Dm] (request-local order: trunk, then each question)
+        and option vectors ``w_opt`` [sum n_opt, Dm]."""
+        if j in self._cache:
+            return self._cache[j]
+        r = self.requests[j]
+        n = rows_of(r)
+        x0 = _rng(self.base, "stack_x", j).standard_normal((n, self.shapes.Dm)).astype(np.float32)
+        w = _rng(self.base, "stack_opt", j).standard_normal((int(sum(r.n_opt)), self.shapes.Dm))
+        out = {"x0": self._act(x0), "w_opt": self._act((w / np.sqrt(self.shapes.Dm)).astype(np.float32))}
+        self._cache[j] = out
+        return out
+
+    def segment_rows(self, j: int) -> List[tuple]:
+        r = self.requests[j]
+        segs = [(0, r.P - r.m)]
+        at = r.P - r.m
+        for L in r.q_len:
+            segs.append((at, L))
+            at += L
+        return segs
+
+
+def make_stack(shapes: StackShapes, dtype: str, requests: Sequence[Request], base: int = 5) -> Stack:
+    """A stack of the given shapes over a round with a hand-written structure."""
+    for r in requests:
+        if r.m != 0:
+            raise ValueError("stack rounds start every trunk at position 0")
+    return Stack(base, dtype, shapes, list(requests))
