@@ -217,6 +217,79 @@ def measured_peaks(torch):
     return {"d2d_copy_GB/s": round(copy_gbs, 1), "bf16_gemm_8192_TFLOP/s": round(gemm, 1)}
 
 
+def stack_main(args):
+    """A multi-layer hybrid stack over the short-round workload's structure (64 requests, P~U[256,768], one
+    question of 16..48 rows each): model width 1024, SwiGLU MLP of 2816, eight layers (three GDN layers of
+    16 heads x 128, then full attention of 16 q / 4 kv heads x 256; again, ending with a sliding-window layer
+    of W=1024), bf16, seeded random weights.  Prints one JSON line: whole-stack stream tokens/s (graph
+    replays back to back, each after its metadata upload) and tokens/s per layer (HIP events around each
+    layer of an eager run on the launch stream)."""
+    import numpy as np
+    import torch
+
+    from tree_forked_hybrid_amd import flide as F
+    from tree_forked_hybrid_amd.runner import StackRunner
+    from workloads import StackShapes, make_round, make_stack
+
+    shapes = StackShapes(Dm=1024, F=2816, layers=("gdn", "gdn", "gdn", "attn", "gdn", "gdn", "gdn", "swa"), H=16,
+                         dk=128, dv=128, conv_k=4, Hq=16, Hkv=4, d=256, theta=1e6, window=1024)
+    reqs = make_round(1, args.seed).requests
+    stack = make_stack(shapes, "bf16", reqs, base=9000 + args.seed)
+    T = sum((r.P - r.m) + sum(r.q_len) for r in reqs)
+    n_q = sum(len(r.q_len) for r in reqs)
+    n_opt = sum(sum(r.n_opt) for r in reqs)
+    ctx = F.Context(0)
+    sr = StackRunner(stack, T_cap=_round_up(T, 4096), R_cap=_round_up(len(reqs), 64), Q_cap=_round_up(n_q, 64),
+                     opt_cap=n_opt)
+    img = F.flide_plan_round(reqs, sr.caps)
+    sr.fill(F.decode_image(img, sr.caps))
+    st = torch.cuda.current_stream()
+    sr.upload(ctx, img, st)
+    # per-layer times: events after every layer of an eager run (the last entry: final norm + readout)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(shapes.layers) + 2)]
+    per_layer = np.zeros(len(shapes.layers) + 1)
+    reps = 3
+    for _ in range(reps):
+        sr.fill(F.decode_image(img, sr.caps))
+        torch.cuda.synchronize()
+        ev[0].record(st)
+        sr.run(ctx, st, layer_hook=lambda i: ev[i + 1].record(st))
+        ev[-1].record(st)
+        torch.cuda.synchronize()
+        per_layer += [ev[i].elapsed_time(ev[i + 1]) for i in range(len(ev) - 1)]
+    per_layer *= 1e3 / reps  # us
+    F.flide_check_device(ctx, sr.caps, sr.dev_meta)
+    sr.capture(ctx)
+    for _ in range(args.warmup):
+        sr.replay(ctx, img)
+    torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        sr.replay(ctx, img)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gc.enable()
+    F.flide_check_device(ctx, sr.caps, sr.dev_meta)
+    ms = (t1 - t0) * 1e3 / args.steps
+    layers = [{"layer": i, "kind": k, "us": round(per_layer[i], 1), "tokens_per_s": round(T / (per_layer[i] * 1e-6), 1)}
+              for i, k in enumerate(shapes.layers)]
+    rec = {
+        "metric": "hybrid stack tokens/s per layer (row-wise layers + ForkAttention token mixers)",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic (seeded random weights)",
+        "config": {"workload": "8-layer hybrid stack (GDN x3, full attention, GDN x3, sliding window W=1024), width "
+                               "1024, MLP 2816, over the short-round structure (64 requests, one question each)",
+                   "stream_rows": T, "questions": n_q},
+        "per_layer": layers,
+        "final_norm_and_readout_us": round(per_layer[-1], 1),
+    }
+    print(json.dumps(rec), flush=True)
+    ctx.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,11 +303,17 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="counter pass: one launch of every kernel per sub-round plus a 256 MiB device copy (for "
                          "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE and the copy-kernel scale factor); prints no JSON")
+    ap.add_argument("--stack", action="store_true",
+                    help="time the multi-layer hybrid stack instead of the ForkAttention round (its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the ForkAttention round runs on a single MI355X "
               "(request-sharded multi-GPU rounds are not built); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.stack:
+        stack_main(args)
+        return
 
     import torch
 

@@ -418,6 +418,44 @@ flide_status flide_readout(flide_ctx* ctx, const flide_caps* caps, const int32_t
                            void* stream);
 
 /* ------------------------------------------------------------------------
+ * Row-wise layers of a multi-layer hybrid stack
+ * ------------------------------------------------------------------------
+ * Every layer other than the token mixers acts on each row alone ([ZH]
+ * §方法步骤详情 second step), so on the flat stream it runs over the rows
+ * unchanged; after the last token mixer only the question-final rows are
+ * needed ([ZH] §方法步骤详情 fourth step; [KO] §어떻게 쓰나, selective
+ * readout).  Each call acts on a row set read from dev_meta at run time:
+ * FLIDE_ROWS_ALL = stream rows [0, T), FLIDE_ROWS_QFINAL = the rows
+ * qfin_row[0 .. n_qst); rows outside the set are left untouched, so one
+ * captured graph serves every round of its capacity.  Tensors are row-major
+ * over stream rows in the dtype given (f32 or bf16; gains, biases and gates
+ * fp32); every pointer is caller-owned device memory.
+ */
+typedef enum { FLIDE_ROWS_ALL = 0, FLIDE_ROWS_QFINAL = 1 } flide_rows;
+
+/* y[r] = x[r] / sqrt(mean(x[r]^2) + eps) * g   (x, y [T_cap, D]; g [D] fp32; fp32 accumulation).
+ * x and y may be the same buffer.  Errors: FLIDE_E_INVALID_ARG, FLIDE_E_UNSUPPORTED, FLIDE_E_HIP. */
+flide_status flide_rmsnorm(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta, int32_t rows,
+                           int32_t dtype, int32_t D, const void* x, const float* g, float eps, void* y,
+                           void* stream);
+/* c[r, n] = sum_k a[r, k] w[n, k] (+ resid[r, n]) for n < N: a linear layer with its weight stored
+ * [N, K] (out, in).  a has row stride lda >= K, c and resid row stride ldc >= N; resid may be NULL or c
+ * itself (in-place residual add), never a.  fp32 accumulation (bf16: on MFMA, K a multiple of 32 and lda
+ * of 8; f32: in order along K).  Errors: FLIDE_E_INVALID_ARG, FLIDE_E_UNSUPPORTED, FLIDE_E_HIP. */
+flide_status flide_linear(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta, int32_t rows,
+                          int32_t dtype, int32_t N, int32_t K, const void* a, int64_t lda, const void* w,
+                          const void* resid, void* c, int64_t ldc, void* stream);
+/* out[r, f] = silu(gu[r, f]) * gu[r, F + f]   (gu [T_cap, 2F]: gate | up; out [T_cap, F]).
+ * Errors: FLIDE_E_INVALID_ARG, FLIDE_E_UNSUPPORTED, FLIDE_E_HIP. */
+flide_status flide_swiglu(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta, int32_t rows,
+                          int32_t dtype, int32_t F, const void* gu, void* out, void* stream);
+/* The gates of a Gated DeltaNet layer from a projection z [T_cap, 2H] (dtype): alpha[r, h] =
+ * sigmoid(z[r, h] + bias[h]), eta[r, h] = sigmoid(z[r, H + h] + bias[H + h]) (alpha, eta [T_cap, H] fp32,
+ * the layout flide_fork_gdn reads), over all stream rows.  Errors: as flide_swiglu. */
+flide_status flide_gdn_gates(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta, int32_t dtype,
+                             int32_t H, const void* z, const float* bias, float* alpha, float* eta, void* stream);
+
+/* ------------------------------------------------------------------------
  * Whole rounds: graph buckets per stream capacity ([ZH] §核心方法 and
  * §方法步骤详情 third step; [KO] §어떻게 쓰나)
  * ------------------------------------------------------------------------ */

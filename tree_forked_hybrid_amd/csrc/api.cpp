@@ -546,6 +546,83 @@ flide_status flide_readout(flide_ctx* ctx, const flide_caps* caps, const int32_t
   }
 }
 
+namespace {
+
+flide_status check_rows(flide_ctx* ctx, int32_t rows, int32_t dtype) {
+  if (rows != FLIDE_ROWS_ALL && rows != FLIDE_ROWS_QFINAL)
+    return fail(ctx, FLIDE_E_INVALID_ARG, "rows must be FLIDE_ROWS_ALL or FLIDE_ROWS_QFINAL");
+  if (dtype != FLIDE_F32 && dtype != FLIDE_BF16) return fail(ctx, FLIDE_E_UNSUPPORTED, "dtype must be f32 or bf16");
+  return FLIDE_OK;
+}
+
+}  // namespace
+
+flide_status flide_rmsnorm(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta, int32_t rows,
+                           int32_t dtype, int32_t D, const void* x, const float* g, float eps, void* y,
+                           void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    FLIDE_TRY(check_rows(ctx, rows, dtype));
+    if (D < 1 || !x || !g || !y || !(eps >= 0.f)) return fail(ctx, FLIDE_E_INVALID_ARG, "rmsnorm: bad arguments");
+    MetaView mv;
+    FLIDE_TRY(view_of(ctx, caps, dev_meta, &mv));
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    return launched(ctx, launch_rmsnorm(mv, rows, dtype, D, x, g, eps, y, stream), "rmsnorm");
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_rmsnorm");
+  }
+}
+
+flide_status flide_linear(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta, int32_t rows,
+                          int32_t dtype, int32_t N, int32_t K, const void* a, int64_t lda, const void* w,
+                          const void* resid, void* c, int64_t ldc, void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    FLIDE_TRY(check_rows(ctx, rows, dtype));
+    if (N < 1 || K < 1 || !a || !w || !c || lda < K || ldc < N)
+      return fail(ctx, FLIDE_E_INVALID_ARG, "linear: bad arguments");
+    if (dtype == FLIDE_BF16 && (K % 32 != 0 || lda % 8 != 0))
+      return fail(ctx, FLIDE_E_UNSUPPORTED, "linear (bf16): K must be a multiple of 32 and lda of 8");
+    if (a == c) return fail(ctx, FLIDE_E_INVALID_ARG, "linear: the output must not alias the input rows");
+    MetaView mv;
+    FLIDE_TRY(view_of(ctx, caps, dev_meta, &mv));
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    return launched(ctx, launch_linear(mv, rows, dtype, N, K, a, lda, w, resid, c, ldc, stream), "linear");
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_linear");
+  }
+}
+
+flide_status flide_swiglu(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta, int32_t rows,
+                          int32_t dtype, int32_t F, const void* gu, void* out, void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    FLIDE_TRY(check_rows(ctx, rows, dtype));
+    if (F < 1 || !gu || !out || gu == out) return fail(ctx, FLIDE_E_INVALID_ARG, "swiglu: bad arguments");
+    MetaView mv;
+    FLIDE_TRY(view_of(ctx, caps, dev_meta, &mv));
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    return launched(ctx, launch_swiglu(mv, rows, dtype, F, gu, out, stream), "swiglu");
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_swiglu");
+  }
+}
+
+flide_status flide_gdn_gates(flide_ctx* ctx, const flide_caps* caps, const int32_t* dev_meta, int32_t dtype,
+                             int32_t H, const void* z, const float* bias, float* alpha, float* eta, void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    FLIDE_TRY(check_rows(ctx, FLIDE_ROWS_ALL, dtype));
+    if (H < 1 || !z || !bias || !alpha || !eta) return fail(ctx, FLIDE_E_INVALID_ARG, "gdn_gates: bad arguments");
+    MetaView mv;
+    FLIDE_TRY(view_of(ctx, caps, dev_meta, &mv));
+    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+    return launched(ctx, launch_gates(mv, dtype, H, z, bias, alpha, eta, stream), "gdn_gates");
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_gdn_gates");
+  }
+}
+
 flide_status flide_graph_capture(flide_ctx* ctx, const flide_round_bufs* bufs, void* stream, int32_t* bucket_id) {
   if (!ctx) return FLIDE_E_INVALID_ARG;
   (void)stream;

@@ -144,6 +144,14 @@ int launch_attn_core(const MetaView& mv, const flide_attn_params& p, const RopeA
 // Interior checkpoints: K/V of positions 0..save_m-1 of every saving request into its cache slot.
 int launch_attn_save_kv(const MetaView& mv, const flide_attn_params& p, const void* v, const void* workspace,
                         void* k_cache, void* v_cache, void* stream);
+// Row-wise layers of a stack (stack_kernels.hip); rows_mode 0 = stream rows [0, T), 1 = question-final rows.
+int launch_rmsnorm(const MetaView& mv, int rows_mode, int dtype, int D, const void* x, const float* g, float eps,
+                   void* y, void* stream);
+int launch_swiglu(const MetaView& mv, int rows_mode, int dtype, int F, const void* gu, void* out, void* stream);
+int launch_gates(const MetaView& mv, int dtype, int H, const void* z, const float* bias, float* alpha, float* eta,
+                 void* stream);
+int launch_linear(const MetaView& mv, int rows_mode, int dtype, int N, int K, const void* a, int64_t lda,
+                  const void* w, const void* resid, void* c, int64_t ldc, void* stream);
 bool attn_uses_mfma(const flide_attn_params& p);
 int64_t attn_workspace_bytes(const flide_caps& c, const flide_attn_params& p);
 int launch_gdn(const MetaView& mv, const flide_gdn_params& p, int phase, const void* x, const float* conv_w,

@@ -22,6 +22,7 @@ FLIDE_OK, FLIDE_E_INVALID_ARG, FLIDE_E_CAPACITY, FLIDE_E_UNSUPPORTED, FLIDE_E_HI
     FLIDE_E_INTERNAL = range(7)
 FLIDE_F32, FLIDE_BF16 = 0, 1
 FLIDE_GDN_TRUNKS, FLIDE_GDN_QUESTIONS = 0, 1
+FLIDE_ROWS_ALL, FLIDE_ROWS_QFINAL = 0, 1
 
 
 class FlideError(RuntimeError):
@@ -123,6 +124,12 @@ _SIGNATURES = {
                                  _VP, _VP, _VP, _VP, _VP, C.c_int32, _VP, _VP]),
     "flide_readout": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.POINTER(flide_readout_params), _VP, _VP, _VP,
                                 _VP, C.c_int32, _VP, _VP]),
+    "flide_rmsnorm": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.c_int32, C.c_int32, C.c_int32, _VP, _VP,
+                                C.c_float, _VP, _VP]),
+    "flide_linear": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _VP,
+                               C.c_int64, _VP, _VP, _VP, C.c_int64, _VP]),
+    "flide_swiglu": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.c_int32, C.c_int32, C.c_int32, _VP, _VP, _VP]),
+    "flide_gdn_gates": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, C.c_int32, C.c_int32, _VP, _VP, _VP, _VP, _VP]),
     "flide_graph_capture": (C.c_int, [_VP, C.POINTER(flide_round_bufs), _VP, C.POINTER(C.c_int32)]),
     "flide_select_bucket": (C.c_int, [_VP, C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32)]),
     "flide_graph_replay": (C.c_int, [_VP, C.c_int32, C.POINTER(C.c_int32), _VP]),
@@ -435,6 +442,33 @@ def flide_readout(ctx: Context, caps: flide_caps, dev_meta, p: flide_readout_par
     _check(load_library().flide_readout(ctx.handle, C.byref(caps), _ptr(dev_meta), C.byref(p), _ptr(h), _ptr(w_opt),
                                         _ptr(opt_off), _ptr(opt_id), int(n_opt_rows), _ptr(probs), _stream(stream)),
            "flide_readout", ctx.handle)
+
+
+def flide_rmsnorm(ctx: Context, caps: flide_caps, dev_meta, rows: int, dtype: int, D: int, x, g, eps: float, y,
+                  stream=None) -> None:
+    _check(load_library().flide_rmsnorm(ctx.handle, C.byref(caps), _ptr(dev_meta), int(rows), int(dtype), int(D),
+                                        _ptr(x), _ptr(g), float(eps), _ptr(y), _stream(stream)), "flide_rmsnorm",
+           ctx.handle)
+
+
+def flide_linear(ctx: Context, caps: flide_caps, dev_meta, rows: int, dtype: int, N: int, K: int, a, lda: int, w,
+                 resid, c, ldc: int, stream=None) -> None:
+    _check(load_library().flide_linear(ctx.handle, C.byref(caps), _ptr(dev_meta), int(rows), int(dtype), int(N),
+                                       int(K), _ptr(a), int(lda), _ptr(w), _ptr(resid), _ptr(c), int(ldc),
+                                       _stream(stream)), "flide_linear", ctx.handle)
+
+
+def flide_swiglu(ctx: Context, caps: flide_caps, dev_meta, rows: int, dtype: int, F: int, gu, out,
+                 stream=None) -> None:
+    _check(load_library().flide_swiglu(ctx.handle, C.byref(caps), _ptr(dev_meta), int(rows), int(dtype), int(F),
+                                       _ptr(gu), _ptr(out), _stream(stream)), "flide_swiglu", ctx.handle)
+
+
+def flide_gdn_gates(ctx: Context, caps: flide_caps, dev_meta, dtype: int, H: int, z, bias, alpha, eta,
+                    stream=None) -> None:
+    _check(load_library().flide_gdn_gates(ctx.handle, C.byref(caps), _ptr(dev_meta), int(dtype), int(H), _ptr(z),
+                                          _ptr(bias), _ptr(alpha), _ptr(eta), _stream(stream)), "flide_gdn_gates",
+           ctx.handle)
 
 
 def flide_graph_capture(ctx: Context, bufs: flide_round_bufs, stream=None) -> int:

@@ -364,3 +364,161 @@ class SplitExecutor:
 
     def table_of(self, k: int) -> BucketTable:
         return self.tables[k % len(self.tables)]
+
+
+class StackRunner:
+    """Device buffers and launch sequence of a multi-layer hybrid stack at one capacity — marshalling only.
+
+    Per layer (pre-norm residual block): rmsnorm -> the token mixer (GDN: input projection, gate projection
+    and gates, the two GDN calls, output projection with the residual add; attention: q, k, v projections,
+    the tree-masked attention, output projection with the residual add) -> rmsnorm -> SwiGLU MLP with the
+    residual add.  After the last token mixer the row-wise layers run on question-final rows only
+    (selective readout), then the final norm and the readout.  Every step is a call of the C ABI; the
+    whole sequence can be captured into one HIP graph (``capture``) and replayed after each round's
+    metadata upload."""
+
+    def __init__(self, stack, T_cap: int, R_cap: int, Q_cap: int, opt_cap: int, device: str = "cuda"):
+        s = stack.shapes
+        self.stack, self.s = stack, s
+        self.dtype = stack.dtype
+        fd = _flide_dtype(stack.dtype)
+        self.fd = fd
+        dt = _torch_dtype(stack.dtype)
+        self.device = device
+        self.caps = F.caps_of(T_cap, R_cap, Q_cap)
+        self.layout = F.flide_meta_layout_for(self.caps)
+        T = T_cap
+        z = lambda *shape, dtype=dt: torch.zeros(*shape, dtype=dtype, device=device)  # noqa: E731
+        self.dev_meta = z(self.layout.dev_words, dtype=torch.int32)
+        self.n_slots = max(r.out_slot for r in stack.requests) + 1
+        kinds = set(s.layers)
+        self.x, self.h, self.hf = z(T, s.Dm), z(T, s.Dm), z(T, s.Dm)
+        self.gu, self.mid = z(T, 2 * s.F), z(T, s.F)
+        if "gdn" in kinds:
+            C = s.gdn_channels
+            self.xg, self.zab = z(T, C), z(T, 2 * s.H)
+            self.alpha, self.eta = z(T, s.H, dtype=torch.float32), z(T, s.H, dtype=torch.float32)
+            self.o_gdn = z(T, s.H, s.dv)
+            self.gdn_params = F.flide_gdn_params(s.H, s.dk, s.dv, s.conv_k, 0, 64, fd, 0)
+        if kinds & {"attn", "swa"}:
+            self.q, self.k, self.v = z(T, s.Hq, s.d), z(T, s.Hkv, s.d), z(T, s.Hkv, s.d)
+            self.o_attn = z(T, s.Hq, s.d)
+        max_pos = max([r.P + (max(r.q_len) if r.q_len else 0) for r in stack.requests] + [1])
+        w = stack.weights()
+        self.layers = []
+        for L in w["layers"]:
+            D = {"kind": L["kind"]}
+            for name, val in L.items():
+                if name == "kind":
+                    continue
+                t = torch.from_numpy(np.ascontiguousarray(val))
+                keep_f32 = name in ("norm1", "norm2", "b_ab", "conv_w")
+                D[name] = t.to(device=device, dtype=torch.float32 if keep_f32 else dt)
+            if L["kind"] == "gdn":
+                D["state_pool"] = z(self.n_slots, s.H, s.dv, s.dk, dtype=torch.float32)
+                D["conv_pool"] = z(self.n_slots, max(1, s.conv_k - 1), s.gdn_channels)
+            else:
+                p = F.flide_attn_params(s.Hq, s.Hkv, s.d, s.window if L["kind"] == "swa" else 0, float(s.theta),
+                                        int(max_pos), 0, 0, fd, 0)
+                D["params"] = p
+                D["ws"] = torch.zeros(F.flide_attn_workspace_bytes(self.caps, p), dtype=torch.uint8, device=device)
+            self.layers.append(D)
+        self.norm_f = torch.from_numpy(w["norm_f"]).to(device)
+        self.ro_params = F.flide_readout_params(s.Dm, fd)
+        self.w_opt = z(max(1, opt_cap), s.Dm)
+        self.opt_off = z(Q_cap + 1, dtype=torch.int32)
+        self.opt_id = z(max(1, opt_cap), dtype=torch.int32)
+        self.probs = z(max(1, opt_cap), dtype=torch.float32)
+        self.opt_cap = max(1, opt_cap)
+        self.graph = None
+
+    def fill(self, placement) -> None:
+        """Input embeddings at the stream rows named by ``placement`` and the round's option rows (CSR over
+        questions in stream order)."""
+        st = self.stack
+        self.x.zero_()
+        host = np.zeros((self.caps.T_cap, self.s.Dm), np.float32)
+        w_rows, off = [], [0]
+        for j, r in enumerate(st.requests):
+            pl = st.payload(j)
+            segs = st.segment_rows(j)
+            r0 = int(placement["req_trunk_row0"][j])
+            host[r0:r0 + segs[0][1]] = pl["x0"][:segs[0][1]]
+            q0 = int(placement["req_q_seg0"][j])
+            for i, (a, L) in enumerate(segs[1:]):
+                rr = int(placement["seg_row0"][q0 + i])
+                host[rr:rr + L] = pl["x0"][a:a + L]
+            w_rows.append(pl["w_opt"])
+            for n in r.n_opt:
+                off.append(off[-1] + int(n))
+        self.x.copy_(torch.from_numpy(host).to(self.x.dtype))
+        n_opt = off[-1]
+        if n_opt > self.opt_cap:
+            raise ValueError("too many options for the buffers")
+        if n_opt:
+            self.w_opt[:n_opt].copy_(torch.from_numpy(np.concatenate(w_rows, axis=0)).to(self.w_opt.dtype))
+            self.opt_id[:n_opt].copy_(torch.arange(n_opt, dtype=torch.int32))
+        self.opt_off[:len(off)].copy_(torch.from_numpy(np.asarray(off, np.int32)))
+
+    def upload(self, ctx: F.Context, image: np.ndarray, stream=None) -> None:
+        F.flide_meta_upload(ctx, self.caps, image, self.dev_meta, stream)
+
+    def run(self, ctx: F.Context, stream=None, selective: bool = True, layer_hook=None) -> None:
+        """The whole stack over the uploaded round.  selective=False runs the last layer's MLP on every row
+        (for comparing every row of the final layer).  layer_hook(i) is called after layer i is enqueued."""
+        s, c, m, fd = self.s, self.caps, self.dev_meta, self.fd
+        ALL, QF = F.FLIDE_ROWS_ALL, F.FLIDE_ROWS_QFINAL
+        nl = len(self.layers)
+        for li, L in enumerate(self.layers):
+            F.flide_rmsnorm(ctx, c, m, ALL, fd, s.Dm, self.x, L["norm1"], 1e-6, self.h, stream)
+            if L["kind"] == "gdn":
+                C = s.gdn_channels
+                F.flide_linear(ctx, c, m, ALL, fd, C, s.Dm, self.h, s.Dm, L["w_x"], None, self.xg, C, stream)
+                F.flide_linear(ctx, c, m, ALL, fd, 2 * s.H, s.Dm, self.h, s.Dm, L["w_ab"], None, self.zab, 2 * s.H,
+                               stream)
+                F.flide_gdn_gates(ctx, c, m, fd, s.H, self.zab, L["b_ab"], self.alpha, self.eta, stream)
+                for phase in (F.FLIDE_GDN_TRUNKS, F.FLIDE_GDN_QUESTIONS):
+                    F.flide_fork_gdn(ctx, c, m, self.gdn_params, phase, self.xg, L["conv_w"], self.alpha, self.eta,
+                                     L["state_pool"], L["conv_pool"], self.n_slots, self.o_gdn, stream)
+                F.flide_linear(ctx, c, m, ALL, fd, s.Dm, s.H * s.dv, self.o_gdn, s.H * s.dv, L["w_o"], self.x, self.x,
+                               s.Dm, stream)
+            else:
+                F.flide_linear(ctx, c, m, ALL, fd, s.Hq * s.d, s.Dm, self.h, s.Dm, L["w_q"], None, self.q,
+                               s.Hq * s.d, stream)
+                F.flide_linear(ctx, c, m, ALL, fd, s.Hkv * s.d, s.Dm, self.h, s.Dm, L["w_k"], None, self.k,
+                               s.Hkv * s.d, stream)
+                F.flide_linear(ctx, c, m, ALL, fd, s.Hkv * s.d, s.Dm, self.h, s.Dm, L["w_v"], None, self.v,
+                               s.Hkv * s.d, stream)
+                F.flide_fork_attn(ctx, c, m, L["params"], self.q, self.k, self.v, None, None, self.o_attn, L["ws"],
+                                  stream)
+                F.flide_linear(ctx, c, m, ALL, fd, s.Dm, s.Hq * s.d, self.o_attn, s.Hq * s.d, L["w_o"], self.x,
+                               self.x, s.Dm, stream)
+            rows = QF if (selective and li == nl - 1) else ALL
+            F.flide_rmsnorm(ctx, c, m, rows, fd, s.Dm, self.x, L["norm2"], 1e-6, self.h, stream)
+            F.flide_linear(ctx, c, m, rows, fd, 2 * s.F, s.Dm, self.h, s.Dm, L["gate_up"], None, self.gu, 2 * s.F,
+                           stream)
+            F.flide_swiglu(ctx, c, m, rows, fd, s.F, self.gu, self.mid, stream)
+            F.flide_linear(ctx, c, m, rows, fd, s.Dm, s.F, self.mid, s.F, L["down"], self.x, self.x, s.Dm, stream)
+            if layer_hook is not None:
+                layer_hook(li)
+        F.flide_rmsnorm(ctx, c, m, QF, fd, s.Dm, self.x, self.norm_f, 1e-6, self.hf, stream)
+        F.flide_readout(ctx, c, m, self.ro_params, self.hf, self.w_opt, self.opt_off, self.opt_id, self.opt_cap,
+                        self.probs, stream)
+
+    def capture(self, ctx: F.Context) -> None:
+        """Capture ``run`` into one HIP graph (after an eager run, which builds the rotary tables)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run(ctx, side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run(ctx, torch.cuda.current_stream())
+        self.graph = g
+
+    def replay(self, ctx: F.Context, image: np.ndarray) -> None:
+        """Upload the round's metadata on the current stream, then replay the captured stack."""
+        self.upload(ctx, image, torch.cuda.current_stream())
+        self.graph.replay()
