@@ -106,6 +106,20 @@ def test_fan_out_whole_round_three_replays(ctx):
         _close(tables)
 
 
+@pytest.mark.parametrize("config,requests", [(1, range(5)), (2, range(2))])
+def test_repeated_runs_are_bitwise_identical(ctx, config, requests):
+    """The same round run five times (eager, direct and graph replays interleaved) gives the same bits
+    every time: no kernel of the path depends on timing."""
+    rnd = make_round(config, 0, requests=requests)
+    runs = []
+    for mode in ("eager", "direct", "graph", "eager", "direct"):
+        bufs, _ = harness.run_gpu(rnd, ctx, mode)
+        runs.append(harness.outputs(bufs))
+    for i, got in enumerate(runs[1:], 1):
+        for k in runs[0]:
+            np.testing.assert_array_equal(got[k], runs[0][k], err_msg=f"run {i}: {k}")
+
+
 def test_split_equals_unsplit_bitwise(ctx):
     """Twelve short-round requests run once in one 8,192-row bucket and once split at request boundaries
     for a 2,048-row capacity (four or more replays in smaller buckets): every request's attention and GDN

@@ -407,9 +407,8 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
     load_desc();
   }
   if (tile >= n_tiles_round) return;
-  const int kvh = yy / HG, hl = (yy % HG) * 4 + w;
-  const bool active = hl < G;
-  const int h = kvh * G + hl;
+  const int kvh = yy / HG, hg0 = (yy % HG) * 4;  // kv head; first q head of the group in this workgroup
+  const int ng = min(4, G - hg0);                  // q heads of this workgroup (1 .. 4)
   const int seg = td[TD_SEG];
   if (seg < 0) return;  // unused position (an inconsistent segment was flagged by meta_expand)
   const bool question = td[TD_QUESTION] != 0;
@@ -426,6 +425,12 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
     if (tid == 0) flag_error(mv.dev_error, E_POSITION);
     return;
   }
+  // Query columns: the tile's 32 rows x ng heads in row-major order, wave w taking columns 32 w .. 32 w + 31
+  // (column k is row k / ng of head hg0 + k % ng).  All heads of a row see the same keys, and each column's
+  // arithmetic involves that column only, so the assignment of columns to waves and lanes changes no bit;
+  // with four heads a wave holds 8 rows, and a wave whose rows all lie past the tile's last row (short
+  // question tiles) skips the key loop's arithmetic.
+  const bool active = w < ng && (32 * w) / ng < nrows;
   const int64_t VT = vt_cols(mv.T_cap, mv.seg_cap);
   const int lo_w = window > 0 ? qpos_min - window + 1 : INT_MIN;
 
@@ -441,21 +446,40 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   const int n1 = lo1 < hi1 ? (hi1 - ts01 + BN - 1) / BN : 0;
   const int n2 = lo2 < hi2 ? (hi2 - ts02 + BN - 1) / BN : 0;
   const int n_tiles = n0 + n1 + n2;
-  struct TileInfo {
-    int src, ts, lo, hi;
-    int64_t roff, voff;
+  // A cursor walks the key tiles in order: range rg (0, 1, 2 as above), tile start ts (a position) and the
+  // byte addresses of the tile's first key row (kp) and first value column (vp), advanced by one tile's
+  // stride; the range's parameters are looked up only when the cursor enters it.  Every field is uniform
+  // across the workgroup.
+  struct Cursor {
+    int rg, ts, lo, hi, vstride;
+    const unsigned char* kp;
+    const unsigned char* vp;
   };
-  // range and key interval of flat tile index t (all values are uniform across the workgroup)
-  auto tile_info = [&](int t) {
-    TileInfo ti;
-    if (t < n0) {
-      ti = TileInfo{0, ts00 + t * BN, lo0, hi0, roff0, 0};
-    } else if (t < n0 + n1) {
-      ti = TileInfo{1, ts01 + (t - n0) * BN, lo1, hi1, roff1, voff1};
+  auto range_start = [&](int rg) {
+    Cursor c;
+    c.rg = rg;
+    int64_t roff, voff;
+    const bf16_t *kbase, *vbase;
+    if (rg == 0) {
+      c.ts = ts00, c.lo = lo0, c.hi = hi0, roff = roff0, voff = 0, c.vstride = cache_rows;
+      kbase = k_cache + int64_t(kvh) * D;
+      vbase = v_cache + (int64_t(ckpt) * Hkv + kvh) * D * cache_rows;
     } else {
-      ti = TileInfo{2, ts02 + (t - n0 - n1) * BN, lo2, hi2, roff2, voff2};
+      c.ts = rg == 1 ? ts01 : ts02, c.lo = rg == 1 ? lo1 : lo2, c.hi = rg == 1 ? hi1 : hi2;
+      roff = rg == 1 ? roff1 : roff2, voff = rg == 1 ? voff1 : voff2, c.vstride = int(VT);
+      kbase = k_rot + int64_t(kvh) * D;
+      vbase = vt + int64_t(kvh) * D * VT;
     }
-    return ti;
+    c.kp = reinterpret_cast<const unsigned char*>(kbase + (int64_t(c.ts) + roff) * Hkv * D);
+    c.vp = reinterpret_cast<const unsigned char*>(vbase + (int64_t(c.ts) + voff));
+    return c;
+  };
+  // the next tile (called only while one is left: the ranges hold n_tiles tiles in all)
+  auto advance = [&](Cursor& c) {
+    c.ts += BN;
+    c.kp += int64_t(BN) * Hkv * D * 2;
+    c.vp += BN * 2;
+    if (__builtin_expect(c.ts >= c.hi, 0)) c = range_start(c.rg == 0 && n1 > 0 ? 1 : 2);
   };
   // Lane constants of the copies: wave w issues copy instructions I = w*IPW + ii; lane l of
   // instruction I fills 16-byte LDS slot 64 I + l.  Key slot -> row k_row = I * 64 / KCH + l / KCH and
@@ -471,40 +495,40 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
     k_off0[ii] = (krow * Hkv * D + (((slot % KCH) ^ ksw(krow)) * 8)) * 2;  // bytes from the tile's first key row
   }
   const int vc = (l & 3) ^ ((l >> 4) & 3);
-  auto issue = [&](int t, int buf) {
-    const TileInfo ti = tile_info(t);
-    const int ts = ti.ts, lo = ti.lo, hi = ti.hi;
+  auto issue = [&](const Cursor& c, int buf) {
+    const int ts = c.ts, lo = c.lo, hi = c.hi, vstride = c.vstride;
     const bool edge = ts < lo || ts + BN > hi;
-    const bf16_t* kbase = (ti.src == 0 ? k_cache : k_rot) + int64_t(kvh) * D;
-    const bf16_t* vbase =
-        ti.src == 0 ? v_cache + (int64_t(ckpt) * Hkv + kvh) * D * cache_rows : vt + int64_t(kvh) * D * VT;
-    const int vstride = ti.src == 0 ? cache_rows : int(VT);
     unsigned char* kl = lds + buf * TILE_BYTES;
     unsigned char* vl = lds + (2 + buf) * TILE_BYTES;
-    const unsigned char* ktile = reinterpret_cast<const unsigned char*>(kbase + (int64_t(ts) + ti.roff) * Hkv * D);
-    const unsigned char* vtile = reinterpret_cast<const unsigned char*>(vbase + (int64_t(ts) + ti.voff));
     int lv = l;
     asm volatile("" : "+v"(lv));  // recomputed per tile: registers are scarce in the key-tile loop
     const int voff0 = (((w * IPW * 16) + (lv >> 2)) * vstride + 8 * vc) * 2;
+    // both offsets are >= 0 (clamped rows and chunks stay inside the range): 32-bit unsigned offsets
+    // from a scalar base
+    if (!edge) {  // interior tile: fixed lane offsets
 #pragma unroll
-    for (int ii = 0; ii < IPW; ++ii) {
+      for (int ii = 0; ii < IPW; ++ii) {
+        async_copy16(c.kp + uint32_t(k_off0[ii % KP] + (ii / KP) * 4 * Hkv * D * 2), kl + (w * IPW + ii) * 1024);
+        async_copy16(c.vp + uint32_t(voff0 + ii * 16 * vstride * 2), vl + (w * IPW + ii) * 1024);
+      }
+      return;
+    }
+#pragma unroll
+    for (int ii = 0; ii < IPW; ++ii) {  // masked keys read a valid row / value chunk of the range
       int koff = k_off0[ii % KP] + (ii / KP) * 4 * Hkv * D * 2;
       int voff = voff0 + ii * 16 * vstride * 2;
-      if (edge) {  // masked keys read a valid row / value chunk of the range
-        const int p = ts + ((w * IPW + ii) * 64 + lv) / KCH;
-        const int pc = p < lo ? lo : (p >= hi ? hi - 1 : p);
-        koff += (pc - p) * Hkv * D * 2;
-        const int p0 = ts + 8 * vc;
-        const int lo8 = lo & ~7, hi8 = (hi - 1) & ~7;
-        const int p0c = p0 < lo8 ? lo8 : (p0 > hi8 ? hi8 : p0);
-        voff += (p0c - p0) * 2;
-      }
-      // both offsets are >= 0 (clamped rows and chunks stay inside the range): 32-bit unsigned offsets
-      // from a scalar base
-      async_copy16(ktile + uint32_t(koff), kl + (w * IPW + ii) * 1024);
-      async_copy16(vtile + uint32_t(voff), vl + (w * IPW + ii) * 1024);
+      const int p = ts + ((w * IPW + ii) * 64 + lv) / KCH;
+      const int pc = p < lo ? lo : (p >= hi ? hi - 1 : p);
+      koff += (pc - p) * Hkv * D * 2;
+      const int p0 = ts + 8 * vc;
+      const int lo8 = lo & ~7, hi8 = (hi - 1) & ~7;
+      const int p0c = p0 < lo8 ? lo8 : (p0 > hi8 ? hi8 : p0);
+      voff += (p0c - p0) * 2;
+      async_copy16(c.kp + uint32_t(koff), kl + (w * IPW + ii) * 1024);
+      async_copy16(c.vp + uint32_t(voff), vl + (w * IPW + ii) * 1024);
     }
   };
+  Cursor cur = range_start(n0 > 0 ? 0 : (n1 > 0 ? 1 : 2));  // the first tile (unused when there is none)
 
   // ---- rotated, pre-scaled queries as MFMA B fragments (query = column) ----
   // The rotation table rows of the tile's 32 positions are the same for every head: they are copied
@@ -528,28 +552,31 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   }
   const float sl2 = 1.4426950408889634f * rsqrtf(float(D));
   u32x4v qf[2][NC];
-  int qpos[2];
+  int qpos[2], qrow[2];  // position and tile row of this lane's query column in block qb
   {
     u32x4v qa[2][NC / 2], qb_[2][NC / 2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int r = qb * 16 + r16;
+      const int col = 32 * w + qb * 16 + r16;
+      const int r = col / ng, hc = kvh * G + hg0 + col % ng;
       const int rr = (active && r < nrows) ? r : 0;
+      qrow[qb] = rr;
       qpos[qb] = qpos_min + r;
-      const int64_t rowbase = (int64_t(x0 + rr) * Hq + h) * D + 8 * g4;
+      const int64_t rowbase = (int64_t(x0 + rr) * Hq + hc) * D + 8 * g4;
 #pragma unroll
       for (int c = 0; c < NC / 2; ++c) {
         qa[qb][c] = *reinterpret_cast<const u32x4v*>(q + rowbase + 32 * c);
         qb_[qb][c] = *reinterpret_cast<const u32x4v*>(q + rowbase + 32 * c + D / 2);
       }
     }
-    if (n_tiles > 0) issue(0, 0);
+    if (n_tiles > 0) issue(cur, 0);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's table rows (and everything else) have landed
     __syncthreads();                // ... and every wave's
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const bool qv = active && qb * 16 + r16 < nrows;
-      const unsigned char* trow = lds + (qb == 0 ? TILE_BYTES : 3 * TILE_BYTES) + r16 * RB;
+      const int rt = qrow[qb];  // table row (0 for columns past the tile)
+      const bool qv = active && (32 * w + qb * 16 + r16) / ng < nrows;
+      const unsigned char* trow = lds + (rt < 16 ? TILE_BYTES : 3 * TILE_BYTES) + (rt & 15) * RB;
 #pragma unroll
       for (int c = 0; c < NC / 2; ++c) {
         u32x4v lo, hi;
@@ -559,7 +586,7 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
           const float a0 = __uint_as_float(av << 16), a1 = __uint_as_float(av & 0xFFFF0000u);
           const float b0 = __uint_as_float(bv << 16), b1 = __uint_as_float(bv & 0xFFFF0000u);
           // (cos, sin) of pairs 8 g4 + 32 c + 2 ww and the next one: chunk 4 g4 + 16 c + ww of the row
-          const float4 t4 = *reinterpret_cast<const float4*>(trow + (((4 * g4 + 16 * c + ww) ^ r16) << 4));
+          const float4 t4 = *reinterpret_cast<const float4*>(trow + (((4 * g4 + 16 * c + ww) ^ (rt & 15)) << 4));
           lo[ww] = pack_bf16x2((a0 * t4.x - b0 * t4.y) * sl2, (a1 * t4.z - b1 * t4.w) * sl2);
           hi[ww] = pack_bf16x2((b0 * t4.x + a0 * t4.y) * sl2, (b1 * t4.z + a1 * t4.w) * sl2);
         }
@@ -595,10 +622,12 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
     constexpr int BUF = decltype(bufc)::value;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile t have landed
     __syncthreads();                // ... and every wave's; buffer BUF ^ 1 is free
-    if (t + 1 < n_tiles) issue(t + 1, BUF ^ 1);
-    if (!active) return;
-    const TileInfo cur = tile_info(t);
     const int ts = cur.ts, lo = cur.lo, hi = cur.hi;
+    if (t + 1 < n_tiles) {
+      advance(cur);
+      issue(cur, BUF ^ 1);
+    }
+    if (!active) return;
     // lane addresses of the operand reads (the array is 1024-byte aligned, so the chunk XOR of bits
     // 6-7 commutes with adding its base); tile, buffer and block offsets are instruction immediates
     int kf = kfrag0;
@@ -693,9 +722,9 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   }
   if (t < n_tiles) step(t, std::integral_constant<int, 0>{});
 
-  // Output: each wave stages its 32 x D tile row-major in its quarter of the LDS (16-byte chunk c of
-  // row r at slot c ^ (r % 16): conflict-free for both the 8-byte fragment writes and the 16-byte row
-  // reads), then stores whole rows, 16 bytes per lane.  The accumulator layout would otherwise give
+  // Output: each wave stages its 32 columns x D row-major in its quarter of the LDS (16-byte chunk c of
+  // column k at slot c ^ (k % 16): conflict-free for both the 8-byte fragment writes and the 16-byte
+  // reads), then stores whole head rows, 16 bytes per lane.  The accumulator layout would otherwise give
   // 8-byte pieces of sixteen rows per store.
   __syncthreads();  // every wave is done with the key and value tiles
   if (!active) return;
@@ -703,9 +732,9 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   unsigned char* ow = lds + w * TILE_BYTES;  // BN == 32 rows of D: one wave's output tile
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int row = qb * 16 + r16;
+    const int row = qb * 16 + r16;  // staging row: the column's index in the wave
     const float l_col = rows4_sum(l_run[qb]);
-    const float inv = row < nrows ? 1.f / l_col : 0.f;
+    const float inv = (32 * w + row) / ng < nrows ? 1.f / l_col : 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const f32x4v a = acc[qb][db];
@@ -718,9 +747,10 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   const int c16 = l % CPR;
 #pragma unroll
   for (int k = 0; k < BN / RPI; ++k) {
-    const int row = k * RPI + l / CPR;
+    const int row = k * RPI + l / CPR;  // staging row = column 32 w + row
     const u32x4v v = *reinterpret_cast<const u32x4v*>(ow + row * (D * 2) + ((c16 ^ (row & 15)) << 4));
-    if (row < nrows) *reinterpret_cast<u32x4v*>(o + (int64_t(x0 + row) * Hq + h) * D + c16 * 8) = v;
+    const int col = 32 * w + row, qr = col / ng, hc = kvh * G + hg0 + col % ng;
+    if (qr < nrows) *reinterpret_cast<u32x4v*>(o + (int64_t(x0 + qr) * Hq + hc) * D + c16 * 8) = v;
   }
 }
 
