@@ -649,6 +649,9 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
     constexpr int KD = 3;  // operand reads in flight
     u32x4v fa[KD];
     static_for<0, KD>([&](auto J) { fa[decltype(J)::value] = kread(J); });
+    // A wave in its score products issues ahead of the other wave of its SIMD, which is then mostly in
+    // its softmax: the two overlap MFMA and VALU work better (2-3% on long-context rounds, measured).
+    __builtin_amdgcn_s_setprio(1);
     static_for<0, 2 * NC>([&](auto J) {
       constexpr int j = decltype(J)::value, kb = j / NC, c = j % NC;
       lds_wait<(KD - 1 < 2 * NC - 1 - j ? KD - 1 : 2 * NC - 1 - j)>(fa[j % KD]);
@@ -656,6 +659,7 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
       s[kb][1] = mfma16x16x32(fa[j % KD], qf[1][c], s[kb][1]);
       if constexpr (j + KD < 2 * NC) fa[j % KD] = kread(std::integral_constant<int, j + KD>{});
     });
+    __builtin_amdgcn_s_setprio(0);
     u32x4v fv[KD];
     static_for<0, KD>([&](auto J) { fv[decltype(J)::value] = vread(J); });
 
