@@ -303,6 +303,9 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="counter pass: one launch of every kernel per sub-round plus a 256 MiB device copy (for "
                          "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE and the copy-kernel scale factor); prints no JSON")
+    ap.add_argument("--nondeterministic", action="store_true",
+                    help="GDN chunk boundaries on the stream's 64-row grid (bits then depend on the round's "
+                         "composition); the default is the composition-independent mode")
     ap.add_argument("--stack", action="store_true",
                     help="time the multi-layer hybrid stack instead of the ForkAttention round (its own JSON line)")
     args = ap.parse_args()
@@ -335,6 +338,7 @@ def main():
     opt_cap = max(sum(sum(r.n_opt) for r in s.requests) for s in subs)
     caps_table = bucket_capacities(rnd.t_max, R_cap, Q_cap)
     spec = spec_for_round(rnd, T_cap=rnd.t_max, R_cap=R_cap, Q_cap=Q_cap, opt_cap=opt_cap)
+    spec.deterministic = not args.nondeterministic
     print(f"[bench] {spec_cfg.name}: {T} rows, {len(subs)} sub-round(s), table of {len(caps_table)} buckets "
           f"(R_cap {R_cap}, Q_cap {Q_cap})", flush=True)
     tables = []
@@ -501,7 +505,8 @@ def main():
         "config": {"workload": f"{spec_cfg.name}: {spec_cfg.description}; {sub_note}",
                    "stream_rows": T, "requests": len(rnd.requests),
                    "questions": sum(len(r.q_len) for r in rnd.requests),
-                   "bucket_table_T_caps": [c.T_cap for c in caps_table], "seed": args.seed},
+                   "bucket_table_T_caps": [c.T_cap for c in caps_table], "seed": args.seed,
+                   "deterministic": spec.deterministic},
         "round_latency_ms": {"p10": round(lat_ms[len(lat_ms) // 10], 4), "median": round(lat_ms[len(lat_ms) // 2], 4),
                              "p90": round(lat_ms[(9 * len(lat_ms)) // 10], 4)},
         "per_layer_tokens_per_s": {

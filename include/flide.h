@@ -277,9 +277,10 @@ flide_status flide_meta_upload(flide_ctx* ctx, const flide_caps* caps, const int
  *  theta        rotary base
  *  max_pos      exclusive bound on every position of the rounds run (rotary table size)
  *  cache_rows, cache_slots  shape of the K/V cache (0 if no request resumes)
- *  deterministic 1 = per-question tiles and a fixed key order (the kernels
- *               already use a composition-independent order; the flag is
- *               accepted for interface stability)                              */
+ *  deterministic accepted for symmetry with flide_gdn_params: attention always
+ *               runs per-segment query tiles over position-aligned key tiles,
+ *               so its bits never depend on the round's composition (no
+ *               cheaper composition-dependent tiling exists here)             */
 typedef struct {
   int32_t Hq, Hkv, d, window;
   double theta;
@@ -349,7 +350,13 @@ flide_status flide_fork_attn_noalloc(flide_ctx* ctx, const flide_caps* caps, con
  *  conv_pool  [n_slots, conv_k-1, H*(2dk+dv)] in the dtype of x
  *  o          [T_cap, H, dv] in the dtype of x (tail rows untouched)
  * Errors: FLIDE_E_INVALID_ARG, FLIDE_E_UNSUPPORTED, FLIDE_E_HIP.  A slot index
- * outside [0, n_slots) found on the device sets the device error word.      */
+ * outside [0, n_slots) found on the device sets the device error word.
+ * deterministic (the optional mode of [KO] §어떻게 쓰나, default on in the Python
+ * binding): 1 = chunks of 64 rows from each segment's first row, so a request's
+ * output bits do not depend on the rest of the round; 0 = chunk boundaries at
+ * the multiples of 64 stream rows (and at an interior checkpoint), the grid of
+ * a packed batch, under which a segment's bits depend on where it lands.  The
+ * per-token kernel (f32, other head sizes) has no chunks and ignores it.     */
 typedef enum { FLIDE_GDN_TRUNKS = 0, FLIDE_GDN_QUESTIONS = 1 } flide_gdn_phase;
 typedef struct {
   int32_t H, dk, dv, conv_k;

@@ -120,6 +120,28 @@ def test_repeated_runs_are_bitwise_identical(ctx, config, requests):
             np.testing.assert_array_equal(got[k], runs[0][k], err_msg=f"run {i}: {k}")
 
 
+def test_chunk_grid_mode_depends_on_stream_position(ctx):
+    """GDN with deterministic = 0 cuts chunks on the stream's 64-row grid: outputs still match the oracle,
+    but a request's bits change when other requests move it along the stream; with deterministic = 1
+    (chunks from each segment's first row) they do not."""
+    from tree_forked_hybrid_amd.runner import spec_for_round
+    full = make_round(1, 0, requests=range(4))
+    one = full.subset([3])
+    got = {}
+    for det in (False, True):
+        b1, l1 = harness.run_gpu(one, ctx, "direct", spec=dataclasses.replace(spec_for_round(one), deterministic=det))
+        g1 = harness.outputs(b1)
+        b4, l4 = harness.run_gpu(full, ctx, "direct", spec=dataclasses.replace(spec_for_round(full),
+                                                                              deterministic=det))
+        g4 = harness.outputs(b4)
+        if not det:
+            harness.check_round(full, g4, l4, mode="memo")
+            assert int(l4["req_trunk_row0"][3]) % 64 != 0  # the request lands off the grid in the round
+        rows1, rows4 = harness.stream_rows(one, l1, 0), harness.stream_rows(full, l4, 3)
+        got[det] = np.array_equal(g1["gdn_o"][rows1], g4["gdn_o"][rows4])
+    assert got[True] and not got[False], got
+
+
 def test_split_equals_unsplit_bitwise(ctx):
     """Twelve short-round requests run once in one 8,192-row bucket and once split at request boundaries
     for a 2,048-row capacity (four or more replays in smaller buckets): every request's attention and GDN

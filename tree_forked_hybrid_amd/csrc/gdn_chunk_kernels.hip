@@ -296,7 +296,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
                                                        const float* __restrict__ alpha,
                                                        const float* __restrict__ eta, float* __restrict__ state_pool,
                                                        bf16_t* __restrict__ conv_pool, int n_slots,
-                                                       bf16_t* __restrict__ o) {
+                                                       bf16_t* __restrict__ o, int det) {
   __shared__ ChunkLds L;
   __shared__ ChunkIn I;
   // workgroups are dispatched in linear order: rank = position in the longest-first work list
@@ -391,8 +391,15 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
   _Float16* const am = L.kl;           // -A [t][s] (strictly lower blocks), after the Gram products
   _Float16* const pm = L.kl + CK * CK;  // P [t][s] (lower blocks)
 
-  for (int c0 = 0; c0 < len; c0 += CK) {
-    const int n = min(CK, len - c0);
+  // Chunk boundaries: every 64 rows from the segment's first row (det != 0: the arithmetic of a segment
+  // depends on the segment alone), or at the multiples of 64 stream rows and at an interior checkpoint
+  // (det == 0: the grid of a packed batch, under which a segment's bits depend on where it lands).
+  for (int c0 = 0, n = 0; c0 < len; c0 += n) {
+    n = min(CK, len - c0);
+    if (!det) {
+      n = min(n, CK - ((row0 + c0) & (CK - 1)));
+      if (save_rows > c0) n = min(n, save_rows - c0);
+    }
     // Lane indices recomputed per chunk from an opaque copy: the per-lane LDS addresses derived from
     // them below are cheap to rebuild, and keeping them out of the loop preheader keeps them out of
     // registers across the whole segment.
@@ -508,7 +515,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
       }
     }
     lds_barrier();
-    if (c0 + CK < len) issue_chunk_loads(I, xs, as, es, len, c0 + CK, w, l, rowb, head_b, sect_b, H * 4);
+    if (c0 + n < len) issue_chunk_loads(I, xs, as, es, len, c0 + n, w, l, rowb, head_b, sect_b, H * 4);
     // ---- Gram blocks, held in registers until every wave is done with the lo tiles.  Waves 4-7 take
     // two P blocks and one strictly lower A block each; waves 0-3 one remaining block and, one each,
     // the diagonal A blocks and their inverses: the substitution chain runs on the older wave of each
@@ -568,7 +575,7 @@ __global__ void __launch_bounds__(NT) gdn_chunk_kernel(MetaView mv, int H, int K
     }
     // The state after a question's last chunk is not kept (only trunks emit a state), so the question
     // call skips the state update there.
-    const bool keep_state = PHASE == 0 || c0 + CK < len;
+    const bool keep_state = PHASE == 0 || c0 + n < len;
     lds_barrier();
     // ---- blocked forward substitution U = (I + A)^{-1} RHS ----
     h4v uh[4];
@@ -677,7 +684,8 @@ int launch_gdn(const MetaView& mv, const flide_gdn_params& p, int phase, const v
   auto kern = phase == 0 ? (p.act == 1 ? gdn_chunk_kernel<0, 1> : gdn_chunk_kernel<0, 0>)
                         : (p.act == 1 ? gdn_chunk_kernel<1, 1> : gdn_chunk_kernel<1, 0>);
   hipLaunchKernelGGL(kern, grid, dim3(NT), 0, (hipStream_t)stream, mv, p.H, p.conv_k,
-                     (const bf16_t*)x, conv_w, alpha, eta, state_pool, (bf16_t*)conv_pool, n_slots, (bf16_t*)o);
+                     (const bf16_t*)x, conv_w, alpha, eta, state_pool, (bf16_t*)conv_pool, n_slots, (bf16_t*)o,
+                     p.deterministic != 0 ? 1 : 0);
   return int(hipGetLastError());
 }
 

@@ -40,6 +40,8 @@ class RoundSpec:
     opt_cap: int            # rows of w_opt / entries of probs
     cache_rows: int = 0     # K/V cache rows per slot (0: no cache)
     max_pos: int = 1 << 16
+    # composition-independent bits (the default); False puts GDN chunk boundaries on the stream's 64-row grid
+    deterministic: bool = True
 
 
 class RoundBuffers:
@@ -63,7 +65,8 @@ class RoundBuffers:
         for layer in range(self.n_attn):
             p = F.flide_attn_params(s.Hq, s.Hkv, s.d, 0 if layer == 0 else s.swa_window, float(s.theta),
                                     int(spec.max_pos), int(spec.cache_rows),
-                                    int(spec.n_slots if spec.cache_rows > 0 else 0), _flide_dtype(spec.dtype), 0)
+                                    int(spec.n_slots if spec.cache_rows > 0 else 0), _flide_dtype(spec.dtype),
+                                    int(spec.deterministic))
             self.attn_params.append(p)
             if spec.cache_rows > 0:
                 # keys [slot, row, kv head, d]; values transposed [slot, kv head, d, row]
@@ -76,7 +79,8 @@ class RoundBuffers:
             self.ws.append(torch.zeros(nbytes, dtype=torch.uint8, device=device))
         C = s.channels
         act = 1 if getattr(s, "gdn_act", "none") == "silu" else 0
-        self.gdn_params = F.flide_gdn_params(s.H, s.dk, s.dv, s.conv_k, act, 64, _flide_dtype(spec.dtype), 0)
+        self.gdn_params = F.flide_gdn_params(s.H, s.dk, s.dv, s.conv_k, act, 64, _flide_dtype(spec.dtype),
+                                             int(spec.deterministic))
         self.x = z(T, C)
         self.conv_w = z(C, s.conv_k, dtype=torch.float32)
         self.alpha = z(T, s.H, dtype=torch.float32)
@@ -399,7 +403,7 @@ class StackRunner:
             self.xg, self.zab = z(T, C), z(T, 2 * s.H)
             self.alpha, self.eta = z(T, s.H, dtype=torch.float32), z(T, s.H, dtype=torch.float32)
             self.o_gdn = z(T, s.H, s.dv)
-            self.gdn_params = F.flide_gdn_params(s.H, s.dk, s.dv, s.conv_k, 0, 64, fd, 0)
+            self.gdn_params = F.flide_gdn_params(s.H, s.dk, s.dv, s.conv_k, 0, 64, fd, 1)
         if kinds & {"attn", "swa"}:
             self.q, self.k, self.v = z(T, s.Hq, s.d), z(T, s.Hkv, s.d), z(T, s.Hkv, s.d)
             self.o_attn = z(T, s.Hq, s.d)
@@ -419,7 +423,7 @@ class StackRunner:
                 D["conv_pool"] = z(self.n_slots, max(1, s.conv_k - 1), s.gdn_channels)
             else:
                 p = F.flide_attn_params(s.Hq, s.Hkv, s.d, s.window if L["kind"] == "swa" else 0, float(s.theta),
-                                        int(max_pos), 0, 0, fd, 0)
+                                        int(max_pos), 0, 0, fd, 1)
                 D["params"] = p
                 D["ws"] = torch.zeros(F.flide_attn_workspace_bytes(self.caps, p), dtype=torch.uint8, device=device)
             self.layers.append(D)
