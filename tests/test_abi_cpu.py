@@ -204,3 +204,26 @@ def test_planner_interior_checkpoints():
     assert d["req_save_m"].tolist() == [256, 0, 200]
     assert d["req_save_slot"].tolist() == [4, -1, 5]
     assert d["req_ckpt"].tolist() == [-1, -1, 2]
+
+
+def test_host_code_under_sanitizers(tmp_path):
+    """The planner and the checkpoint store built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (plain g++, host code only) run thousands of seeded rounds, valid and broken, into images of exactly
+    the size their layout names, and random store operation sequences, without a finding."""
+    import shutil
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ is not available")
+    exe = str(tmp_path / "sanitize_host")
+    srcs = [os.path.join(ROOT, "tree_forked_hybrid_amd", "csrc", f) for f in ("plan.cpp", "store.cpp")]
+    srcs.append(os.path.join(ROOT, "tests", "sanitize_host.cpp"))
+    flags = ["-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=all", "-I" + os.path.join(ROOT, "include")]
+    res = subprocess.run([gxx, *flags, *srcs, "-o", exe], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-3000:]
+    # verify_asan_link_order=0: the runtime need not come first when the environment preloads a library
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0", UBSAN_OPTIONS="print_stacktrace=1")
+    run = subprocess.run([exe, "3000"], capture_output=True, text=True, env=env, timeout=300)
+    assert run.returncode == 0, (run.stdout[-2000:], run.stderr[-4000:])
+    assert "sanitized host run" in run.stdout
+    print(run.stdout.strip())
