@@ -273,6 +273,41 @@ def stack_main(args):
     gc.enable()
     F.flide_check_device(ctx, sr.caps, sr.dev_meta)
     ms = (t1 - t0) * 1e3 / args.steps
+    # the row-wise layers' kernels at this workload's shapes (layer 0 weights, all stream rows), HIP events on
+    # the launch stream; the linear layers are MFMA-bound: 2 T N K FLOPs per call
+    L0 = sr.layers[0]
+    fd, ALL, Dm, Fm = F.FLIDE_BF16, F.FLIDE_ROWS_ALL, shapes.Dm, shapes.F
+    C = shapes.gdn_channels
+    calls = {
+        "linear_gate_up": (lambda: F.flide_linear(ctx, sr.caps, sr.dev_meta, ALL, fd, 2 * Fm, Dm, sr.h, Dm,
+                                                  L0["gate_up"], None, sr.gu, 2 * Fm, st), 2.0 * T * 2 * Fm * Dm),
+        "linear_down": (lambda: F.flide_linear(ctx, sr.caps, sr.dev_meta, ALL, fd, Dm, Fm, sr.mid, Fm, L0["down"],
+                                               None, sr.hf, Dm, st), 2.0 * T * Dm * Fm),
+        "linear_gdn_in": (lambda: F.flide_linear(ctx, sr.caps, sr.dev_meta, ALL, fd, C, Dm, sr.h, Dm, L0["w_x"],
+                                                 None, sr.xg, C, st), 2.0 * T * C * Dm),
+        "rmsnorm": (lambda: F.flide_rmsnorm(ctx, sr.caps, sr.dev_meta, ALL, fd, Dm, sr.x, L0["norm1"], 1e-6, sr.h,
+                                            st), None),
+        "swiglu": (lambda: F.flide_swiglu(ctx, sr.caps, sr.dev_meta, ALL, fd, Fm, sr.gu, sr.mid, st), None),
+    }
+    kern = {}
+    for name, (fn, flops) in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(args.kernel_reps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.kernel_reps
+        kern[name] = {"us": round(us, 2)}
+        if flops:
+            kern[name]["TFLOP/s"] = round(flops / (us * 1e-6) / 1e12, 1)
+            kern[name]["mfma_frac"] = round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    dom = max((k for k in kern if k.startswith("linear")), key=lambda k: kern[k]["us"])
+    roof = {"bound": "mfma", "achieved": kern[dom]["TFLOP/s"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": kern[dom]["mfma_frac"], "traffic": None, "kernel": dom, "avg_launch_us": kern[dom]["us"],
+            "algorithmic_per_launch": round(calls[dom][1])}
     layers = [{"layer": i, "kind": k, "us": round(per_layer[i], 1), "tokens_per_s": round(T / (per_layer[i] * 1e-6), 1)}
               for i, k in enumerate(shapes.layers)]
     rec = {
@@ -285,9 +320,40 @@ def stack_main(args):
                    "stream_rows": T, "questions": n_q},
         "per_layer": layers,
         "final_norm_and_readout_us": round(per_layer[-1], 1),
+        "kernels": kern,
+        "roofline": roof,
+        "cpu_baseline": stack_cpu_baseline(shapes, 9000 + args.seed) if args.cpu_sample > 0 else None,
     }
     print(json.dumps(rec), flush=True)
     ctx.close()
+
+
+def stack_cpu_baseline(shapes, base: int):
+    """The stack oracle (as it stands: fp64 NumPy, rows one at a time through every layer, one BLAS thread)
+    on a bounded sample of the workload: one request of the same weights with a 96-row trunk and one
+    16-row question, memo order; tokens/s = its rows / wall time."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # noqa: BLE001
+        threadpool_limits = None
+    from oracle import stack as ostack
+    from workloads import Request, make_stack
+    small = make_stack(shapes, "bf16", [Request(P=96, m=0, q_len=(16,), n_opt=(3,), out_slot=0)], base=base)
+    small.weights()
+    small.payload(0)
+    limiter = threadpool_limits(1) if threadpool_limits else None
+    try:
+        t0 = time.perf_counter()
+        ostack.run_stack_request(small, 0, "memo")
+        t1 = time.perf_counter()
+    finally:
+        if limiter is not None:
+            limiter.unregister()
+    return {"value": round(112 / (t1 - t0), 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"one request of the stack's weights, 96 trunk rows + one 16-row question (112 rows through "
+                      f"all {len(shapes.layers)} layers), memo order, fp64, one BLAS thread: {t1 - t0:.1f} s; "
+                      f"host {os.cpu_count()} logical CPUs, {_host_cpu()}",
+            "host_cpus": os.cpu_count()}
 
 
 def main():
