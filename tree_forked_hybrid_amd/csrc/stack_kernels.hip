@@ -155,6 +155,151 @@ __global__ void __launch_bounds__(256) linear_mfma_kernel(MetaView mv, int rows_
     }
 }
 
+// Larger form for K a multiple of 64: workgroup tile 128 rows x 128 columns, four waves of 64 x 64
+// (4 x 4 blocks of 16 x 16), K advancing 64 at a time.  Both operand tiles are copied straight into LDS
+// (16 bytes per lane) one K step ahead into the other of two buffers, with the 16-byte chunks of row r
+// XOR-swizzled by (r / 2) % 8 so that the fragment reads (16 rows x 16 bytes per pass) are conflict-free;
+// fragments are read with inline-asm ds_read_b128 and explicit lgkmcnt waits (the compiler would drain
+// every LDS read behind the copies in flight).  Each output element accumulates the same 32-wide K chunks,
+// in the same order, on the same MFMA as linear_mfma_kernel: the two forms give identical bits.
+constexpr int TM = 128, TN = 128, TK = 64;
+constexpr int TROW = TK * 2;        // bytes per tile row
+constexpr int TBYTES = TM * TROW;   // bytes per operand tile (16 KB)
+
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src),
+                                   (__attribute__((address_space(3))) void*)(lds_dst), 16, 0, 0);
+}
+template <int OFF>
+__device__ __forceinline__ u32x4v ds_read16(unsigned addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset field");
+  u32x4v r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+// returns once at most N of this wave's LDS reads are outstanding, ordered before any use of the eight tied
+// fragments
+template <int N>
+__device__ __forceinline__ void lgkm_wait8(u32x4v (&f)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]), "+v"(f[6]), "+v"(f[7])
+               : "i"(N));
+}
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+linear_tile_kernel(MetaView mv, int rows_mode, const bf16_t* __restrict__ a, int64_t lda,
+                   const bf16_t* __restrict__ w, int N, int K, const bf16_t* R, bf16_t* C, int64_t ldc) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * TBYTES];  // A0 W0 A1 W1
+  const int tid = threadIdx.x, l = tid & 63, r16 = l & 15, g4 = l >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wv >> 1, wn = wv & 1;
+  const int i0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
+  const int n_set = rows_mode == 0 ? mv.hdr[H_T] : mv.hdr[H_NQST];
+  if (i0 >= n_set) return;  // the whole tile is past the row set
+  // copies: instruction I = 4 wv + ii of an operand fills 16-byte slots 64 I + l, i.e. tile row 8 I + l / 8,
+  // physical chunk l % 8 = logical chunk (l % 8) ^ ((row / 2) % 8).  Rows past the set or past N read a
+  // valid row (their results are not stored).
+  const bf16_t* asrc[4];
+  const bf16_t* wsrc[4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const int row = 8 * (4 * wv + ii) + (l >> 3);
+    const int c = (l & 7) ^ ((row >> 1) & 7);
+    int ar = row_of(mv, rows_mode, i0 + row);
+    if (ar < 0) ar = row_of(mv, rows_mode, i0);
+    const int wr = min(n0 + row, N - 1);
+    asrc[ii] = a + int64_t(ar) * lda + 8 * c;
+    wsrc[ii] = w + int64_t(wr) * K + 8 * c;
+  }
+  auto issue = [&](int k0, int stage) {
+    unsigned char* at = lds + stage * 2 * TBYTES;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      copy16_to_lds(asrc[ii] + k0, at + (4 * wv + ii) * 1024);
+      copy16_to_lds(wsrc[ii] + k0, at + TBYTES + (4 * wv + ii) * 1024);
+    }
+  };
+  // fragment of row block b (rows 64 wm + 16 b + r16 of A, or 64 wn + 16 b + r16 of W), K half kk: logical
+  // chunk 4 kk + g4 of the row; the swizzle of those rows is (r16 / 2) % 8
+  const int swz = (r16 >> 1) & 7;
+  const unsigned lds_base = unsigned(uintptr_t((__attribute__((address_space(3))) void*)lds));
+  const unsigned abase = lds_base + unsigned((64 * wm + r16) * TROW);
+  const unsigned wbase = lds_base + TBYTES + unsigned((64 * wn + r16) * TROW);
+  const unsigned off0 = unsigned(((0 + g4) ^ swz) << 4), off1 = unsigned(((4 + g4) ^ swz) << 4);
+  f32x4v acc[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  auto step = [&](auto STAGE) {
+    constexpr int SO = decltype(STAGE)::value * 2 * TBYTES;
+    u32x4v f0[8], f1[8];  // K half 0 and 1: A blocks 0-3, then W blocks 0-3
+    f0[0] = ds_read16<SO + 0 * 16 * TROW>(abase + off0);
+    f0[1] = ds_read16<SO + 1 * 16 * TROW>(abase + off0);
+    f0[2] = ds_read16<SO + 2 * 16 * TROW>(abase + off0);
+    f0[3] = ds_read16<SO + 3 * 16 * TROW>(abase + off0);
+    f0[4] = ds_read16<SO + 0 * 16 * TROW>(wbase + off0);
+    f0[5] = ds_read16<SO + 1 * 16 * TROW>(wbase + off0);
+    f0[6] = ds_read16<SO + 2 * 16 * TROW>(wbase + off0);
+    f0[7] = ds_read16<SO + 3 * 16 * TROW>(wbase + off0);
+    f1[0] = ds_read16<SO + 0 * 16 * TROW>(abase + off1);
+    f1[1] = ds_read16<SO + 1 * 16 * TROW>(abase + off1);
+    f1[2] = ds_read16<SO + 2 * 16 * TROW>(abase + off1);
+    f1[3] = ds_read16<SO + 3 * 16 * TROW>(abase + off1);
+    f1[4] = ds_read16<SO + 0 * 16 * TROW>(wbase + off1);
+    f1[5] = ds_read16<SO + 1 * 16 * TROW>(wbase + off1);
+    f1[6] = ds_read16<SO + 2 * 16 * TROW>(wbase + off1);
+    f1[7] = ds_read16<SO + 3 * 16 * TROW>(wbase + off1);
+    lgkm_wait8<8>(f0);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, f0[rb]),
+                                                              __builtin_bit_cast(bf16x8v, f0[4 + cb]), acc[rb][cb], 0,
+                                                              0, 0);
+    lgkm_wait8<0>(f1);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, f1[rb]),
+                                                              __builtin_bit_cast(bf16x8v, f1[4 + cb]), acc[rb][cb], 0,
+                                                              0, 0);
+  };
+  const int nst = K / TK;
+  issue(0, 0);
+  for (int s0 = 0; s0 < nst; s0 += 2) {
+    // stage s0 (buffer 0): its copies have landed everywhere; buffer 1 is free for stage s0 + 1
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (s0 + 1 < nst) issue((s0 + 1) * TK, 1);
+    step(std::integral_constant<int, 0>{});
+    if (s0 + 1 >= nst) break;
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (s0 + 2 < nst) issue((s0 + 2) * TK, 0);
+    step(std::integral_constant<int, 1>{});
+  }
+  // explicit wait states before the VALU reads of the accumulators (see linear_mfma_kernel)
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(acc[rb][0]), "+v"(acc[rb][1]), "+v"(acc[rb][2]), "+v"(acc[rb][3]));
+  // lane holds C[64 wm + 16 rb + 4 g4 + i][64 wn + 16 cb + r16] of the tile
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = row_of(mv, rows_mode, i0 + 64 * wm + 16 * rb + 4 * g4 + i);
+      if (r < 0) continue;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int n = n0 + 64 * wn + 16 * cb + r16;
+        if (n >= N) continue;
+        float v = acc[rb][cb][i];
+        if (R) v += bf16_to_f32(R[int64_t(r) * ldc + n]);
+        C[int64_t(r) * ldc + n] = f32_to_bf16(v);
+      }
+    }
+}
+
 // fp32 linear layers: one output per thread, the K loop in order (fp32 mode is a correctness path).
 __global__ void __launch_bounds__(256) linear_f32_kernel(MetaView mv, int rows_mode, const float* __restrict__ a,
                                                          int64_t lda, const float* __restrict__ w, int N, int K,
@@ -218,7 +363,11 @@ int launch_linear(const MetaView& mv, int rows_mode, int dtype, int N, int K, co
                   const void* w, const void* resid, void* c, int64_t ldc, void* stream) {
   const int n = rows_mode == 0 ? mv.T_cap : (mv.Q_cap > 0 ? mv.Q_cap : 1);
   hipStream_t st = (hipStream_t)stream;
-  if (dtype == FLIDE_BF16) {
+  if (dtype == FLIDE_BF16 && K % TK == 0) {
+    const dim3 grid((N + TN - 1) / TN, (n + TM - 1) / TM);
+    hipLaunchKernelGGL(linear_tile_kernel, grid, dim3(256), 0, st, mv, rows_mode, (const bf16_t*)a, lda,
+                       (const bf16_t*)w, N, K, (const bf16_t*)resid, (bf16_t*)c, ldc);
+  } else if (dtype == FLIDE_BF16) {
     const dim3 grid((N + GN - 1) / GN, (n + GM - 1) / GM);
     hipLaunchKernelGGL(linear_mfma_kernel, grid, dim3(256), 0, st, mv, rows_mode, (const bf16_t*)a, lda,
                        (const bf16_t*)w, N, K, (const bf16_t*)resid, (bf16_t*)c, ldc);
