@@ -10,6 +10,7 @@ memory and streams.
 from __future__ import annotations
 
 import ctypes as C
+import itertools
 import os
 from typing import Iterable, List, Optional, Sequence, Tuple
 
@@ -212,28 +213,36 @@ _REQ_DTYPE = np.dtype({"names": list(_REQ_FIELDS),
 
 class Requests:
     """A round's requests as a C array of flide_request (keeps the q_len storage alive).  Built as one
-    numpy record array: per-field ctypes assignment costs more host time than the planner itself."""
+    numpy record array from one pass over the requests: per-field ctypes assignment costs more host time
+    than the planner itself.  The binding's planner functions accept an instance in place of the request
+    sequence, so a caller that plans one round several ways marshals it once."""
 
     def __init__(self, requests: Sequence):
         n = len(requests)
         self.n = n
         qls = [r.q_len for r in requests]
-        nq = np.fromiter((len(q) for q in qls), np.int64, n)
-        self._q = np.ascontiguousarray(np.concatenate([np.asarray(q, dtype=np.int32).ravel() for q in qls])
-                                       if n and nq.sum() else np.zeros(1, np.int32), dtype=np.int32)
+        ints = np.array([(r.P, r.m, len(q), r.ckpt_slot, r.out_slot, getattr(r, "save_m", 0),
+                          getattr(r, "save_slot", -1)) for r, q in zip(requests, qls)],
+                        dtype=np.int64).reshape(n, 7)
+        nq = ints[:, 2]
+        total = int(nq.sum())
+        self._q = np.fromiter(itertools.chain.from_iterable(qls), np.int32, total) if total else np.zeros(1, np.int32)
         rec = np.zeros(max(1, n), _REQ_DTYPE)
         if n:
-            rec["P"][:n] = np.fromiter((r.P for r in requests), np.int64, n)
-            rec["m"][:n] = np.fromiter((r.m for r in requests), np.int64, n)
-            rec["n_q"][:n] = nq
-            off = np.concatenate([[0], np.cumsum(nq)[:-1]])
+            rec["P"][:n], rec["m"][:n], rec["n_q"][:n] = ints[:, 0], ints[:, 1], nq
+            rec["ckpt_slot"][:n], rec["out_slot"][:n] = ints[:, 3], ints[:, 4]
+            rec["save_m"][:n], rec["save_slot"][:n] = ints[:, 5], ints[:, 6]
+            off = np.cumsum(nq) - nq
             rec["q_len"][:n] = np.where(nq > 0, self._q.ctypes.data + 4 * off, 0).astype(np.uint64)
-            rec["ckpt_slot"][:n] = np.fromiter((r.ckpt_slot for r in requests), np.int64, n)
-            rec["out_slot"][:n] = np.fromiter((r.out_slot for r in requests), np.int64, n)
-            rec["save_m"][:n] = np.fromiter((getattr(r, "save_m", 0) for r in requests), np.int64, n)
-            rec["save_slot"][:n] = np.fromiter((getattr(r, "save_slot", -1) for r in requests), np.int64, n)
         self._rec = rec
         self.arr = rec.ctypes.data_as(C.POINTER(flide_request))
+
+    def __len__(self) -> int:
+        return self.n
+
+
+def _marshal(requests) -> Requests:
+    return requests if isinstance(requests, Requests) else Requests(requests)
 
 
 def caps_of(T_cap: int, R_cap: int, Q_cap: int) -> flide_caps:
@@ -251,7 +260,7 @@ def flide_meta_layout_for(caps: flide_caps) -> flide_meta_layout:
 
 
 def flide_plan_sizes(requests: Sequence) -> Tuple[int, int, int]:
-    rq = Requests(requests)
+    rq = _marshal(requests)
     T, ns, nq = C.c_int32(), C.c_int32(), C.c_int32()
     _check(load_library().flide_plan_sizes(rq.arr, rq.n, C.byref(T), C.byref(ns), C.byref(nq)), "flide_plan_sizes")
     return T.value, ns.value, nq.value
@@ -262,7 +271,7 @@ def flide_plan_round(requests: Sequence, caps: flide_caps, image: Optional[np.nd
     L = flide_meta_layout_for(caps)
     if image is None:
         image = np.zeros(L.host_words, np.int32)
-    rq = Requests(requests)
+    rq = _marshal(requests)
     _check(load_library().flide_plan_round(rq.arr, rq.n, C.byref(caps),
                                            image.ctypes.data_as(C.POINTER(C.c_int32)), int(image.size)),
            "flide_plan_round")
@@ -270,7 +279,7 @@ def flide_plan_round(requests: Sequence, caps: flide_caps, image: Optional[np.nd
 
 
 def flide_split_round(requests: Sequence, T_max: int) -> Tuple[List[int], List[bool]]:
-    rq = Requests(requests)
+    rq = _marshal(requests)
     first = (C.c_int32 * (rq.n + 1))()
     eager = (C.c_uint8 * max(1, rq.n))()
     n_sub = C.c_int32()

@@ -321,8 +321,9 @@ class BucketTable:
         return bid, F.flide_plan_round(requests, caps, img)
 
     def run(self, requests, stream=None, bid: Optional[int] = None) -> int:
-        """Plan the round for its bucket, upload the metadata and replay the bucket's graph."""
-        bid, img = self.plan(requests, bid)
+        """Plan the round for its bucket, upload the metadata and replay the bucket's graph (the request list
+        is marshalled for the C ABI once, for both the bucket choice and the plan)."""
+        bid, img = self.plan(F.Requests(requests), bid)
         F.flide_graph_replay(self.ctx, bid, img, stream)
         self.last = (bid, img)
         return bid
