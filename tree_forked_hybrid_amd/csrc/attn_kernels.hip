@@ -334,8 +334,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 // direct global-to-LDS copies issued one tile ahead, so memory latency overlaps
 // the MFMA work; 64 KB of LDS per workgroup leaves room for two workgroups per
 // CU.  Both tiles are stored with an XOR swizzle of their 16-byte chunks (key
-// row r: chunk c at slot c ^ ksw(r); value row d: chunk c at slot
-// c ^ ((d >> 2) & 3)), which makes the MFMA operand reads bank-conflict free.
+// row r: chunk c at slot c ^ ksw(r); value row d: chunk c at slot c ^ vsw(d)),
+// which makes the MFMA operand reads bank-conflict free.
 // Score block kb row r is key 8 (r / 4) + 4 kb + r % 4, so each lane ends up
 // with the probabilities of 8 consecutive keys: exactly the k-slots of its
 // P^T fragment, whose matching V^T fragment is then one 16-byte read.
@@ -347,6 +347,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Swizzle of the key tile's 16-byte chunks: distinct for the 16 rows one MFMA
 // operand read touches (rows 8a + 4kb + b, a, b in 0..3).
 __device__ __forceinline__ int ksw(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
+// Swizzle of the value tile's chunks (rows of four 16-byte chunks).  Measured on gfx950: a 16-byte LDS read
+// (ds_read_b128) serves the wave in four groups of 16 lanes, lane l in group (l / 16) ^ (bit 2 of l ^ bit 3
+// of l), and a group takes one pass when its lanes hit 16 distinct 16-byte columns of a 256-byte bank row
+// (equal addresses are broadcast).  The V^T operand read (lane l: row l % 16, chunk l / 16) therefore needs
+// distinct chunk ^ swizzle over rows 4a + b, a = 0..3, after that lane regrouping; ((row >> 2) & 3) alone
+// leaves two rows of each group on one column and halves the read rate.
+__device__ __forceinline__ int vsw(int row) { return ((row >> 2) & 3) ^ (((row >> 2) ^ (row >> 3)) & 1); }
 
 template <int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -494,7 +501,7 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
     const int krow = slot / KCH;
     k_off0[ii] = (krow * Hkv * D + (((slot % KCH) ^ ksw(krow)) * 8)) * 2;  // bytes from the tile's first key row
   }
-  const int vc = (l & 3) ^ ((l >> 4) & 3);
+  const int vc = (l & 3) ^ vsw(l >> 2);
   auto issue = [&](const Cursor& c, int buf) {
     const int ts = c.ts, lo = c.lo, hi = c.hi, vstride = c.vstride;
     const bool edge = ts < lo || ts + BN > hi;
@@ -612,7 +619,7 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   // (bits 6-7 of these offsets hold c % 4 ^ (ks >> 2) and nothing carries into them, so one base
   // and an XOR give all four)
   const int kfrag0 = krow0 * KROW + ((g4 ^ (ks & 3)) << 4) + ((ks >> 2) << 6);
-  const int vfrag = r16 * VROW + ((g4 ^ ((r16 >> 2) & 3)) << 4);
+  const int vfrag = r16 * VROW + ((g4 ^ vsw(r16)) << 4);
   const unsigned lds_base = unsigned(uintptr_t((__attribute__((address_space(3))) void*)lds));
 
   // One key tile.  Copies of tile t + 1 go out right after the barrier that frees their buffer; the
