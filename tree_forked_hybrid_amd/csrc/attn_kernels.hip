@@ -608,7 +608,10 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4v{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};  // l_run: this lane's share of the sum
+  // m_run starts far below any score instead of at -inf: the first visible key always moves it, its
+  // correction factor is then exactly 0 (as it would be from -inf), and no select is needed for the
+  // exponent offset.  l_run: this lane's share of the column's sum.
+  float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.f, 0.f};
   // LDS byte offsets of this lane's MFMA operand reads.  Key fragment (kb, c) (key row
   // 8 (r16 / 4) + 4 kb + r16 % 4, chunk 4 c + g4 swizzled) sits at kfrag[c % 4] + kb * 4 * KROW +
   // 256 (c / 4): the swizzle is the same for both kb and only permutes chunk groups of four, so four
@@ -689,28 +692,29 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
             s[kb][qb][i] = ok ? s[kb][qb][i] : -INFINITY;
           }
       }
-      float mx = fmaxf(fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), fmaxf(s[0][qb][2], s[0][qb][3])),
-                       fmaxf(fmaxf(s[1][qb][0], s[1][qb][1]), fmaxf(s[1][qb][2], s[1][qb][3])));
-      mx = rows4_max(mx);
-      // move the running maximum only when it grows by more than 8 (log2 units)
-      const bool grow = mx > m_run[qb] + 8.f;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? fmaxf(m_run[qb], mx) : m_run[qb];
-        const float corr = m_run[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+      // The running maximum of a column moves only when the column's maximum grows by more than 8 (log2
+      // units), which is when one of its four lanes' maxima does: the lanes compare their own 8 keys, and
+      // the column maximum is formed only in the (rare) tiles where some lane of the wave moves.
+      const float mx = fmaxf(fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), fmaxf(s[0][qb][2], s[0][qb][3])),
+                             fmaxf(fmaxf(s[1][qb][0], s[1][qb][1]), fmaxf(s[1][qb][2], s[1][qb][3])));
+      if (__builtin_amdgcn_ballot_w64(mx > m_run[qb] + 8.f)) {
+        const float mc = rows4_max(mx);
+        const float m_new = mc > m_run[qb] + 8.f ? fmaxf(m_run[qb], mc) : m_run[qb];
+        const float corr = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
         l_run[qb] *= corr;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) acc[qb][db] *= corr;
         m_run[qb] = m_new;
       }
-      const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
-      float rs = 0.f;
+      const float m_use = m_run[qb];
+      float rs;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float pv = __builtin_amdgcn_exp2f(s[kb][qb][i] - m_use);
           s[kb][qb][i] = pv;
-          rs += pv;
+          rs = kb == 0 && i == 0 ? pv : rs + pv;
         }
       l_run[qb] += rs;  // this lane's 8 keys; the four lanes of a column are summed once, at the end
       pf[qb] = u32x4v{pack_bf16x2(s[0][qb][0], s[0][qb][1]), pack_bf16x2(s[0][qb][2], s[0][qb][3]),
