@@ -187,8 +187,9 @@ def cpu_baseline(rnd, n_trunk_sample: int = 48):
 
 
 def measured_peaks(torch):
-    """Device-to-device copy bandwidth and a large bf16 GEMM (the vendor library) in this job: practical
-    ceilings beside the published peaks."""
+    """Device-to-device copy bandwidth, a large bf16 GEMM (the vendor library) and a loop of independent bf16
+    matrix products (libflide's flide_measure_mfma_peak) in this job: practical ceilings beside the published
+    peaks."""
     n = 1 << 30
     a = torch.empty(n // 2, dtype=torch.bfloat16, device="cuda")
     b = torch.empty_like(a)
@@ -214,7 +215,10 @@ def measured_peaks(torch):
     torch.cuda.synchronize()
     gemm = 2 * m ** 3 * 10 / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12
     del x, y, z
-    return {"d2d_copy_GB/s": round(copy_gbs, 1), "bf16_gemm_8192_TFLOP/s": round(gemm, 1)}
+    from tree_forked_hybrid_amd import flide as F
+    mfma = F.flide_measure_mfma_peak(4096, torch.cuda.current_stream())
+    return {"d2d_copy_GB/s": round(copy_gbs, 1), "bf16_gemm_8192_TFLOP/s": round(gemm, 1),
+            "bf16_mfma_loop_TFLOP/s": round(mfma, 1)}
 
 
 def stack_main(args):

@@ -528,6 +528,15 @@ flide_status flide_graph_release(flide_ctx* ctx, int32_t bucket_id);
  * request above the largest capacity ([KO] §어떻게 쓰나).                      */
 flide_status flide_round_eager(flide_ctx* ctx, const flide_round_bufs* bufs, const int32_t* image, void* stream);
 
+/* Infrastructure (a measured ceiling beside the published bf16 MFMA peak; no
+ * passage of the pages asks for it).  Runs a loop of independent bf16
+ * 16x16x32 matrix products (eight accumulators per wave, 512 workgroups of
+ * 256 threads, `iters` x 8 products per wave) on `stream` after one short
+ * warm-up launch, synchronises the stream and writes the rate in TFLOP/s to
+ * *tflops (host).  Allocates nothing on the device.
+ * Errors: FLIDE_E_INVALID_ARG (iters < 1 or tflops NULL), FLIDE_E_HIP.      */
+flide_status flide_measure_mfma_peak(int32_t iters, void* stream, double* tflops);
+
 /* Infrastructure.  Synchronise `stream`, read and clear the device error word
  * of dev_meta (device).  Returns FLIDE_E_DEVICE (with a message) if a kernel
  * flagged bad metadata, FLIDE_E_HIP if the stream reports an error.          */

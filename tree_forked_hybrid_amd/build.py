@@ -28,6 +28,7 @@ SOURCES = [
     "gdn_chunk_kernels.hip",
     "readout_kernels.hip",
     "noalloc.hip",
+    "peak_kernels.hip",
     "stack_kernels.hip",
 ]
 HEADERS = ["flide_internal.hpp", "device_common.hpp"]

@@ -137,6 +137,7 @@ _SIGNATURES = {
     "flide_graph_release": (C.c_int, [_VP, C.c_int32]),
     "flide_round_eager": (C.c_int, [_VP, C.POINTER(flide_round_bufs), C.POINTER(C.c_int32), _VP]),
     "flide_check_device": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, _VP]),
+    "flide_measure_mfma_peak": (C.c_int, [C.c_int32, _VP, C.POINTER(C.c_double)]),
 }
 
 _lib: Optional[C.CDLL] = None
@@ -517,6 +518,13 @@ def flide_round_eager(ctx: Context, bufs: flide_round_bufs, image: np.ndarray, s
 def flide_check_device(ctx: Context, caps: flide_caps, dev_meta, stream=None) -> None:
     _check(load_library().flide_check_device(ctx.handle, C.byref(caps), _ptr(dev_meta), _stream(stream)),
            "flide_check_device", ctx.handle)
+
+
+def flide_measure_mfma_peak(iters: int = 4096, stream=None) -> float:
+    """TFLOP/s of a loop of independent bf16 matrix products (a measured ceiling; synchronises `stream`)."""
+    out = C.c_double(0.0)
+    _check(load_library().flide_measure_mfma_peak(int(iters), _stream(stream), C.byref(out)), "flide_measure_mfma_peak")
+    return out.value
 
 
 def exported_names() -> Iterable[str]:
