@@ -376,6 +376,9 @@ def main():
     ap.add_argument("--nondeterministic", action="store_true",
                     help="GDN chunk boundaries on the stream's 64-row grid (bits then depend on the round's "
                          "composition); the default is the composition-independent mode")
+    ap.add_argument("--serial-subrounds", action="store_true",
+                    help="replay the sub-rounds of a split round one after another (the default runs their fronts "
+                         "— metadata expansion and the trunk GDN call — side by side, runner.FrontScheduler)")
     ap.add_argument("--stack", action="store_true",
                     help="time the multi-layer hybrid stack instead of the ForkAttention round (its own JSON line)")
     args = ap.parse_args()
@@ -391,7 +394,7 @@ def main():
     import torch
 
     from tree_forked_hybrid_amd import flide as F
-    from tree_forked_hybrid_amd.runner import BucketTable, bucket_capacities, spec_for_round
+    from tree_forked_hybrid_amd.runner import BucketTable, FrontScheduler, bucket_capacities, spec_for_round
     from workloads import CONFIGS, make_round
 
     spec_cfg = CONFIGS[args.config]
@@ -420,8 +423,16 @@ def main():
         print(f"[bench] sub-round {k}: {len(sub.requests)} requests, bucket T_cap {tab.caps_of(bid).T_cap}",
               flush=True)
     sub_reqs = [s.requests for s in subs]
+    # The sub-rounds' fronts (metadata upload and expansion, trunk GDN call) run side by side, each on a
+    # stream of its own; the backs (question GDN call, attention, readout) follow in order on the launch
+    # stream (a single sub-round: front and back on the launch stream).
+    co_schedule = len(tables) > 1 and not args.serial_subrounds
+    sched = FrontScheduler(len(tables)) if co_schedule else None
 
     def step():
+        if sched is not None:
+            sched.run(tables, sub_reqs)
+            return
         for tab, reqs in zip(tables, sub_reqs):
             tab.run(reqs)
 
@@ -580,7 +591,8 @@ def main():
                    "stream_rows": T, "requests": len(rnd.requests),
                    "questions": sum(len(r.q_len) for r in rnd.requests),
                    "bucket_table_T_caps": [c.T_cap for c in caps_table], "seed": args.seed,
-                   "deterministic": spec.deterministic},
+                   "deterministic": spec.deterministic,
+                   "subround_fronts": "side by side" if co_schedule else "in order"},
         "round_latency_ms": {"p10": round(lat_ms[len(lat_ms) // 10], 4), "median": round(lat_ms[len(lat_ms) // 2], 4),
                              "p90": round(lat_ms[(9 * len(lat_ms)) // 10], 4)},
         "per_layer_tokens_per_s": {

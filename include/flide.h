@@ -503,7 +503,8 @@ typedef struct {
 
 /* Capture the whole round (metadata expansion, GDN phases 0 and 1, attention
  * layers, the checkpoint K/V of requests with save_m > 0 when the layer has a
- * K/V cache, readout) into a HIP graph for capacity bufs->caps.  Launch shapes
+ * K/V cache, readout) into HIP graphs (the front and back halves of
+ * flide_graph_replay_front / _back) for capacity bufs->caps.  Launch shapes
  * depend only on the capacity; kernels read their work from the metadata.
  * *bucket_id receives the bucket's id.  Errors: FLIDE_E_INVALID_ARG,
  * FLIDE_E_UNSUPPORTED, FLIDE_E_HIP.                                           */
@@ -518,6 +519,21 @@ flide_status flide_select_bucket(const flide_ctx* ctx, int32_t T, int32_t R, int
  * Errors: FLIDE_E_INVALID_ARG (no such or released bucket, NULL image),
  * FLIDE_E_CAPACITY (image planned for larger caps), FLIDE_E_HIP. */
 flide_status flide_graph_replay(flide_ctx* ctx, int32_t bucket_id, const int32_t* image, void* stream);
+/* Infrastructure (scheduling of the request-boundary sub-rounds of [KO]
+ * §어떻게 쓰나).  The captured round in two halves: the front (metadata
+ * expansion and GDN call 1, the trunks) and the back (GDN call 2, attention,
+ * checkpoint K/V, readout).  flide_graph_replay_front uploads `image` as
+ * flide_graph_replay does and launches the front on `stream`;
+ * flide_graph_replay_back launches the back on `stream`.  Front then back of
+ * one bucket, in that order, is exactly flide_graph_replay; the caller orders
+ * the back after the front (the same stream, or an event) and the next front
+ * of the bucket after the back.  Fronts of different buckets (different
+ * buffers) may run side by side: a sub-round's trunk call alone fills only as
+ * many CUs as it has (segment, head) pairs.
+ * Errors: FLIDE_E_INVALID_ARG (no such or released bucket, NULL image),
+ * FLIDE_E_CAPACITY (image planned for larger caps), FLIDE_E_HIP.            */
+flide_status flide_graph_replay_front(flide_ctx* ctx, int32_t bucket_id, const int32_t* image, void* stream);
+flide_status flide_graph_replay_back(flide_ctx* ctx, int32_t bucket_id, void* stream);
 /* Infrastructure (the capacity buckets of [KO] §어떻게 쓰나 are captured at
  * init; a caller that frees a bucket's buffers releases its graph first).
  * Destroy bucket `bucket_id`'s graph and staging after the device is idle; the

@@ -80,10 +80,11 @@ def run_gpu(rnd, ctx, mode: str = "direct", spec=None, bufs=None, repeats: int =
     return bufs, lay
 
 
-def run_split(rnd, tables, t_max: Optional[int] = None):
+def run_split(rnd, tables, t_max: Optional[int] = None, co_schedule: bool = False):
     """Run ``rnd`` through bucket tables: split at request boundaries for the tables' largest capacity (or
     ``t_max``), sub-round k filled into table k mod len(tables) (placement by the oracle's layout) and all
-    sub-rounds replayed back to back, each in the smallest bucket that holds it.  Tables must not be reused
+    sub-rounds replayed back to back, each in the smallest bucket that holds it (co_schedule: the fronts of
+    the sub-rounds side by side on streams of their own, runner.FrontScheduler).  Tables must not be reused
     within one call (len(tables) >= number of sub-rounds).  Returns [(sub-round, table, layout)]."""
     import torch
     from tree_forked_hybrid_amd import flide as F
@@ -96,10 +97,15 @@ def run_split(rnd, tables, t_max: Optional[int] = None):
         lay = olayout.build_layout(sub.requests)
         tables[k].bufs.fill(sub, lay)
         out.append((sub, tables[k], lay))
+    if co_schedule:
+        from tree_forked_hybrid_amd.runner import FrontScheduler
+        FrontScheduler(len(out)).run([tab for _, tab, _ in out], [sub.requests for sub, _, _ in out])
+    else:
+        for sub, tab, _ in out:
+            tab.run(sub.requests)
     for sub, tab, _ in out:
-        bid = tab.run(sub.requests)
         print(f"[gpu] split sub-round: {len(sub.requests)} requests, T={tab.last[1][tab.bufs.layout.hdr]} "
-              f"bucket T_cap={tab.caps_of(bid).T_cap}", flush=True)
+              f"bucket T_cap={tab.caps_of(tab.last[0]).T_cap}", flush=True)
     torch.cuda.synchronize()
     for _, tab, _ in out:
         tab.check()

@@ -166,6 +166,26 @@ def test_split_equals_unsplit_bitwise(ctx):
         _assert_same(a[rid], b[rid], f"request {rid}")
 
 
+def test_coscheduled_fronts_equal_serial_bitwise(ctx):
+    """Twelve short-round requests split for a 2,048-row capacity (four or more sub-rounds), replayed once
+    one sub-round after another and once with every sub-round's front (metadata expansion, trunk GDN call)
+    on a stream of its own and the backs in order (flide_graph_replay_front / _back): every request's
+    outputs are bit-identical."""
+    from tree_forked_hybrid_amd import flide as F
+    rnd = make_round(1, 0, requests=range(12))
+    n_sub = len(F.flide_split_round(rnd.requests, 2048)[1])
+    assert n_sub >= 4
+    outs = []
+    for co in (False, True):
+        tabs = _tables(rnd, n_sub, 2048, 16, 16, t_min=512)
+        try:
+            outs.append(_split_request_outputs(harness.run_split(rnd, tabs, co_schedule=co)))
+        finally:
+            _close(tabs)
+    for rid in outs[0]:
+        _assert_same(outs[0][rid], outs[1][rid], f"request {rid}")
+
+
 def test_same_round_in_two_buckets_bitwise(ctx):
     """One round replayed in the smallest bucket that holds it and in a bucket twice as large: same bits."""
     rnd = make_round(1, 0, requests=range(12))

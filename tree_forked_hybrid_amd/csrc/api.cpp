@@ -34,11 +34,14 @@ struct Staging {
   int next = 0;
 };
 
+// A captured bucket: the round in two graphs, the front (metadata expansion and the trunk GDN call) and the
+// back (the question GDN call, attention, checkpoint K/V, readout), so that the fronts of independent
+// sub-rounds can run side by side (flide_graph_replay_front / _back).
 struct Bucket {
   flide_round_bufs bufs;
   flide_meta_layout L;
-  hipGraph_t graph = nullptr;
-  hipGraphExec_t exec = nullptr;
+  hipGraph_t graph[2] = {nullptr, nullptr};
+  hipGraphExec_t exec[2] = {nullptr, nullptr};
   Staging st;
   bool live = true;  // false once released: the id is never reused, replays of it are rejected
 };
@@ -117,10 +120,12 @@ void staging_free(Staging& st) {
 }
 
 void bucket_free(Bucket* b) {
-  if (b->exec) (void)hipGraphExecDestroy(b->exec);
-  if (b->graph) (void)hipGraphDestroy(b->graph);
-  b->exec = nullptr;
-  b->graph = nullptr;
+  for (int i = 0; i < 2; ++i) {
+    if (b->exec[i]) (void)hipGraphExecDestroy(b->exec[i]);
+    if (b->graph[i]) (void)hipGraphDestroy(b->graph[i]);
+    b->exec[i] = nullptr;
+    b->graph[i] = nullptr;
+  }
   staging_free(b->st);
   b->live = false;
 }
@@ -294,12 +299,20 @@ flide_status enqueue_gdn(flide_ctx* ctx, const MetaView& mv, const flide_gdn_par
                   "fork_gdn");
 }
 
-flide_status enqueue_round(flide_ctx* ctx, const flide_round_bufs* b, hipStream_t stream) {
+// The front of a round: metadata expansion and GDN call 1 (trunks).  Its kernels read the uploaded
+// metadata and the round's inputs and write the expanded metadata, the trunk states, windows and outputs.
+flide_status enqueue_round_front(flide_ctx* ctx, const flide_round_bufs* b, hipStream_t stream) {
   MetaView mv;
   FLIDE_TRY(view_of(ctx, &b->caps, b->dev_meta, &mv));
   FLIDE_TRY(launched(ctx, launch_meta_expand(mv, stream), "meta_expand"));
-  FLIDE_TRY(enqueue_gdn(ctx, mv, b->gdn, 0, b->x, b->conv_w, b->alpha, b->eta, b->state_pool, b->conv_pool,
-                        b->n_slots, b->o_gdn, stream));
+  return enqueue_gdn(ctx, mv, b->gdn, 0, b->x, b->conv_w, b->alpha, b->eta, b->state_pool, b->conv_pool,
+                     b->n_slots, b->o_gdn, stream);
+}
+
+// The back of a round (after its front): GDN call 2 (questions), attention, checkpoint K/V, readout.
+flide_status enqueue_round_back(flide_ctx* ctx, const flide_round_bufs* b, hipStream_t stream) {
+  MetaView mv;
+  FLIDE_TRY(view_of(ctx, &b->caps, b->dev_meta, &mv));
   FLIDE_TRY(enqueue_gdn(ctx, mv, b->gdn, 1, b->x, b->conv_w, b->alpha, b->eta, b->state_pool, b->conv_pool,
                         b->n_slots, b->o_gdn, stream));
   for (int l = 0; l < b->n_attn; ++l) {
@@ -322,6 +335,11 @@ flide_status enqueue_round(flide_ctx* ctx, const flide_round_bufs* b, hipStream_
   return FLIDE_OK;
 }
 
+flide_status enqueue_round(flide_ctx* ctx, const flide_round_bufs* b, hipStream_t stream) {
+  FLIDE_TRY(enqueue_round_front(ctx, b, stream));
+  return enqueue_round_back(ctx, b, stream);
+}
+
 flide_status check_round_bufs(flide_ctx* ctx, const flide_round_bufs* b) {
   if (!b) return fail(ctx, FLIDE_E_INVALID_ARG, "round buffers are NULL");
   flide_meta_layout L;
@@ -331,6 +349,22 @@ flide_status check_round_bufs(flide_ctx* ctx, const flide_round_bufs* b) {
   for (int l = 0; l < b->n_attn; ++l) FLIDE_TRY(check_attn(ctx, &b->attn[l]));
   FLIDE_TRY(check_gdn(ctx, &b->gdn, b->n_slots));
   FLIDE_TRY(check_readout(ctx, &b->ro));
+  return FLIDE_OK;
+}
+
+// parts: 1 = front, 2 = back, 3 = both; the front uploads `image` first
+flide_status graph_replay_parts(flide_ctx* ctx, int32_t bucket_id, const int32_t* image, void* stream, int parts) {
+  if (bucket_id < 0 || size_t(bucket_id) >= ctx->buckets.size() || !ctx->buckets[size_t(bucket_id)]->live)
+    return fail(ctx, FLIDE_E_INVALID_ARG, "no such bucket (never captured, or released)");
+  Bucket* b = ctx->buckets[size_t(bucket_id)];
+  FLIDE_HIP(ctx, hipSetDevice(ctx->device));
+  if (parts & 1) {
+    if (!image) return fail(ctx, FLIDE_E_INVALID_ARG, "image is NULL");
+    FLIDE_TRY(check_image(ctx, b->bufs.caps, b->L, image));
+    FLIDE_TRY(staging_upload(ctx, b->st, image, b->L.host_words, b->bufs.dev_meta, (hipStream_t)stream));
+    FLIDE_HIP(ctx, hipGraphLaunch(b->exec[0], (hipStream_t)stream));
+  }
+  if (parts & 2) FLIDE_HIP(ctx, hipGraphLaunch(b->exec[1], (hipStream_t)stream));
   return FLIDE_OK;
 }
 
@@ -639,31 +673,34 @@ flide_status flide_graph_capture(flide_ctx* ctx, const flide_round_bufs* bufs, v
     b->bufs = *bufs;
     compute_layout(bufs->caps, b->L);
     hipStream_t cs = ctx->capture_stream;
-    hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
-    if (e != hipSuccess) {
-      delete b;
-      return fail_hip(ctx, e, "hipStreamBeginCapture");
+    for (int part = 0; part < 2; ++part) {  // the front, then the back of the round
+      hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+      if (e != hipSuccess) {
+        bucket_free(b);
+        delete b;
+        return fail_hip(ctx, e, "hipStreamBeginCapture");
+      }
+      flide_status st = part == 0 ? enqueue_round_front(ctx, bufs, cs) : enqueue_round_back(ctx, bufs, cs);
+      hipGraph_t g = nullptr;
+      e = hipStreamEndCapture(cs, &g);
+      if (st != FLIDE_OK || e != hipSuccess) {
+        if (g) (void)hipGraphDestroy(g);
+        bucket_free(b);
+        delete b;
+        if (st != FLIDE_OK) return st;
+        return fail_hip(ctx, e, "hipStreamEndCapture");
+      }
+      b->graph[part] = g;
+      e = hipGraphInstantiate(&b->exec[part], g, nullptr, nullptr, 0);
+      if (e != hipSuccess) {
+        bucket_free(b);
+        delete b;
+        return fail_hip(ctx, e, "hipGraphInstantiate");
+      }
     }
-    flide_status st = enqueue_round(ctx, bufs, cs);
-    hipGraph_t g = nullptr;
-    e = hipStreamEndCapture(cs, &g);
-    if (st != FLIDE_OK || e != hipSuccess) {
-      if (g) (void)hipGraphDestroy(g);
-      delete b;
-      if (st != FLIDE_OK) return st;
-      return fail_hip(ctx, e, "hipStreamEndCapture");
-    }
-    b->graph = g;
-    e = hipGraphInstantiate(&b->exec, g, nullptr, nullptr, 0);
-    if (e != hipSuccess) {
-      (void)hipGraphDestroy(g);
-      delete b;
-      return fail_hip(ctx, e, "hipGraphInstantiate");
-    }
-    st = staging_init(ctx, b->st, b->L.host_words);
+    flide_status st = staging_init(ctx, b->st, b->L.host_words);
     if (st != FLIDE_OK) {
-      (void)hipGraphExecDestroy(b->exec);
-      (void)hipGraphDestroy(g);
+      bucket_free(b);
       delete b;
       return st;
     }
@@ -690,20 +727,31 @@ flide_status flide_select_bucket(const flide_ctx* ctx, int32_t T, int32_t R, int
   return FLIDE_OK;
 }
 
+
 flide_status flide_graph_replay(flide_ctx* ctx, int32_t bucket_id, const int32_t* image, void* stream) {
   if (!ctx) return FLIDE_E_INVALID_ARG;
   try {
-    if (bucket_id < 0 || size_t(bucket_id) >= ctx->buckets.size() || !ctx->buckets[size_t(bucket_id)]->live)
-      return fail(ctx, FLIDE_E_INVALID_ARG, "no such bucket (never captured, or released)");
-    if (!image) return fail(ctx, FLIDE_E_INVALID_ARG, "image is NULL");
-    Bucket* b = ctx->buckets[size_t(bucket_id)];
-    FLIDE_TRY(check_image(ctx, b->bufs.caps, b->L, image));
-    FLIDE_HIP(ctx, hipSetDevice(ctx->device));
-    FLIDE_TRY(staging_upload(ctx, b->st, image, b->L.host_words, b->bufs.dev_meta, (hipStream_t)stream));
-    FLIDE_HIP(ctx, hipGraphLaunch(b->exec, (hipStream_t)stream));
-    return FLIDE_OK;
+    return graph_replay_parts(ctx, bucket_id, image, stream, 3);
   } catch (...) {
     return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_graph_replay");
+  }
+}
+
+flide_status flide_graph_replay_front(flide_ctx* ctx, int32_t bucket_id, const int32_t* image, void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    return graph_replay_parts(ctx, bucket_id, image, stream, 1);
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_graph_replay_front");
+  }
+}
+
+flide_status flide_graph_replay_back(flide_ctx* ctx, int32_t bucket_id, void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    return graph_replay_parts(ctx, bucket_id, nullptr, stream, 2);
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_graph_replay_back");
   }
 }
 

@@ -134,6 +134,8 @@ _SIGNATURES = {
     "flide_graph_capture": (C.c_int, [_VP, C.POINTER(flide_round_bufs), _VP, C.POINTER(C.c_int32)]),
     "flide_select_bucket": (C.c_int, [_VP, C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32)]),
     "flide_graph_replay": (C.c_int, [_VP, C.c_int32, C.POINTER(C.c_int32), _VP]),
+    "flide_graph_replay_front": (C.c_int, [_VP, C.c_int32, C.POINTER(C.c_int32), _VP]),
+    "flide_graph_replay_back": (C.c_int, [_VP, C.c_int32, _VP]),
     "flide_graph_release": (C.c_int, [_VP, C.c_int32]),
     "flide_round_eager": (C.c_int, [_VP, C.POINTER(flide_round_bufs), C.POINTER(C.c_int32), _VP]),
     "flide_check_device": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, _VP]),
@@ -499,6 +501,18 @@ def flide_graph_replay(ctx: Context, bucket_id: int, image: np.ndarray, stream=N
     image = np.ascontiguousarray(image, dtype=np.int32)
     _check(load_library().flide_graph_replay(ctx.handle, int(bucket_id), image.ctypes.data_as(C.POINTER(C.c_int32)),
                                              _stream(stream)), "flide_graph_replay", ctx.handle)
+
+
+def flide_graph_replay_front(ctx: Context, bucket_id: int, image: np.ndarray, stream=None) -> None:
+    image = np.ascontiguousarray(image, dtype=np.int32)
+    _check(load_library().flide_graph_replay_front(ctx.handle, int(bucket_id),
+                                                   image.ctypes.data_as(C.POINTER(C.c_int32)), _stream(stream)),
+           "flide_graph_replay_front", ctx.handle)
+
+
+def flide_graph_replay_back(ctx: Context, bucket_id: int, stream=None) -> None:
+    _check(load_library().flide_graph_replay_back(ctx.handle, int(bucket_id), _stream(stream)),
+           "flide_graph_replay_back", ctx.handle)
 
 
 def flide_graph_release(ctx: Context, bucket_id: int) -> None:

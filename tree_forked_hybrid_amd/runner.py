@@ -328,6 +328,17 @@ class BucketTable:
         self.last = (bid, img)
         return bid
 
+    def run_front(self, requests, stream=None, bid: Optional[int] = None) -> int:
+        """Plan the round, upload its metadata and replay the front of its bucket (metadata expansion and the
+        trunk GDN call); run_back replays the rest."""
+        bid, img = self.plan(F.Requests(requests), bid)
+        F.flide_graph_replay_front(self.ctx, bid, img, stream)
+        self.last = (bid, img)
+        return bid
+
+    def run_back(self, stream=None) -> None:
+        F.flide_graph_replay_back(self.ctx, self.last[0], stream)
+
     def caps_of(self, bid: int) -> F.flide_caps:
         return self.buckets[bid][0]
 
@@ -369,6 +380,34 @@ class SplitExecutor:
 
     def table_of(self, k: int) -> BucketTable:
         return self.tables[k % len(self.tables)]
+
+
+class FrontScheduler:
+    """The sub-rounds of one split round, each in a bucket table of its own: every front (metadata upload and
+    expansion, GDN call 1) on a side stream of its own, all ordered after the work already on the launch
+    stream, then the backs (GDN call 2, attention, readout) one after another on the launch stream, each
+    after its own front.  A sub-round's trunk call fills only as many CUs as it has (segment, head) pairs
+    (96 of 256 on a fan-out sub-round), so the trunk calls of the sub-rounds run side by side; the attention
+    launches, which fill the GPU, stay in order (side by side they slow each other down).  The next round's
+    fronts wait for this round's backs, which read the same buffers."""
+
+    def __init__(self, n: int):
+        self.side = [torch.cuda.Stream() for _ in range(n)]
+        self.start = torch.cuda.Event()
+        self.done = [torch.cuda.Event() for _ in range(n)]
+
+    def run(self, tables: Sequence[BucketTable], sub_requests, stream=None) -> None:
+        assert len(tables) == len(sub_requests) <= len(self.side)
+        assert len({id(t) for t in tables}) == len(tables), "each sub-round needs a table of its own"
+        main = stream if stream is not None else torch.cuda.current_stream()
+        self.start.record(main)
+        for k, (tab, reqs) in enumerate(zip(tables, sub_requests)):
+            self.side[k].wait_event(self.start)
+            tab.run_front(reqs, stream=self.side[k])
+            self.done[k].record(self.side[k])
+        for k, tab in enumerate(tables):
+            main.wait_event(self.done[k])
+            tab.run_back(stream=main)
 
 
 class StackRunner:
