@@ -13,7 +13,7 @@
 // chunks of a segment.  Chunks start at multiples of 64 rows from the segment
 // start, so a segment's arithmetic never depends on the rest of the round.
 //
-// Workgroup = (segment, head), 8 waves, two workgroups per CU.  Wave w owns
+// Workgroup = (segment, head), 8 waves, one workgroup per CU (140 KB of LDS).  Wave w owns
 // value channels [16w, 16w + 16) and the matching 16 rows of S, which stay in
 // registers for the whole segment in the layout the next chunk's MFMA needs as
 // its B operand.  Everything that depends on those channels (the values' conv,
