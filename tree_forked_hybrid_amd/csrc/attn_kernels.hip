@@ -316,6 +316,11 @@ __device__ __forceinline__ void lds_wait(u32x4v& r) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
 }
 // f(integral_constant<int, I>) for I = B .. E - 1, in order (compile-time indices for the reads above).
+// acc + lo + hi of a pair of bf16 values (one dot-product instruction against (1, 1))
+__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, pair), __builtin_bit_cast(bf16x2v, 0x3f803f80u),
+                                         acc, false);
+}
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (B < E) {
@@ -446,6 +451,9 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   // with four heads a wave holds 8 rows, and a wave whose rows all lie past the tile's last row (short
   // question tiles) skips the key loop's arithmetic.
   const bool active = w < ng && (32 * w) / ng < nrows;
+  // the same flag as a scalar integer: tested once per key tile, where a boolean would be rebuilt from a
+  // lane mask with vector instructions
+  const int active_s = __builtin_amdgcn_readfirstlane(int(active));
   const int64_t VT = vt_cols(mv.T_cap, mv.seg_cap);
   const int lo_w = window > 0 ? qpos_min - window + 1 : INT_MIN;
 
@@ -462,31 +470,32 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   const int n2 = lo2 < hi2 ? (hi2 - ts02 + BN - 1) / BN : 0;
   const int n_tiles = n0 + n1 + n2;
   // A cursor walks the key tiles in order: range rg (0, 1, 2 as above), tile start ts (a position) and the
-  // byte addresses of the tile's first key row (kp) and first value column (vp), advanced by one tile's
-  // stride; the range's parameters are looked up only when the cursor enters it.  Every field is uniform
-  // across the workgroup.
+  // byte addresses of the tile's first key row (kp) and of the first value column of this wave's first
+  // value row (vp), advanced by one tile's stride; vrow is the byte stride of value rows.  The range's
+  // parameters are looked up only when the cursor enters it.  Every field is uniform across the wave.
   struct Cursor {
-    int rg, ts, lo, hi, vstride;
+    int rg, ts, lo, hi, vrow;
     const unsigned char* kp;
     const unsigned char* vp;
   };
   auto range_start = [&](int rg) {
     Cursor c;
     c.rg = rg;
-    int64_t roff, voff;
+    int64_t roff, voff, vstride;
     const bf16_t *kbase, *vbase;
     if (rg == 0) {
-      c.ts = ts00, c.lo = lo0, c.hi = hi0, roff = roff0, voff = 0, c.vstride = cache_rows;
+      c.ts = ts00, c.lo = lo0, c.hi = hi0, roff = roff0, voff = 0, vstride = cache_rows;
       kbase = k_cache + int64_t(kvh) * D;
       vbase = v_cache + (int64_t(ckpt) * Hkv + kvh) * D * cache_rows;
     } else {
       c.ts = rg == 1 ? ts01 : ts02, c.lo = rg == 1 ? lo1 : lo2, c.hi = rg == 1 ? hi1 : hi2;
-      roff = rg == 1 ? roff1 : roff2, voff = rg == 1 ? voff1 : voff2, c.vstride = int(VT);
+      roff = rg == 1 ? roff1 : roff2, voff = rg == 1 ? voff1 : voff2, vstride = VT;
       kbase = k_rot + int64_t(kvh) * D;
       vbase = vt + int64_t(kvh) * D * VT;
     }
+    c.vrow = int(2 * vstride);
     c.kp = reinterpret_cast<const unsigned char*>(kbase + (int64_t(c.ts) + roff) * Hkv * D);
-    c.vp = reinterpret_cast<const unsigned char*>(vbase + (int64_t(c.ts) + voff));
+    c.vp = reinterpret_cast<const unsigned char*>(vbase + (int64_t(c.ts) + voff + w * IPW * 16 * vstride));
     return c;
   };
   // the next tile (called only while one is left: the ranges hold n_tiles tiles in all)
@@ -511,27 +520,37 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   }
   const int vc = (l & 3) ^ vsw(l >> 2);
   auto issue = [&](const Cursor& c, int buf) {
-    const int ts = c.ts, lo = c.lo, hi = c.hi, vstride = c.vstride;
+    const int ts = c.ts, lo = c.lo, hi = c.hi, vrow = c.vrow;
     const bool edge = ts < lo || ts + BN > hi;
     unsigned char* kl = lds + buf * TILE_BYTES;
     unsigned char* vl = lds + (2 + buf) * TILE_BYTES;
     int lv = l;
     asm volatile("" : "+v"(lv));  // recomputed per tile: registers are scarce in the key-tile loop
-    const int voff0 = (((w * IPW * 16) + (lv >> 2)) * vstride + 8 * vc) * 2;
+    // the fixed key offsets are kept as 32-bit values inside the loop (which keeps the copies in their
+    // scalar-base form instead of 64-bit lane addresses)
+#pragma unroll
+    for (int ii = 0; ii < KP; ++ii) asm volatile("" : "+v"(k_off0[ii]));
     // both offsets are >= 0 (clamped rows and chunks stay inside the range): 32-bit unsigned offsets
     // from a scalar base
-    if (!edge) {  // interior tile: fixed lane offsets
+    if (!edge) {
+      // Interior tile: every per-instruction term goes into the scalar base, so the lane offsets are the
+      // fixed key offsets and one value offset per tile.
+      const uint32_t vlane = __umul24(uint32_t(lv >> 2), uint32_t(vrow)) + uint32_t(16 * vc);
 #pragma unroll
       for (int ii = 0; ii < IPW; ++ii) {
-        async_copy16(c.kp + uint32_t(k_off0[ii % KP] + (ii / KP) * 4 * Hkv * D * 2), kl + (w * IPW + ii) * 1024);
-        async_copy16(c.vp + uint32_t(voff0 + ii * 16 * vstride * 2), vl + (w * IPW + ii) * 1024);
+        const unsigned char* kb = c.kp + uint32_t((ii / KP) * 4 * Hkv * D * 2);
+        const unsigned char* vb = c.vp + uint32_t(ii * 16 * vrow);
+        async_copy16(kb + uint32_t(k_off0[ii % KP]), kl + (w * IPW + ii) * 1024);
+        async_copy16(vb + vlane, vl + (w * IPW + ii) * 1024);
       }
+      asm volatile("");  // keeps this path's last copy out of a tail shared with the edge path
       return;
     }
+    const int voff0 = (lv >> 2) * vrow + 16 * vc;
 #pragma unroll
     for (int ii = 0; ii < IPW; ++ii) {  // masked keys read a valid row / value chunk of the range
       int koff = k_off0[ii % KP] + (ii / KP) * 4 * Hkv * D * 2;
-      int voff = voff0 + ii * 16 * vstride * 2;
+      int voff = voff0 + ii * 16 * vrow;
       const int p = ts + ((w * IPW + ii) * 64 + lv) / KCH;
       const int pc = p < lo ? lo : (p >= hi ? hi - 1 : p);
       koff += (pc - p) * Hkv * D * 2;
@@ -645,7 +664,7 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
       advance(cur);
       issue(cur, BUF ^ 1);
     }
-    if (!active) return;
+    if (!active_s) return;
     // lane addresses of the operand reads (the array is 1024-byte aligned, so the chunk XOR of bits
     // 6-7 commutes with adding its base); tile, buffer and block offsets are instruction immediates
     int kf = kfrag0;
@@ -715,18 +734,17 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
         m_run[qb] = m_new;
       }
       const float m_use = m_run[qb];
-      float rs;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(s[kb][qb][i] - m_use);
-          s[kb][qb][i] = pv;
-          rs = kb == 0 && i == 0 ? pv : rs + pv;
-        }
-      l_run[qb] += rs;  // this lane's 8 keys; the four lanes of a column are summed once, at the end
+        for (int i = 0; i < 4; ++i) s[kb][qb][i] = __builtin_amdgcn_exp2f(s[kb][qb][i] - m_use);
       pf[qb] = u32x4v{pack_bf16x2(s[0][qb][0], s[0][qb][1]), pack_bf16x2(s[0][qb][2], s[0][qb][3]),
                       pack_bf16x2(s[1][qb][0], s[1][qb][1]), pack_bf16x2(s[1][qb][2], s[1][qb][3])};
+      // The column's sum takes the bf16 weights the output products use (so the weights of a column
+      // sum to one up to fp32 rounding), two per instruction: this lane's 8 keys; the four lanes of a
+      // column are summed once, at the end.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l_run[qb] = add_bf16_pair(pf[qb][i], l_run[qb]);
     }
     // O^T += V^T P^T over the tile's 32 keys (lane k-slots 8 g4 .. +7 = keys 8 g4 .. +7)
     static_for<0, NDB>([&](auto DB) {
