@@ -302,15 +302,34 @@ flide_status flide_plan_round(const flide_request* reqs, int32_t R, const flide_
             t_seg[k * kXcdClasses + size_t(c)] = cls[c][k].seg;
             t_row[k * kXcdClasses + size_t(c)] = cls[c][k].row0;
           }
-      } else {  // unbalanced classes: one list, heaviest first, without XCD affinity
+      } else {
+        // Unbalanced classes (a few large requests): one list, heaviest first, cut into bands of
+        // kXcdClasses x kLongTileGroup tiles of similar cost.  Within a band the tiles are ordered by
+        // request and dealt to the classes in runs of up to kLongTileGroup, so each XCD takes a
+        // request-contiguous run of each band while every XCD gets an equal share of every band.
+        // With the tile-group order the workgroups resident on an XCD then read one request's keys for
+        // one kv head (fan-out round, measured on MI355X in the design notes).
         std::vector<Tile> all;
         for (auto& v : cls) all.insert(all.end(), v.begin(), v.end());
         std::stable_sort(all.begin(), all.end(), [](const Tile& x, const Tile& y) { return x.cost > y.cost; });
-        n_tiles = int32_t(all.size());
-        for (int32_t x = 0; x < n_tiles; ++x) {
-          t_seg[x] = all[size_t(x)].seg;
-          t_row[x] = all[size_t(x)].row0;
+        const size_t band = size_t(kXcdClasses) * kLongTileGroup;
+        size_t k0 = 0;  // first class index of the band
+        n_tiles = 0;
+        for (size_t b0 = 0; b0 < all.size(); b0 += band) {
+          const size_t nb = std::min(band, all.size() - b0);
+          const size_t per = (nb + kXcdClasses - 1) / kXcdClasses;  // positions per class in this band
+          std::stable_sort(all.begin() + b0, all.begin() + b0 + nb,
+                           [&](const Tile& x, const Tile& y) { return s_req[x.seg] < s_req[y.seg]; });
+          for (size_t k = 0; k < per * kXcdClasses; ++k) {
+            const size_t x = (k0 + k % per) * kXcdClasses + k / per;
+            t_seg[x] = k < nb ? all[b0 + k].seg : -1;
+            t_row[x] = k < nb ? all[b0 + k].row0 : 0;
+          }
+          k0 += per;
         }
+        n_tiles = int32_t(k0) * kXcdClasses;
+        if (n_tiles > L.tile_cap) return FLIDE_E_INTERNAL;
+        if (total >= kLongTileKeys * n_all) tile_group = kLongTileGroup;
       }
     }
     // GDN work list: trunk segments, then question segments, each longest first (ties in stream
