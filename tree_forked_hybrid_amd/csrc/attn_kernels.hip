@@ -176,15 +176,21 @@ __device__ __forceinline__ f32x4v mfma16x16x32(u32x4v a, u32x4v b, f32x4v c) {
 // Two floats to two bf16 (round to nearest even) in one hardware conversion.
 
 // Columns of the transposed value workspace per (kv head, channel): the stream
-// capacity plus up to 7 alignment columns per segment, rounded up.
+// capacity plus up to 31 alignment columns per segment, rounded up to whole blocks.
 __host__ __device__ __forceinline__ int64_t vt_cols(int T_cap, int seg_cap) {
-  return ((int64_t(T_cap) + 8 * int64_t(seg_cap) + 64 + 63) / 64) * 64;
+  return ((int64_t(T_cap) + 32 * int64_t(seg_cap) + 64 + 63) / 64) * 64;
+}
+// Tile-major transposed values: vt [Hkv, vt_cols / 32, D, 32] -- column block b of kv head g holds, per
+// channel, the 32 values of columns 32 b .. 32 b + 31 -- so the value tile of 32 positions is one
+// contiguous D x 64-byte block.  Element index of (kv head g, channel dd, column col):
+__host__ __device__ __forceinline__ int64_t vt_index(int g, int dd, int64_t col, int D, int64_t VT) {
+  return ((int64_t(g) * (VT / 32) + (col >> 5)) * D + dd) * 32 + (col & 31);
 }
 
 // Prep pass of the MFMA path: rotate every key row once (rotate-half pairs at
 // the row's metadata position) into k_rot [T_cap, Hkv, D], and write the values
-// transposed into vt [Hkv, D, vt_cols]; the value of position p of segment s
-// lands in column seg_vcol0[s] + p, so 8-aligned positions are 16-byte aligned.
+// transposed and tile-major into vt (vt_index); the value of position p of segment s
+// lands in column seg_vcol0[s] + p, so 32-aligned positions start a column block.
 //
 // One workgroup = 64 rows of one kv head.  Every load of a thread is issued before the first use
 // (value rows, key rows and positions, then the rotation table rows at those positions), so a
@@ -283,8 +289,8 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(MetaView mv, const bf16_t*
   __syncthreads();
   if (col < 0) return;
   const int64_t VT = vt_cols(mv.T_cap, mv.seg_cap);
-  bf16_t* dst = vt + int64_t(g) * D * VT + col;
-  for (int dd = w; dd < D; dd += 4) dst[int64_t(dd) * VT] = v_lds[lane * STR + dd];
+  bf16_t* dst = vt + vt_index(g, 0, col, D, VT);
+  for (int dd = w; dd < D; dd += 4) dst[dd * 32] = v_lds[lane * STR + dd];
 }
 
 typedef __attribute__((address_space(3))) void* lds_vptr_t;
@@ -471,38 +477,36 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   const int n_tiles = n0 + n1 + n2;
   // A cursor walks the key tiles in order: range rg (0, 1, 2 as above), tile start ts (a position) and the
   // byte addresses of the tile's first key row (kp) and of the first value column of this wave's first
-  // value row (vp), advanced by one tile's stride; vrow is the byte stride of value rows.  The range's
+  // value row (vp), advanced by one tile's stride (vstep for values); vrow is the byte stride of value
+  // rows: the checkpoint cache holds whole transposed rows, the workspace one 64-byte row per block.  The range's
   // parameters are looked up only when the cursor enters it.  Every field is uniform across the wave.
   struct Cursor {
-    int rg, ts, lo, hi, vrow;
+    int rg, ts, lo, hi, vrow, vstep;
     const unsigned char* kp;
     const unsigned char* vp;
   };
   auto range_start = [&](int rg) {
     Cursor c;
     c.rg = rg;
-    int64_t roff, voff, vstride;
-    const bf16_t *kbase, *vbase;
-    if (rg == 0) {
-      c.ts = ts00, c.lo = lo0, c.hi = hi0, roff = roff0, voff = 0, vstride = cache_rows;
-      kbase = k_cache + int64_t(kvh) * D;
-      vbase = v_cache + (int64_t(ckpt) * Hkv + kvh) * D * cache_rows;
-    } else {
+    if (rg == 0) {  // checkpoint cache: keys [slot rows, Hkv, D], values [slot, Hkv, D, cache_rows]
+      c.ts = ts00, c.lo = lo0, c.hi = hi0, c.vrow = 2 * cache_rows, c.vstep = BN * 2;
+      c.kp = reinterpret_cast<const unsigned char*>(k_cache + int64_t(kvh) * D + (int64_t(c.ts) + roff0) * Hkv * D);
+      c.vp = reinterpret_cast<const unsigned char*>(v_cache + (int64_t(ckpt) * Hkv + kvh) * D * cache_rows +
+                                                    int64_t(c.ts) + int64_t(w * IPW * 16) * cache_rows);
+    } else {  // workspace: rotated keys, tile-major values (ts + voff is a multiple of 32)
       c.ts = rg == 1 ? ts01 : ts02, c.lo = rg == 1 ? lo1 : lo2, c.hi = rg == 1 ? hi1 : hi2;
-      roff = rg == 1 ? roff1 : roff2, voff = rg == 1 ? voff1 : voff2, vstride = VT;
-      kbase = k_rot + int64_t(kvh) * D;
-      vbase = vt + int64_t(kvh) * D * VT;
+      const int64_t roff = rg == 1 ? roff1 : roff2, voff = rg == 1 ? voff1 : voff2;
+      c.vrow = BN * 2, c.vstep = D * BN * 2;
+      c.kp = reinterpret_cast<const unsigned char*>(k_rot + int64_t(kvh) * D + (int64_t(c.ts) + roff) * Hkv * D);
+      c.vp = reinterpret_cast<const unsigned char*>(vt + vt_index(kvh, w * IPW * 16, int64_t(c.ts) + voff, D, VT));
     }
-    c.vrow = int(2 * vstride);
-    c.kp = reinterpret_cast<const unsigned char*>(kbase + (int64_t(c.ts) + roff) * Hkv * D);
-    c.vp = reinterpret_cast<const unsigned char*>(vbase + (int64_t(c.ts) + voff + w * IPW * 16 * vstride));
     return c;
   };
   // the next tile (called only while one is left: the ranges hold n_tiles tiles in all)
   auto advance = [&](Cursor& c) {
     c.ts += BN;
     c.kp += int64_t(BN) * Hkv * D * 2;
-    c.vp += BN * 2;
+    c.vp += c.vstep;
     if (__builtin_expect(c.ts >= c.hi, 0)) c = range_start(c.rg == 0 && n1 > 0 ? 1 : 2);
   };
   // Lane constants of the copies: wave w issues copy instructions I = w*IPW + ii; lane l of
@@ -871,19 +875,20 @@ __global__ void __launch_bounds__(256) attn_save_kv_kernel(MetaView mv, const T*
   }
   auto value_at = [&](int dd, int t) {
     if (t < m) return v_cache[((int64_t(ck) * Hkv + g) * D + dd) * cache_rows + t];
-    if (TRANSPOSED_V) return vsrc[(int64_t(g) * D + dd) * VT + vcol0 + t];
+    if (TRANSPOSED_V) return vsrc[vt_index(g, dd, vcol0 + t, D, VT)];
     return vsrc[((row0 + t - m) * Hkv + g) * D + dd];
   };
   // values: a row per channel, position fastest; a whole 16-byte piece of positions on one side of m is
   // one copy when both sides are transposed rows (piece starts are multiples of 8 positions: 16-byte
-  // aligned in the cache and, with 8-aligned segment columns, in the workspace), else element by element
+  // aligned in the cache and, with segment columns congruent to positions modulo 32, inside one column
+  // block of the workspace), else element by element
   const int cpc = (np + EPC - 1) / EPC;
   for (int c = threadIdx.x; c < D * cpc; c += 256) {
     const int dd = c / cpc, t0 = p0 + (c % cpc) * EPC, n = min(EPC, p0 + np - t0);
     T* dst = v_cache + ((int64_t(slot) * Hkv + g) * D + dd) * cache_rows + t0;
     if (TRANSPOSED_V && n == EPC && (t0 + EPC <= m || t0 >= m)) {
       const T* src = t0 < m ? v_cache + ((int64_t(ck) * Hkv + g) * D + dd) * cache_rows + t0
-                            : vsrc + (int64_t(g) * D + dd) * VT + vcol0 + t0;
+                            : vsrc + vt_index(g, dd, vcol0 + t0, D, VT);
       *reinterpret_cast<u32x4v*>(dst) = *reinterpret_cast<const u32x4v*>(src);
     } else {
       for (int e = 0; e < n; ++e) dst[e] = value_at(dd, t0 + e);

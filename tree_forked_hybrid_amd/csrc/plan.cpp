@@ -206,14 +206,14 @@ flide_status flide_plan_round(const flide_request* reqs, int32_t R, const flide_
         max_pos = std::max(max_pos, r.P + r.q_len[i]);
       }
     }
-    // Columns of the transposed value workspace: every segment starts at the
-    // first free column congruent to its first position modulo 8, so value tiles
-    // aligned in position space are 16-byte aligned in memory.
+    // Columns of the transposed value workspace: every segment starts at the first free column
+    // congruent to its first position modulo 32, so a value tile aligned in position space (32
+    // positions) is exactly one 32-column block of the tile-major workspace.
     {
       int64_t vend = 0;
       for (int32_t s = 0; s < seg; ++s) {
         const int64_t pos0 = s_pos[s];
-        const int64_t vstart = vend + (((pos0 - vend) % 8) + 8) % 8;
+        const int64_t vstart = vend + (((pos0 - vend) % 32) + 32) % 32;
         s_vc[s] = int32_t(vstart - pos0);
         vend = vstart + s_len[s];
       }
