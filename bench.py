@@ -377,8 +377,8 @@ def main():
                     help="GDN chunk boundaries on the stream's 64-row grid (bits then depend on the round's "
                          "composition); the default is the composition-independent mode")
     ap.add_argument("--serial-subrounds", action="store_true",
-                    help="replay the sub-rounds of a split round one after another (the default runs their fronts "
-                         "— metadata expansion and the trunk GDN call — side by side, runner.FrontScheduler)")
+                    help="replay every sub-round on the launch stream, one after another (the default lets "
+                         "runner.FrontScheduler run trunk GDN calls beside other work)")
     ap.add_argument("--stack", action="store_true",
                     help="time the multi-layer hybrid stack instead of the ForkAttention round (its own JSON line)")
     args = ap.parse_args()
@@ -423,10 +423,10 @@ def main():
         print(f"[bench] sub-round {k}: {len(sub.requests)} requests, bucket T_cap {tab.caps_of(bid).T_cap}",
               flush=True)
     sub_reqs = [s.requests for s in subs]
-    # The sub-rounds' fronts (metadata upload and expansion, trunk GDN call) run side by side, each on a
-    # stream of its own; the backs (question GDN call, attention, readout) follow in order on the launch
-    # stream (a single sub-round: front and back on the launch stream).
-    co_schedule = len(tables) > 1 and not args.serial_subrounds
+    # runner.FrontScheduler picks the schedule: trunk GDN calls beside the attention when they are small,
+    # else the sub-rounds' fronts side by side and the backs in order (a single sub-round: in order).
+    # --serial-subrounds replays every sub-round on the launch stream, one after another.
+    co_schedule = not args.serial_subrounds
     sched = FrontScheduler(len(tables)) if co_schedule else None
 
     def step():
@@ -592,7 +592,7 @@ def main():
                    "questions": sum(len(r.q_len) for r in rnd.requests),
                    "bucket_table_T_caps": [c.T_cap for c in caps_table], "seed": args.seed,
                    "deterministic": spec.deterministic,
-                   "subround_fronts": "side by side" if co_schedule else "in order"},
+                   "schedule": sched.last_mode if sched is not None else "in order"},
         "round_latency_ms": {"p10": round(lat_ms[len(lat_ms) // 10], 4), "median": round(lat_ms[len(lat_ms) // 2], 4),
                              "p90": round(lat_ms[(9 * len(lat_ms)) // 10], 4)},
         "per_layer_tokens_per_s": {

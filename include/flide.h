@@ -503,8 +503,8 @@ typedef struct {
 
 /* Capture the whole round (metadata expansion, GDN phases 0 and 1, attention
  * layers, the checkpoint K/V of requests with save_m > 0 when the layer has a
- * K/V cache, readout) into HIP graphs (the front and back halves of
- * flide_graph_replay_front / _back) for capacity bufs->caps.  Launch shapes
+ * K/V cache, readout) into HIP graphs (the four parts of
+ * flide_graph_replay_parts) for capacity bufs->caps.  Launch shapes
  * depend only on the capacity; kernels read their work from the metadata.
  * *bucket_id receives the bucket's id.  Errors: FLIDE_E_INVALID_ARG,
  * FLIDE_E_UNSUPPORTED, FLIDE_E_HIP.                                           */
@@ -520,18 +520,24 @@ flide_status flide_select_bucket(const flide_ctx* ctx, int32_t T, int32_t R, int
  * FLIDE_E_CAPACITY (image planned for larger caps), FLIDE_E_HIP. */
 flide_status flide_graph_replay(flide_ctx* ctx, int32_t bucket_id, const int32_t* image, void* stream);
 /* Infrastructure (scheduling of the request-boundary sub-rounds of [KO]
- * §어떻게 쓰나).  The captured round in two halves: the front (metadata
- * expansion and GDN call 1, the trunks) and the back (GDN call 2, attention,
- * checkpoint K/V, readout).  flide_graph_replay_front uploads `image` as
- * flide_graph_replay does and launches the front on `stream`;
- * flide_graph_replay_back launches the back on `stream`.  Front then back of
- * one bucket, in that order, is exactly flide_graph_replay; the caller orders
- * the back after the front (the same stream, or an event) and the next front
- * of the bucket after the back.  Fronts of different buckets (different
- * buffers) may run side by side: a sub-round's trunk call alone fills only as
- * many CUs as it has (segment, head) pairs.
- * Errors: FLIDE_E_INVALID_ARG (no such or released bucket, NULL image),
- * FLIDE_E_CAPACITY (image planned for larger caps), FLIDE_E_HIP.            */
+ * §어떻게 쓰나).  The captured round in four parts: 0 metadata expansion,
+ * 1 GDN call 1 (the trunks), 2 attention and checkpoint K/V, 3 GDN call 2
+ * (the questions) and the readout.  flide_graph_replay_parts launches the
+ * parts whose bit is set in `parts` (bit i = part i, 1 .. 15), in part order,
+ * on `stream`; with bit 0 it first uploads `image` as flide_graph_replay does
+ * (image is ignored otherwise).  All four in order is exactly
+ * flide_graph_replay.  The caller orders parts 1 and 2 after part 0, part 3
+ * after part 1 (the same stream, or events), and the next round's part 0 of
+ * the bucket after every part of this one; parts 1 and 2 of one bucket may
+ * run side by side, and so may parts of different buckets (different
+ * buffers): a sub-round's trunk call alone fills only as many CUs as it has
+ * (segment, head) pairs.  flide_graph_replay_front is parts 0 and 1 (the
+ * front), flide_graph_replay_back parts 2 and 3 (the back).
+ * Errors: FLIDE_E_INVALID_ARG (no such or released bucket, parts out of
+ * range, NULL image with bit 0), FLIDE_E_CAPACITY (image planned for larger
+ * caps), FLIDE_E_HIP.                                                        */
+flide_status flide_graph_replay_parts(flide_ctx* ctx, int32_t bucket_id, const int32_t* image, int32_t parts,
+                                      void* stream);
 flide_status flide_graph_replay_front(flide_ctx* ctx, int32_t bucket_id, const int32_t* image, void* stream);
 flide_status flide_graph_replay_back(flide_ctx* ctx, int32_t bucket_id, void* stream);
 /* Infrastructure (the capacity buckets of [KO] §어떻게 쓰나 are captured at

@@ -83,8 +83,8 @@ def run_gpu(rnd, ctx, mode: str = "direct", spec=None, bufs=None, repeats: int =
 def run_split(rnd, tables, t_max: Optional[int] = None, co_schedule: bool = False):
     """Run ``rnd`` through bucket tables: split at request boundaries for the tables' largest capacity (or
     ``t_max``), sub-round k filled into table k mod len(tables) (placement by the oracle's layout) and all
-    sub-rounds replayed back to back, each in the smallest bucket that holds it (co_schedule: the fronts of
-    the sub-rounds side by side on streams of their own, runner.FrontScheduler).  Tables must not be reused
+    sub-rounds replayed back to back, each in the smallest bucket that holds it (co_schedule: True lets
+    runner.FrontScheduler choose its schedule, "overlap" forces the trunk GDN calls beside the attention).  Tables must not be reused
     within one call (len(tables) >= number of sub-rounds).  Returns [(sub-round, table, layout)]."""
     import torch
     from tree_forked_hybrid_amd import flide as F
@@ -99,7 +99,9 @@ def run_split(rnd, tables, t_max: Optional[int] = None, co_schedule: bool = Fals
         out.append((sub, tables[k], lay))
     if co_schedule:
         from tree_forked_hybrid_amd.runner import FrontScheduler
-        FrontScheduler(len(out)).run([tab for _, tab, _ in out], [sub.requests for sub, _, _ in out])
+        sched = FrontScheduler(len(out), overlap_attention=True if co_schedule == "overlap" else None)
+        sched.run([tab for _, tab, _ in out], [sub.requests for sub, _, _ in out])
+        print(f"[gpu] schedule: {sched.last_mode}", flush=True)
     else:
         for sub, tab, _ in out:
             tab.run(sub.requests)

@@ -168,15 +168,16 @@ def test_split_equals_unsplit_bitwise(ctx):
 
 def test_coscheduled_fronts_equal_serial_bitwise(ctx):
     """Twelve short-round requests split for a 2,048-row capacity (four or more sub-rounds), replayed once
-    one sub-round after another and once with every sub-round's front (metadata expansion, trunk GDN call)
-    on a stream of its own and the backs in order (flide_graph_replay_front / _back): every request's
-    outputs are bit-identical."""
+    one sub-round after another, once with every sub-round's front (metadata expansion, trunk GDN call)
+    on a stream of its own and the backs in order (flide_graph_replay_front / _back), and once with the
+    trunk calls on side streams beside the attention (flide_graph_replay_parts): every request's outputs
+    are bit-identical."""
     from tree_forked_hybrid_amd import flide as F
     rnd = make_round(1, 0, requests=range(12))
     n_sub = len(F.flide_split_round(rnd.requests, 2048)[1])
     assert n_sub >= 4
     outs = []
-    for co in (False, True):
+    for co in (False, True, "overlap"):
         tabs = _tables(rnd, n_sub, 2048, 16, 16, t_min=512)
         try:
             outs.append(_split_request_outputs(harness.run_split(rnd, tabs, co_schedule=co)))
@@ -184,6 +185,23 @@ def test_coscheduled_fronts_equal_serial_bitwise(ctx):
             _close(tabs)
     for rid in outs[0]:
         _assert_same(outs[0][rid], outs[1][rid], f"request {rid}")
+        _assert_same(outs[0][rid], outs[2][rid], f"request {rid} (trunk calls beside attention)")
+
+
+def test_graph_replay_parts_rejects_bad_masks(ctx):
+    """flide_graph_replay_parts takes masks 1 .. 15, and part 0 (the upload) needs an image: the host checks
+    reject the rest before anything is launched."""
+    from tree_forked_hybrid_amd import flide as F
+    rnd = make_round(1, 0, requests=range(2))
+    (tab,) = _tables(rnd, 1, 2048, 8, 8, t_min=2048)
+    try:
+        bid = next(iter(tab.buckets))
+        for parts, image in ((0, None), (16, None), (-1, None), (1, None)):
+            with pytest.raises(F.FlideError) as e:
+                F.flide_graph_replay_parts(tab.ctx, bid, image, parts)
+            assert e.value.status == F.FLIDE_E_INVALID_ARG
+    finally:
+        _close([tab])
 
 
 def test_same_round_in_two_buckets_bitwise(ctx):

@@ -34,14 +34,16 @@ struct Staging {
   int next = 0;
 };
 
-// A captured bucket: the round in two graphs, the front (metadata expansion and the trunk GDN call) and the
-// back (the question GDN call, attention, checkpoint K/V, readout), so that the fronts of independent
-// sub-rounds can run side by side (flide_graph_replay_front / _back).
+// A captured bucket: the round in four graphs (parts), replayed in part order or split over streams:
+// 0 metadata expansion, 1 the trunk GDN call, 2 attention and checkpoint K/V, 3 the question GDN call and
+// the readout.  Parts 1 and 2 read only the expanded metadata and the round's inputs, so a caller may run
+// them side by side; part 3 needs part 1 (flide_graph_replay_parts).
+constexpr int kRoundParts = 4;
 struct Bucket {
   flide_round_bufs bufs;
   flide_meta_layout L;
-  hipGraph_t graph[2] = {nullptr, nullptr};
-  hipGraphExec_t exec[2] = {nullptr, nullptr};
+  hipGraph_t graph[kRoundParts] = {};
+  hipGraphExec_t exec[kRoundParts] = {};
   Staging st;
   bool live = true;  // false once released: the id is never reused, replays of it are rejected
 };
@@ -120,7 +122,7 @@ void staging_free(Staging& st) {
 }
 
 void bucket_free(Bucket* b) {
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kRoundParts; ++i) {
     if (b->exec[i]) (void)hipGraphExecDestroy(b->exec[i]);
     if (b->graph[i]) (void)hipGraphDestroy(b->graph[i]);
     b->exec[i] = nullptr;
@@ -299,22 +301,25 @@ flide_status enqueue_gdn(flide_ctx* ctx, const MetaView& mv, const flide_gdn_par
                   "fork_gdn");
 }
 
-// The front of a round: metadata expansion and GDN call 1 (trunks).  Its kernels read the uploaded
-// metadata and the round's inputs and write the expanded metadata, the trunk states, windows and outputs.
-flide_status enqueue_round_front(flide_ctx* ctx, const flide_round_bufs* b, hipStream_t stream) {
+// One part of a round (the parts of a captured bucket, in order):
+//   0  metadata expansion (reads the uploaded image, writes the per-row and per-tile metadata);
+//   1  GDN call 1, trunks (writes the trunk states, windows and outputs);
+//   2  attention and interior checkpoint K/V (reads the expanded metadata and the round's q, k, v);
+//   3  GDN call 2, questions (reads part 1's states by slot index), then the readout.
+flide_status enqueue_round_part(flide_ctx* ctx, const flide_round_bufs* b, int part, hipStream_t stream) {
   MetaView mv;
   FLIDE_TRY(view_of(ctx, &b->caps, b->dev_meta, &mv));
-  FLIDE_TRY(launched(ctx, launch_meta_expand(mv, stream), "meta_expand"));
-  return enqueue_gdn(ctx, mv, b->gdn, 0, b->x, b->conv_w, b->alpha, b->eta, b->state_pool, b->conv_pool,
-                     b->n_slots, b->o_gdn, stream);
-}
-
-// The back of a round (after its front): GDN call 2 (questions), attention, checkpoint K/V, readout.
-flide_status enqueue_round_back(flide_ctx* ctx, const flide_round_bufs* b, hipStream_t stream) {
-  MetaView mv;
-  FLIDE_TRY(view_of(ctx, &b->caps, b->dev_meta, &mv));
-  FLIDE_TRY(enqueue_gdn(ctx, mv, b->gdn, 1, b->x, b->conv_w, b->alpha, b->eta, b->state_pool, b->conv_pool,
-                        b->n_slots, b->o_gdn, stream));
+  if (part == 0) return launched(ctx, launch_meta_expand(mv, stream), "meta_expand");
+  if (part == 1 || part == 3) {
+    FLIDE_TRY(enqueue_gdn(ctx, mv, b->gdn, part == 1 ? 0 : 1, b->x, b->conv_w, b->alpha, b->eta, b->state_pool,
+                          b->conv_pool, b->n_slots, b->o_gdn, stream));
+    if (part == 1) return FLIDE_OK;
+    if (!b->h || !b->w_opt || !b->opt_off || !b->opt_id || !b->probs)
+      return fail(ctx, FLIDE_E_INVALID_ARG, "readout buffer is NULL");
+    return launched(ctx, launch_readout(mv, b->ro, b->h, b->w_opt, b->opt_off, b->opt_id, b->n_opt_rows, b->probs,
+                                        stream),
+                    "readout");
+  }
   for (int l = 0; l < b->n_attn; ++l) {
     const flide_attn_params& ap = b->attn[l];
     FLIDE_TRY(enqueue_attn(ctx, mv, ap, b->q[l], b->k[l], b->v[l], b->k_cache[l], b->v_cache[l], b->o_attn[l],
@@ -327,17 +332,12 @@ flide_status enqueue_round_back(flide_ctx* ctx, const flide_round_bufs* b, hipSt
                                              const_cast<void*>(b->v_cache[l]), stream),
                          "attn_save_kv"));
   }
-  if (!b->h || !b->w_opt || !b->opt_off || !b->opt_id || !b->probs)
-    return fail(ctx, FLIDE_E_INVALID_ARG, "readout buffer is NULL");
-  FLIDE_TRY(launched(ctx, launch_readout(mv, b->ro, b->h, b->w_opt, b->opt_off, b->opt_id, b->n_opt_rows,
-                                         b->probs, stream),
-                     "readout"));
   return FLIDE_OK;
 }
 
 flide_status enqueue_round(flide_ctx* ctx, const flide_round_bufs* b, hipStream_t stream) {
-  FLIDE_TRY(enqueue_round_front(ctx, b, stream));
-  return enqueue_round_back(ctx, b, stream);
+  for (int part = 0; part < kRoundParts; ++part) FLIDE_TRY(enqueue_round_part(ctx, b, part, stream));
+  return FLIDE_OK;
 }
 
 flide_status check_round_bufs(flide_ctx* ctx, const flide_round_bufs* b) {
@@ -352,8 +352,9 @@ flide_status check_round_bufs(flide_ctx* ctx, const flide_round_bufs* b) {
   return FLIDE_OK;
 }
 
-// parts: 1 = front, 2 = back, 3 = both; the front uploads `image` first
+// parts: bit i replays part i (in part order); part 0 uploads `image` first
 flide_status graph_replay_parts(flide_ctx* ctx, int32_t bucket_id, const int32_t* image, void* stream, int parts) {
+  if (parts <= 0 || parts >= (1 << kRoundParts)) return fail(ctx, FLIDE_E_INVALID_ARG, "parts must be a mask of 1 .. 15");
   if (bucket_id < 0 || size_t(bucket_id) >= ctx->buckets.size() || !ctx->buckets[size_t(bucket_id)]->live)
     return fail(ctx, FLIDE_E_INVALID_ARG, "no such bucket (never captured, or released)");
   Bucket* b = ctx->buckets[size_t(bucket_id)];
@@ -362,9 +363,9 @@ flide_status graph_replay_parts(flide_ctx* ctx, int32_t bucket_id, const int32_t
     if (!image) return fail(ctx, FLIDE_E_INVALID_ARG, "image is NULL");
     FLIDE_TRY(check_image(ctx, b->bufs.caps, b->L, image));
     FLIDE_TRY(staging_upload(ctx, b->st, image, b->L.host_words, b->bufs.dev_meta, (hipStream_t)stream));
-    FLIDE_HIP(ctx, hipGraphLaunch(b->exec[0], (hipStream_t)stream));
   }
-  if (parts & 2) FLIDE_HIP(ctx, hipGraphLaunch(b->exec[1], (hipStream_t)stream));
+  for (int part = 0; part < kRoundParts; ++part)
+    if (parts & (1 << part)) FLIDE_HIP(ctx, hipGraphLaunch(b->exec[part], (hipStream_t)stream));
   return FLIDE_OK;
 }
 
@@ -673,14 +674,14 @@ flide_status flide_graph_capture(flide_ctx* ctx, const flide_round_bufs* bufs, v
     b->bufs = *bufs;
     compute_layout(bufs->caps, b->L);
     hipStream_t cs = ctx->capture_stream;
-    for (int part = 0; part < 2; ++part) {  // the front, then the back of the round
+    for (int part = 0; part < kRoundParts; ++part) {
       hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
       if (e != hipSuccess) {
         bucket_free(b);
         delete b;
         return fail_hip(ctx, e, "hipStreamBeginCapture");
       }
-      flide_status st = part == 0 ? enqueue_round_front(ctx, bufs, cs) : enqueue_round_back(ctx, bufs, cs);
+      flide_status st = enqueue_round_part(ctx, bufs, part, cs);
       hipGraph_t g = nullptr;
       e = hipStreamEndCapture(cs, &g);
       if (st != FLIDE_OK || e != hipSuccess) {
@@ -731,7 +732,7 @@ flide_status flide_select_bucket(const flide_ctx* ctx, int32_t T, int32_t R, int
 flide_status flide_graph_replay(flide_ctx* ctx, int32_t bucket_id, const int32_t* image, void* stream) {
   if (!ctx) return FLIDE_E_INVALID_ARG;
   try {
-    return graph_replay_parts(ctx, bucket_id, image, stream, 3);
+    return graph_replay_parts(ctx, bucket_id, image, stream, 15);
   } catch (...) {
     return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_graph_replay");
   }
@@ -740,7 +741,7 @@ flide_status flide_graph_replay(flide_ctx* ctx, int32_t bucket_id, const int32_t
 flide_status flide_graph_replay_front(flide_ctx* ctx, int32_t bucket_id, const int32_t* image, void* stream) {
   if (!ctx) return FLIDE_E_INVALID_ARG;
   try {
-    return graph_replay_parts(ctx, bucket_id, image, stream, 1);
+    return graph_replay_parts(ctx, bucket_id, image, stream, 3);
   } catch (...) {
     return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_graph_replay_front");
   }
@@ -749,9 +750,19 @@ flide_status flide_graph_replay_front(flide_ctx* ctx, int32_t bucket_id, const i
 flide_status flide_graph_replay_back(flide_ctx* ctx, int32_t bucket_id, void* stream) {
   if (!ctx) return FLIDE_E_INVALID_ARG;
   try {
-    return graph_replay_parts(ctx, bucket_id, nullptr, stream, 2);
+    return graph_replay_parts(ctx, bucket_id, nullptr, stream, 12);
   } catch (...) {
     return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_graph_replay_back");
+  }
+}
+
+flide_status flide_graph_replay_parts(flide_ctx* ctx, int32_t bucket_id, const int32_t* image, int32_t parts,
+                                     void* stream) {
+  if (!ctx) return FLIDE_E_INVALID_ARG;
+  try {
+    return graph_replay_parts(ctx, bucket_id, image, stream, parts);
+  } catch (...) {
+    return fail(ctx, FLIDE_E_INTERNAL, "exception in flide_graph_replay_parts");
   }
 }
 

@@ -136,6 +136,7 @@ _SIGNATURES = {
     "flide_graph_replay": (C.c_int, [_VP, C.c_int32, C.POINTER(C.c_int32), _VP]),
     "flide_graph_replay_front": (C.c_int, [_VP, C.c_int32, C.POINTER(C.c_int32), _VP]),
     "flide_graph_replay_back": (C.c_int, [_VP, C.c_int32, _VP]),
+    "flide_graph_replay_parts": (C.c_int, [_VP, C.c_int32, C.POINTER(C.c_int32), C.c_int32, _VP]),
     "flide_graph_release": (C.c_int, [_VP, C.c_int32]),
     "flide_round_eager": (C.c_int, [_VP, C.POINTER(flide_round_bufs), C.POINTER(C.c_int32), _VP]),
     "flide_check_device": (C.c_int, [_VP, C.POINTER(flide_caps), _VP, _VP]),
@@ -513,6 +514,16 @@ def flide_graph_replay_front(ctx: Context, bucket_id: int, image: np.ndarray, st
 def flide_graph_replay_back(ctx: Context, bucket_id: int, stream=None) -> None:
     _check(load_library().flide_graph_replay_back(ctx.handle, int(bucket_id), _stream(stream)),
            "flide_graph_replay_back", ctx.handle)
+
+
+def flide_graph_replay_parts(ctx: Context, bucket_id: int, image: Optional[np.ndarray], parts: int,
+                             stream=None) -> None:
+    ptr = None
+    if image is not None:
+        image = np.ascontiguousarray(image, dtype=np.int32)
+        ptr = image.ctypes.data_as(C.POINTER(C.c_int32))
+    _check(load_library().flide_graph_replay_parts(ctx.handle, int(bucket_id), ptr, int(parts), _stream(stream)),
+           "flide_graph_replay_parts", ctx.handle)
 
 
 def flide_graph_release(ctx: Context, bucket_id: int) -> None:

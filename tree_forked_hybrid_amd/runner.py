@@ -339,6 +339,17 @@ class BucketTable:
     def run_back(self, stream=None) -> None:
         F.flide_graph_replay_back(self.ctx, self.last[0], stream)
 
+    def run_parts(self, parts: int, requests=None, stream=None, bid: Optional[int] = None) -> None:
+        """Replay the parts of the bucket's round whose bits are set (0 metadata upload and expansion, 1 GDN
+        call 1, 2 attention, 3 GDN call 2 and readout); with part 0 the round is planned from `requests`,
+        else the last planned round's bucket is used."""
+        if parts & 1:
+            bid, img = self.plan(F.Requests(requests), bid)
+            F.flide_graph_replay_parts(self.ctx, bid, img, parts, stream)
+            self.last = (bid, img)
+        else:
+            F.flide_graph_replay_parts(self.ctx, self.last[0], None, parts, stream)
+
     def caps_of(self, bid: int) -> F.flide_caps:
         return self.buckets[bid][0]
 
@@ -383,31 +394,73 @@ class SplitExecutor:
 
 
 class FrontScheduler:
-    """The sub-rounds of one split round, each in a bucket table of its own: every front (metadata upload and
-    expansion, GDN call 1) on a side stream of its own, all ordered after the work already on the launch
-    stream, then the backs (GDN call 2, attention, readout) one after another on the launch stream, each
-    after its own front.  A sub-round's trunk call fills only as many CUs as it has (segment, head) pairs
-    (96 of 256 on a fan-out sub-round), so the trunk calls of the sub-rounds run side by side; the attention
-    launches, which fill the GPU, stay in order (side by side they slow each other down).  The next round's
-    fronts wait for this round's backs, which read the same buffers."""
+    """The sub-rounds of one round (a split round, or a single one), each in a bucket table of its own,
+    replayed part by part (BucketTable.run_parts) on the launch stream and one side stream per sub-round.
+    The trunk GDN call runs one workgroup per (trunk, head), each holding a whole CU for its chunk chain:
 
-    def __init__(self, n: int):
+    * rounds whose trunk calls have few such pairs (at most a quarter of the CUs over all sub-rounds: the
+      long-document round's 64) run each trunk call on a side stream beside the attention of its own
+      sub-round, which does not read it (long document 2.78 -> 2.16 ms per round on MI355X); the question
+      call and the readout follow on the launch stream after both;
+    * otherwise every sub-round's front (metadata expansion, trunk call) runs on its side stream, all side
+      by side, and the backs (attention, question call, readout) in order on the launch stream, each after
+      its own front (fan-out 17.0-18.0 -> 14.7 ms; overlapping attention too gains nothing there, and the
+      agent-resume round's attention loses 1% beside its 128 trunk workgroups);
+    * a single sub-round without the overlap replays on the launch stream alone.
+
+    The attention launches, which fill the GPU, stay in order (side by side they slow each other down).  The
+    next round's work on a table follows this round's on the launch stream, which waits for every side
+    stream before its question calls."""
+
+    def __init__(self, n: int, overlap_attention: Optional[bool] = None):
         self.side = [torch.cuda.Stream() for _ in range(n)]
         self.start = torch.cuda.Event()
+        self.expanded = [torch.cuda.Event() for _ in range(n)]
         self.done = [torch.cuda.Event() for _ in range(n)]
+        self.overlap_attention = overlap_attention
+        self.n_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+        self.last_mode = None
+
+    def mode(self, tables: Sequence[BucketTable], sub_requests) -> str:
+        if self.overlap_attention is None:
+            pairs = sum(len(reqs) * tab.bufs.spec.shapes.H for tab, reqs in zip(tables, sub_requests))
+            overlap = 4 * pairs <= self.n_cus
+        else:
+            overlap = self.overlap_attention
+        if overlap:
+            return "trunk calls beside attention"
+        return "side by side" if len(tables) > 1 else "in order"
 
     def run(self, tables: Sequence[BucketTable], sub_requests, stream=None) -> None:
         assert len(tables) == len(sub_requests) <= len(self.side)
         assert len({id(t) for t in tables}) == len(tables), "each sub-round needs a table of its own"
         main = stream if stream is not None else torch.cuda.current_stream()
-        self.start.record(main)
+        self.last_mode = mode = self.mode(tables, sub_requests)
+        if mode == "in order":
+            for tab, reqs in zip(tables, sub_requests):
+                tab.run(reqs, stream=main)
+            return
+        if mode == "side by side":
+            self.start.record(main)
+            for k, (tab, reqs) in enumerate(zip(tables, sub_requests)):
+                self.side[k].wait_event(self.start)
+                tab.run_front(reqs, stream=self.side[k])
+                self.done[k].record(self.side[k])
+            for k, tab in enumerate(tables):
+                main.wait_event(self.done[k])
+                tab.run_back(stream=main)
+            return
         for k, (tab, reqs) in enumerate(zip(tables, sub_requests)):
-            self.side[k].wait_event(self.start)
-            tab.run_front(reqs, stream=self.side[k])
+            tab.run_parts(1, reqs, stream=main)  # upload and expansion
+            self.expanded[k].record(main)
+        for k, tab in enumerate(tables):
+            self.side[k].wait_event(self.expanded[k])
+            tab.run_parts(2, stream=self.side[k])  # trunk call
             self.done[k].record(self.side[k])
         for k, tab in enumerate(tables):
+            tab.run_parts(4, stream=main)  # attention
             main.wait_event(self.done[k])
-            tab.run_back(stream=main)
+            tab.run_parts(8, stream=main)  # question call, readout
 
 
 class StackRunner:
