@@ -363,7 +363,7 @@ def stack_cpu_baseline(shapes, base: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
@@ -460,13 +460,23 @@ def main():
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    # Round latency: plan, upload and replay every sub-round of one round, then wait for it.
+    # Round latency, host: plan, upload and replay every sub-round of one round, copy its option
+    # probabilities into pinned host memory and wait for them.  Device: HIP events on the launch stream
+    # around the round's replays (the side streams join it before the round ends).
+    n_opt = [sum(sum(r.n_opt) for r in reqs) for reqs in sub_reqs]
+    host_probs = [torch.empty(max(1, n), dtype=torch.float32, pin_memory=True) for n in n_opt]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     lat = []
-    for _ in range(args.steps):
+    for i in range(args.steps):
         s0 = time.perf_counter()
+        ev[i][0].record()
         step()
+        ev[i][1].record()
+        for tab, hp, n in zip(tables, host_probs, n_opt):
+            hp[:n].copy_(tab.bufs.probs[:n], non_blocking=True)
         torch.cuda.synchronize()
         lat.append(time.perf_counter() - s0)
+    dev_ms = sorted(a.elapsed_time(b) for a, b in ev)
     gc.enable()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     for tab in tables:
@@ -594,7 +604,11 @@ def main():
                    "deterministic": spec.deterministic,
                    "schedule": sched.last_mode if sched is not None else "in order"},
         "round_latency_ms": {"p10": round(lat_ms[len(lat_ms) // 10], 4), "median": round(lat_ms[len(lat_ms) // 2], 4),
-                             "p90": round(lat_ms[(9 * len(lat_ms)) // 10], 4)},
+                             "p90": round(lat_ms[(9 * len(lat_ms)) // 10], 4),
+                             "what": "host: plan, metadata upload, replays, probabilities copied to host"},
+        "device_round_ms": {"p10": round(dev_ms[len(dev_ms) // 10], 4), "median": round(dev_ms[len(dev_ms) // 2], 4),
+                            "p90": round(dev_ms[(9 * len(dev_ms)) // 10], 4),
+                            "what": "HIP events on the launch stream around one round's replays"},
         "per_layer_tokens_per_s": {
             "gdn": round(T / ((kernels["fork_gdn_trunks"] + kernels["fork_gdn_questions"]) * 1e-6), 1),
             "attn": round(T / ((kernels["attn_prepare"] + kernels["attn_core"]) * 1e-6), 1),
