@@ -131,12 +131,13 @@ def _host_cpu() -> str:
 
 
 def cpu_baseline(rnd, n_trunk_sample: int = 48):
-    """The oracle (as it stands, single BLAS thread) on a bounded sample of the round's first request:
-    its GDN over the whole trunk and its first question (per-token recurrence: the full cost of those rows),
-    its attention at ``n_trunk_sample`` trunk rows at evenly spaced positions plus every row of the
-    question, and the question's readout.  The trunk's attention time is scaled to all trunk rows by the
-    ratio of visible keys (the oracle's per-row attention cost is linear in them); value = sampled rows /
-    (measured GDN, question attention and readout time + scaled trunk attention time)."""
+    """The oracle (as it stands) on a bounded sample of the round's first request: its GDN over the whole
+    trunk and its first question (per-token recurrence: the full cost of those rows), its attention at
+    ``n_trunk_sample`` trunk rows at evenly spaced positions plus every row of the question, and the
+    question's readout.  The trunk's attention time is scaled to all trunk rows by the ratio of visible keys
+    (the oracle's per-row attention cost is linear in them); value = sampled rows / (measured GDN, question
+    attention and readout time + scaled trunk attention time).  Timed with one BLAS thread (the reported
+    value) and again with a BLAS thread per logical CPU of the host."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_limits
@@ -155,35 +156,42 @@ def cpu_baseline(rnd, n_trunk_sample: int = 48):
     rows = np.arange(tn + L)
     pos = np.concatenate([np.arange(r.m, r.P), np.arange(r.P, r.P + L)])
     samp = sorted(set(np.linspace(0, tn - 1, min(n_trunk_sample, tn)).astype(int).tolist())) if tn else []
-    limiter = threadpool_limits(1) if threadpool_limits else None
-    try:
-        t0 = time.perf_counter()
-        gdn_prompt(pl["gdn_x"][rows], pl["alpha"][rows], pl["eta"][rows], conv_w, sh.H, sh.dk, sh.dv,
-                   pl.get("ckpt_window"), pl.get("ckpt_state"), sh.gdn_act)
-        t1 = time.perf_counter()
-        ck = (pl.get("kv_k"), pl.get("kv_v")) if r.m > 0 else (None, None)
-        prompt_attention(pl["attn_q"][rows], pl["attn_k"][rows], pl["attn_v"][rows], pos, sh.theta,
-                         cache_k=ck[0], cache_v=ck[1], rows=samp)
-        t2 = time.perf_counter()
-        prompt_attention(pl["attn_q"][rows], pl["attn_k"][rows], pl["attn_v"][rows], pos, sh.theta,
-                         cache_k=ck[0], cache_v=ck[1], rows=list(range(tn, tn + L)))
-        if L:
-            option_probs(pl["hidden"][tn + L - 1], pl["w_opt"][:r.n_opt[0]])
-        t3 = time.perf_counter()
-    finally:
-        if limiter is not None:
-            limiter.unregister()
     vis_all = sum(t + 1 for t in range(r.m, r.P))
     vis_samp = sum(int(pos[a]) + 1 for a in samp) or 1
-    t_trunk_attn = (t2 - t1) * vis_all / vis_samp
-    total = (t1 - t0) + t_trunk_attn + (t3 - t2)
-    return {"value": round((tn + L) / total, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+
+    def timed(threads):
+        limiter = threadpool_limits(threads) if threadpool_limits else None
+        try:
+            t0 = time.perf_counter()
+            gdn_prompt(pl["gdn_x"][rows], pl["alpha"][rows], pl["eta"][rows], conv_w, sh.H, sh.dk, sh.dv,
+                       pl.get("ckpt_window"), pl.get("ckpt_state"), sh.gdn_act)
+            t1 = time.perf_counter()
+            ck = (pl.get("kv_k"), pl.get("kv_v")) if r.m > 0 else (None, None)
+            prompt_attention(pl["attn_q"][rows], pl["attn_k"][rows], pl["attn_v"][rows], pos, sh.theta,
+                             cache_k=ck[0], cache_v=ck[1], rows=samp)
+            t2 = time.perf_counter()
+            prompt_attention(pl["attn_q"][rows], pl["attn_k"][rows], pl["attn_v"][rows], pos, sh.theta,
+                             cache_k=ck[0], cache_v=ck[1], rows=list(range(tn, tn + L)))
+            if L:
+                option_probs(pl["hidden"][tn + L - 1], pl["w_opt"][:r.n_opt[0]])
+            t3 = time.perf_counter()
+        finally:
+            if limiter is not None:
+                limiter.unregister()
+        t_trunk_attn = (t2 - t1) * vis_all / vis_samp
+        return (tn + L) / ((t1 - t0) + t_trunk_attn + (t3 - t2)), (t1 - t0, t2 - t1, t_trunk_attn, t3 - t2)
+
+    v1, (g, a, ta, q) = timed(1)
+    n_cpu = os.cpu_count() or 1
+    vn, _ = timed(n_cpu)
+    return {"value": round(v1, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": (f"request 0 of the round ({tn} trunk rows) with its first question ({L} rows), memo order, "
-                       f"fp64, one BLAS thread: GDN over all {tn + L} rows {t1 - t0:.1f} s; attention at "
-                       f"{len(samp)} evenly spaced trunk rows {t2 - t1:.1f} s, scaled by visible keys to all "
-                       f"{tn} trunk rows = {t_trunk_attn:.1f} s (extrapolated); question attention + readout "
-                       f"{t3 - t2:.1f} s; host {os.cpu_count()} logical CPUs, {_host_cpu()}"),
-            "host_cpus": os.cpu_count()}
+                       f"fp64, one BLAS thread: GDN over all {tn + L} rows {g:.1f} s; attention at "
+                       f"{len(samp)} evenly spaced trunk rows {a:.1f} s, scaled by visible keys to all "
+                       f"{tn} trunk rows = {ta:.1f} s (extrapolated); question attention + readout "
+                       f"{q:.1f} s; host {n_cpu} logical CPUs, {_host_cpu()}"),
+            "host_cpus": n_cpu,
+            "all_cores": {"value": round(vn, 3), "cores": n_cpu, "blas_threads": n_cpu}}
 
 
 def measured_peaks(torch):
