@@ -120,20 +120,29 @@ typedef struct {
  *               per head group; chosen by the planner for rounds whose tiles see thousands of keys)
  *   seg_*       [seg_cap]  row0, len, req, branch, pos0, state (slot or -1),
  *                          vcol0: column offset of the segment in the transposed
- *                          value workspace (column = vcol0 + position, so that
- *                          8-aligned positions land on 16-byte aligned columns)
+ *                          value workspace (column = vcol0 + position, congruent
+ *                          to the position modulo 32: 32-aligned positions start a
+ *                          column block of the tile-major workspace)
  *   req_*       [R_cap]    trunk_row0, P, m, ckpt_slot, out_slot, q_seg0, n_q,
  *                          save_m, save_slot (0 and -1 when no checkpoint is made)
  *   qfin_row    [Q_cap]    last stream row of every question (stream order)
- *   tile_seg    [tile_cap] attention work list: segment of each tile
- *   tile_row0   [tile_cap]                      first stream row of each tile
+ *   tile_seg    [tile_cap * 4] attention work list: a tile is four units of up
+ *                          to 8 rows; unit u of position x is at x * 4 + u:
+ *                          its segment (-1: no unit; unit 0 of a used position
+ *                          always exists) ...
+ *   tile_row0   [tile_cap * 4] ... and its first stream row.  A tile's units
+ *                          are consecutive rows of one trunk, or rows of up to
+ *                          four questions of one request
  *   gdn_order   [seg_cap]  GDN work list: trunk segments, then question segments,
  *                          each by length, longest first (ties in stream order)
  *   tok_j/c/t   [T_cap]    per-row metadata (device only)
- *   tile_desc   [tile_cap * 16] per attention work-list position: segment (-1 if
- *                          unused), first row, rows, first position, m, P, checkpoint
- *                          slot, question flag, key-row and value-column offsets of
- *                          the trunk and own ranges, first position of the segment
+ *   tile_desc   [tile_cap * 48] per attention work-list position: segment of
+ *                          unit 0 (-1 if unused), question flag, P, m, checkpoint
+ *                          slot, key-row and value-column offsets of the trunk,
+ *                          first and last query position, own ranges; per unit:
+ *                          first row, rows, first position, own range; per own
+ *                          range (a segment among the units): key-row and
+ *                          value-column offsets, first and one-past-last position
  *                          (device only)
  *   dev_error   [4]        device error word (device only)                     */
 typedef struct {

@@ -73,16 +73,37 @@ def _assert_same_layout(reqs, caps):
     np.testing.assert_array_equal(got["req_P"], [r.P for r in reqs])
     np.testing.assert_array_equal(got["req_m"], [r.m for r in reqs])
     np.testing.assert_array_equal(got["req_nq"], [len(r.q_len) for r in reqs])
-    # the tile list covers every row of every segment exactly once, tiles aligned to segment starts
+    # the tile list covers every row of every segment exactly once: tiles of four units of up to 8 rows
+    # aligned to their segment's start; a trunk tile is 32 consecutive rows of its trunk (aligned to its
+    # start), a question tile holds units of questions of one request, packed in question order
     cover = np.zeros(ref["T"], np.int32)
-    for s, r0 in zip(got["tile_seg"], got["tile_row0"]):
-        if s == -1:  # unused position
+    n_qtiles = {}
+    for segs, rows in zip(got["tile_seg"], got["tile_row0"]):
+        if segs[0] == -1:  # unused position
+            assert (segs == -1).all()
             continue
-        a = r0 - ref["seg_row0"][s]
-        assert a % 32 == 0 and 0 <= a < ref["seg_len"][s]
-        n = min(32, ref["seg_len"][s] - a)
-        cover[r0:r0 + n] += 1
+        used = [(int(s), int(r0)) for s, r0 in zip(segs, rows) if s != -1]
+        assert [s for s in segs if s != -1] == [s for s, _ in used] and all(segs[:len(used)] != -1)
+        assert len({int(ref["seg_req"][s]) for s, _ in used}) == 1
+        trunk = ref["seg_branch"][used[0][0]] == 0
+        for u, (s, r0) in enumerate(used):
+            a = r0 - ref["seg_row0"][s]
+            assert a % 8 == 0 and 0 <= a < ref["seg_len"][s]
+            n = min(8, ref["seg_len"][s] - a)
+            cover[r0:r0 + n] += 1
+            if trunk:
+                assert s == used[0][0] and a == (used[0][1] - ref["seg_row0"][s]) + 8 * u
+        if trunk:
+            assert (used[0][1] - ref["seg_row0"][used[0][0]]) % 32 == 0
+        else:
+            assert all(ref["seg_branch"][s] > 0 for s, _ in used)
+            j = int(ref["seg_req"][used[0][0]])
+            n_qtiles[j] = n_qtiles.get(j, 0) + 1
     assert (cover == 1).all()
+    for j in range(ref["R"]):  # packing: ceil(question units / 4) tiles per request
+        lens = [int(ref["seg_len"][s]) for s in range(ref["n_seg"]) if ref["seg_req"][s] == j and ref["seg_branch"][s] > 0]
+        units = sum((n + 7) // 8 for n in lens)
+        assert n_qtiles.get(j, 0) == (units + 3) // 4
     # the GDN work list: trunks then questions, each a permutation ordered by length (longest first,
     # ties in stream order)
     R, n_seg = ref["R"], ref["n_seg"]
@@ -118,9 +139,11 @@ def test_planner_attention_work_order(config, group):
 def test_planner_worked_example_tiles():
     rnd = make_round(0, 0)
     got = _planner_layout(rnd.requests, F.caps_of(69, 1, 3))
-    # questions (49+ keys) first, then the trunk tile 32..47 (48 keys), then 0..31
-    used = got["tile_seg"] >= 0
-    assert got["tile_row0"][used].tolist() == [60, 53, 48, 32, 0]
+    # the three questions (rows 48-52, 53-59, 60-68) packed into one tile of four units (57 keys for its
+    # last row), then the trunk tile 32..47 (48 keys), then 0..31
+    used = got["tile_seg"][:, 0] >= 0
+    rows = [[int(r) for s, r in zip(ss, rr) if s >= 0] for ss, rr in zip(got["tile_seg"][used], got["tile_row0"][used])]
+    assert rows == [[48, 53, 60, 68], [32, 40], [0, 8, 16, 24]]
 
 
 _req = st.builds(

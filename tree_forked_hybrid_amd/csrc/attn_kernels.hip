@@ -40,15 +40,13 @@ __global__ void __launch_bounds__(256) attn_plain_kernel(MetaView mv, const T* _
   const int g = h / (Hq / Hkv);
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int s = mv.tile_seg[tile];
-  if (s == -1) return;  // unused position of the work list
-  if (s < 0 || s >= mv.hdr[H_NSEG]) {
+  const int s0 = mv.tile_seg[int64_t(tile) * kTileUnits];
+  if (s0 == -1) return;  // unused position of the work list
+  if (s0 < 0 || s0 >= mv.hdr[H_NSEG]) {
     if (threadIdx.x == 0) flag_error(mv.dev_error, E_SEGMENT);
     return;
   }
-  const int seg_row0 = mv.seg_row0[s], seg_len = mv.seg_len[s];
-  const int j = mv.seg_req[s];
-  const bool question = mv.seg_branch[s] > 0;
+  const int j = mv.seg_req[s0];
   const int P = mv.req_P[j], m = mv.req_m[j];
   const int ckpt = mv.req_ckpt[j];
   if (m > 0 && (m > cache_rows || k_cache == nullptr || ckpt < 0 || ckpt >= cache_slots)) {
@@ -59,9 +57,15 @@ __global__ void __launch_bounds__(256) attn_plain_kernel(MetaView mv, const T* _
   const int half = d >> 1;
   const int per_lane = (d + 63) / 64;
 
+  // row r of the tile: row r % kUnitRows of unit r / kUnitRows (the units' segments were checked by
+  // meta_expand: one request, rows inside the segment)
   for (int r = wave; r < kTileRows; r += 4) {
-    const int x = mv.tile_row0[tile] + r;
-    if (x >= seg_row0 + seg_len) break;
+    const int s = mv.tile_seg[int64_t(tile) * kTileUnits + r / kUnitRows];
+    if (s < 0 || s >= mv.hdr[H_NSEG] || mv.seg_req[s] != j) continue;
+    const int seg_row0 = mv.seg_row0[s], seg_len = mv.seg_len[s];
+    const bool question = mv.seg_branch[s] > 0;
+    const int x = mv.tile_row0[int64_t(tile) * kTileUnits + r / kUnitRows] + r % kUnitRows;
+    if (x < seg_row0 || x >= seg_row0 + seg_len) continue;
     const int tx = mv.seg_pos0[s] + (x - seg_row0);
     if (tx >= max_pos) {
       if (lane == 0) flag_error(mv.dev_error, E_POSITION);
@@ -366,7 +370,7 @@ __device__ __forceinline__ int ksw(int row) { return (row & 3) | (((row >> 3) & 
 // leaves two rows of each group on one column and halves the read rate.
 __device__ __forceinline__ int vsw(int row) { return ((row >> 2) & 3) ^ (((row >> 2) ^ (row >> 3)) & 1); }
 
-template <int D>
+template <int D, bool G4>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_rot,
                  const bf16_t* __restrict__ vt, const bf16_t* __restrict__ k_cache,
@@ -409,17 +413,16 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   // the position's descriptor (written by meta_expand): one 64-byte load instead of a chain of table
   // lookups.  The grid has tile_cap positions per head group, so the load is in bounds before the
   // position is known to be used; issuing it beside the header saves a round trip.
-  int32_t td[kTileDescWords];
+  constexpr int kHeadWords = 16;  // the tile's own words; units and own ranges are read where they are used
+  int32_t td[kHeadWords];
+  // The descriptor is read-only here (meta_expand wrote it before this launch) and the same for every lane:
+  // it is read through the scalar path (constant address space), in batches with one wait.
+  typedef const int32_t __attribute__((address_space(4)))* desc_ptr;
+  auto desc_of = [&](int x) { return (desc_ptr)(uintptr_t)(mv.tile_desc + int64_t(x) * kTileDescWords); };
   auto load_desc = [&]() {
-    const int4* src = reinterpret_cast<const int4*>(mv.tile_desc + int64_t(tile) * kTileDescWords);
+    const desc_ptr src = desc_of(tile);
 #pragma unroll
-    for (int i = 0; i < kTileDescWords / 4; ++i) {
-      const int4 v = src[i];
-      td[4 * i] = v.x;
-      td[4 * i + 1] = v.y;
-      td[4 * i + 2] = v.z;
-      td[4 * i + 3] = v.w;
-    }
+    for (int i = 0; i < kHeadWords; ++i) td[i] = src[i];
   };
   load_desc();
   const int n_tiles_round = mv.hdr[H_NTILES];
@@ -434,48 +437,101 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   }
   if (tile >= n_tiles_round) return;
   const int kvh = yy / HG, hg0 = (yy % HG) * 4;  // kv head; first q head of the group in this workgroup
-  const int ng = min(4, G - hg0);                  // q heads of this workgroup (1 .. 4)
+  // q heads of this workgroup (1 .. 4); G4: every head group has four (then wave w holds unit w)
+  const int ng = G4 ? 4 : min(4, G - hg0);
   const int seg = td[TD_SEG];
   if (seg < 0) return;  // unused position (an inconsistent segment was flagged by meta_expand)
   const bool question = td[TD_QUESTION] != 0;
-  const int P = td[TD_P], m = td[TD_M], ckpt = td[TD_CKPT], pos0 = td[TD_POS0];
+  const int P = td[TD_P], m = td[TD_M], ckpt = td[TD_CKPT];
   if (m > 0 && (m > cache_rows || k_cache == nullptr || ckpt < 0 || ckpt >= cache_slots)) {
     if (tid == 0) flag_error(mv.dev_error, E_CACHE);
     return;
   }
-  const int x0 = td[TD_ROW0];
-  const int nrows = td[TD_NROWS];
-  const int qpos_min = td[TD_QPOS0];
-  const int qpos_max = qpos_min + nrows - 1;
+  const int qpos_min = td[TD_QPOS_MIN], qpos_max = td[TD_QPOS_MAX];
+  const int n_own = min(td[TD_NOWN], kTileUnits);
   if (qpos_max >= max_pos) {
     if (tid == 0) flag_error(mv.dev_error, E_POSITION);
     return;
   }
   // Query columns: the tile's 32 rows x ng heads in row-major order, wave w taking columns 32 w .. 32 w + 31
-  // (column k is row k / ng of head hg0 + k % ng).  All heads of a row see the same keys, and each column's
-  // arithmetic involves that column only, so the assignment of columns to waves and lanes changes no bit;
-  // with four heads a wave holds 8 rows, and a wave whose rows all lie past the tile's last row (short
-  // question tiles) skips the key loop's arithmetic.
-  const bool active = w < ng && (32 * w) / ng < nrows;
+  // (column k is row k / ng of head hg0 + k % ng; tile row r is row r % kUnitRows of unit r / kUnitRows,
+  // whose rows belong to one segment: a trunk or one question).  All heads of a row see the same keys, and
+  // each column's arithmetic involves that column only, so the assignment of columns to waves and lanes
+  // changes no bit; with four heads a wave holds one unit, and a wave without a row (a short tile) skips
+  // the key loop's arithmetic.
+  // With four heads the wave's unit is w: its words are read once into scalars.  Otherwise a lane reads the
+  // words of its row's unit from the record (a cached per-lane load).
+  const desc_ptr unit_desc = desc_of(tile) + TD_UNIT;
+  const int32_t* unit_vec = mv.tile_desc + int64_t(tile) * kTileDescWords + TD_UNIT;
+  int w_row0 = 0, w_nrows = 0, w_qpos0 = 0, w_own = 0;
+  if constexpr (G4) {
+    const desc_ptr ud = unit_desc + 4 * w;
+    w_row0 = ud[TU_ROW0], w_nrows = ud[TU_NROWS], w_qpos0 = ud[TU_QPOS0], w_own = ud[TU_OWN];
+  }
+  const desc_ptr own_desc = desc_of(tile) + TD_OWN;
+  auto own_word = [&](int k, int f) __attribute__((always_inline)) { return own_desc[4 * k + f]; };
+  struct ColInfo {
+    bool valid;
+    int row, pos, own;  // stream row, position and own key range of a valid column
+  };
+  // tile row r (column k is row k / ng); selects only, no branch that splits the wave (an invalid row reads
+  // a valid stream row at a valid position)
+  auto row_info = [&](int r) __attribute__((always_inline)) {
+    // with four heads, the rows of wave w's columns (and of its share of the table rows) are unit w's
+    const int ri = r % kUnitRows;
+    int row0, nrows, qpos0, own;
+    if constexpr (G4) {
+      row0 = w_row0, nrows = w_nrows, qpos0 = w_qpos0, own = w_own;
+    } else {
+      const int32_t* ud = unit_vec + 4 * min(r / kUnitRows, kTileUnits - 1);
+      row0 = ud[TU_ROW0], nrows = ud[TU_NROWS], qpos0 = ud[TU_QPOS0], own = ud[TU_OWN];
+    }
+    const bool valid = (r < kTileRows) & (ri < nrows);  // both evaluated: no branch
+    return ColInfo{valid, valid ? row0 + ri : unit_desc[TU_ROW0], valid ? qpos0 + ri : qpos_min, own};
+  };
+  auto col_info = [&](int col) __attribute__((always_inline)) { return row_info(col / ng); };
+  // this lane's two query columns (blocks qb = 0, 1): position and own key range, kept for the key loop
+  int qpos[2], qown[2];
+  bool active, qvalid[2];
+  int own_mask = 0;  // own key ranges that some column of this wave reads (bit k: own range k)
+  {
+    const ColInfo c0 = col_info(32 * w + r16), c1 = col_info(32 * w + 16 + r16);
+    qpos[0] = c0.pos, qpos[1] = c1.pos, qown[0] = c0.own, qown[1] = c1.own;
+    qvalid[0] = c0.valid, qvalid[1] = c1.valid;
+    active = __builtin_amdgcn_ballot_w64(c0.valid || c1.valid) != 0;
+#pragma unroll
+    for (int k = 0; k < kTileUnits; ++k)
+      if (__builtin_amdgcn_ballot_w64((c0.valid && c0.own == k) || (c1.valid && c1.own == k))) own_mask |= 1 << k;
+    own_mask = __builtin_amdgcn_readfirstlane(own_mask);
+  }
   // the same flag as a scalar integer: tested once per key tile, where a boolean would be rebuilt from a
   // lane mask with vector instructions
   const int active_s = __builtin_amdgcn_readfirstlane(int(active));
   const int64_t VT = vt_cols(mv.T_cap, mv.seg_cap);
   const int lo_w = window > 0 ? qpos_min - window + 1 : INT_MIN;
 
-  // ---- the (up to) three key ranges: positions [lo, hi), key row = p + roff, value column = p + voff ----
-  // (A) checkpoint cache, (B) the request's trunk rows (question tiles only), (C) own rows
+  // ---- the key ranges: positions [lo, hi), key row = p + roff, value column = p + voff ----
+  // (A) checkpoint cache, (B) the request's trunk rows (question tiles only), (C_k) own rows: one range per
+  // segment among the tile's units (a trunk, or each question of a packed tile), read only by its columns
   const int lo0 = max(0, lo_w), hi0 = m > 0 ? min(m, qpos_max + 1) : 0;
   const int lo1 = max(m, lo_w), hi1 = question ? P : 0;
-  const int lo2 = max(pos0, lo_w), hi2 = qpos_max + 1;
-  const int64_t roff0 = int64_t(ckpt) * cache_rows, roff1 = td[TD_ROFF_TRUNK], roff2 = td[TD_ROFF_OWN];
-  const int64_t voff1 = td[TD_VOFF_TRUNK], voff2 = td[TD_VOFF_OWN];
-  const int ts00 = lo0 & ~(BN - 1), ts01 = lo1 & ~(BN - 1), ts02 = lo2 & ~(BN - 1);
+  const int64_t roff0 = int64_t(ckpt) * cache_rows, roff1 = td[TD_ROFF_TRUNK];
+  const int64_t voff1 = td[TD_VOFF_TRUNK];
+  const int ts00 = lo0 & ~(BN - 1), ts01 = lo1 & ~(BN - 1);
   const int n0 = lo0 < hi0 ? (hi0 - ts00 + BN - 1) / BN : 0;
   const int n1 = lo1 < hi1 ? (hi1 - ts01 + BN - 1) / BN : 0;
-  const int n2 = lo2 < hi2 ? (hi2 - ts02 + BN - 1) / BN : 0;
-  const int n_tiles = n0 + n1 + n2;
-  // A cursor walks the key tiles in order: range rg (0, 1, 2 as above), tile start ts (a position) and the
+  int n_tiles = n0 + n1;
+  {
+    int olo[kTileUnits], ohi[kTileUnits];  // read together (one scalar round trip), unused ranges ignored
+#pragma unroll
+    for (int k = 0; k < kTileUnits; ++k) olo[k] = own_word(k, TO_LO), ohi[k] = own_word(k, TO_HI);
+#pragma unroll
+    for (int k = 0; k < kTileUnits; ++k) {  // an own range holds its units' positions, so it is never empty
+      const int lo = max(olo[k], lo_w), hi = ohi[k];
+      if (k < n_own) n_tiles += lo < hi ? (hi - (lo & ~(BN - 1)) + BN - 1) / BN : 0;
+    }
+  }
+  // A cursor walks the key tiles in order: range rg (0 = A, 1 = B, 2 + k = C_k), tile start ts (a position) and the
   // byte addresses of the tile's first key row (kp) and of the first value column of this wave's first
   // value row (vp), advanced by one tile's stride (vstep for values); vrow is the byte stride of value
   // rows: the checkpoint cache holds whole transposed rows, the workspace one 64-byte row per block.  The range's
@@ -485,7 +541,7 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
     const unsigned char* kp;
     const unsigned char* vp;
   };
-  auto range_start = [&](int rg) {
+  auto range_start = [&](int rg) __attribute__((always_inline)) {
     Cursor c;
     c.rg = rg;
     if (rg == 0) {  // checkpoint cache: keys [slot rows, Hkv, D], values [slot, Hkv, D, cache_rows]
@@ -494,8 +550,14 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
       c.vp = reinterpret_cast<const unsigned char*>(v_cache + (int64_t(ckpt) * Hkv + kvh) * D * cache_rows +
                                                     int64_t(c.ts) + int64_t(w * IPW * 16) * cache_rows);
     } else {  // workspace: rotated keys, tile-major values (ts + voff is a multiple of 32)
-      c.ts = rg == 1 ? ts01 : ts02, c.lo = rg == 1 ? lo1 : lo2, c.hi = rg == 1 ? hi1 : hi2;
-      const int64_t roff = rg == 1 ? roff1 : roff2, voff = rg == 1 ? voff1 : voff2;
+      int64_t roff = roff1, voff = voff1;
+      c.lo = lo1, c.hi = hi1;
+      if (rg >= 2) {
+        const int k = rg - 2;
+        roff = own_word(k, TO_ROFF), voff = own_word(k, TO_VOFF);
+        c.lo = max(own_word(k, TO_LO), lo_w), c.hi = own_word(k, TO_HI);
+      }
+      c.ts = c.lo & ~(BN - 1);
       c.vrow = BN * 2, c.vstep = D * BN * 2;
       c.kp = reinterpret_cast<const unsigned char*>(k_rot + int64_t(kvh) * D + (int64_t(c.ts) + roff) * Hkv * D);
       c.vp = reinterpret_cast<const unsigned char*>(vt + vt_index(kvh, w * IPW * 16, int64_t(c.ts) + voff, D, VT));
@@ -503,11 +565,11 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
     return c;
   };
   // the next tile (called only while one is left: the ranges hold n_tiles tiles in all)
-  auto advance = [&](Cursor& c) {
+  auto advance = [&](Cursor& c) __attribute__((always_inline)) {
     c.ts += BN;
     c.kp += int64_t(BN) * Hkv * D * 2;
     c.vp += c.vstep;
-    if (__builtin_expect(c.ts >= c.hi, 0)) c = range_start(c.rg == 0 && n1 > 0 ? 1 : 2);
+    if (__builtin_expect(c.ts >= c.hi, 0)) c = range_start(c.rg == 0 ? (n1 > 0 ? 1 : 2) : c.rg + 1);
   };
   // Lane constants of the copies: wave w issues copy instructions I = w*IPW + ii; lane l of
   // instruction I fills 16-byte LDS slot 64 I + l.  Key slot -> row k_row = I * 64 / KCH + l / KCH and
@@ -583,24 +645,22 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
     const int I = w * TPW + i;  // uniform: copy instruction I fills image bytes [1024 I, 1024 I + 1024)
     const int slot_img = I * 64 + l;
     const int row = slot_img / TCH, slot = slot_img % TCH;
-    const int rr = row < nrows ? row : 0;
+    const int pos = row_info(row).pos;
     const unsigned char* src =
-        reinterpret_cast<const unsigned char*>(table) + int64_t(qpos_min + rr) * RB + ((slot ^ (row & 15)) << 4);
+        reinterpret_cast<const unsigned char*>(table) + int64_t(pos) * RB + ((slot ^ (row & 15)) << 4);
     async_copy16(src, lds + (I * 1024 < TILE_BYTES ? TILE_BYTES + I * 1024 : 3 * TILE_BYTES + I * 1024 - TILE_BYTES));
   }
   const float sl2 = 1.4426950408889634f * rsqrtf(float(D));
   u32x4v qf[2][NC];
-  int qpos[2], qrow[2];  // position and tile row of this lane's query column in block qb
+  int qrow[2];  // tile row of this lane's query column in block qb (its rotation table row)
   {
     u32x4v qa[2][NC / 2], qb_[2][NC / 2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int col = 32 * w + qb * 16 + r16;
       const int r = col / ng, hc = kvh * G + hg0 + col % ng;
-      const int rr = (active && r < nrows) ? r : 0;
-      qrow[qb] = rr;
-      qpos[qb] = qpos_min + r;
-      const int64_t rowbase = (int64_t(x0 + rr) * Hq + hc) * D + 8 * g4;
+      qrow[qb] = qvalid[qb] ? r : 0;
+      const int64_t rowbase = (int64_t(col_info(col).row) * Hq + hc) * D + 8 * g4;
 #pragma unroll
       for (int c = 0; c < NC / 2; ++c) {
         qa[qb][c] = *reinterpret_cast<const u32x4v*>(q + rowbase + 32 * c);
@@ -613,7 +673,7 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int rt = qrow[qb];  // table row (0 for columns past the tile)
-      const bool qv = active && (32 * w + qb * 16 + r16) / ng < nrows;
+      const bool qv = qvalid[qb];
       const unsigned char* trow = lds + (rt < 16 ? TILE_BYTES : 3 * TILE_BYTES) + (rt & 15) * RB;
 #pragma unroll
       for (int c = 0; c < NC / 2; ++c) {
@@ -663,12 +723,13 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
     constexpr int BUF = decltype(bufc)::value;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile t have landed
     __syncthreads();                // ... and every wave's; buffer BUF ^ 1 is free
-    const int ts = cur.ts, lo = cur.lo, hi = cur.hi;
+    const int ts = cur.ts, lo = cur.lo, hi = cur.hi, rg = cur.rg;
     if (t + 1 < n_tiles) {
       advance(cur);
       issue(cur, BUF ^ 1);
     }
     if (!active_s) return;
+    if (rg >= 2 && !((own_mask >> (rg - 2)) & 1)) return;  // another question's own rows: none of this wave's keys
     // lane addresses of the operand reads (the array is 1024-byte aligned, so the chunk XOR of bits
     // 6-7 commutes with adding its base); tile, buffer and block offsets are instruction immediates
     int kf = kfrag0;
@@ -706,13 +767,14 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
 
     // mask: key p is visible to query column q iff kmin(q) <= p <= kmax(q)
     const bool full = ts >= lo && ts + BN <= hi && ts + BN - 1 <= qpos_min &&
-                      (window == 0 || qpos_max - ts < window);
+                      (window == 0 || qpos_max - ts < window) && (rg < 2 || n_own == 1);
     u32x4v pf[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       if (!full) {
         const int kmin = window > 0 ? max(lo, qpos[qb] - window + 1) : lo;
-        const int kmax = min(hi - 1, qpos[qb]);
+        // an own range is visible to its own question's columns only
+        const int kmax = rg >= 2 && qown[qb] != rg - 2 ? -1 : min(hi - 1, qpos[qb]);
         const uint32_t span = uint32_t(kmax - kmin);
         const int pb = ts + 8 * g4 - kmin;
 #pragma unroll
@@ -779,7 +841,7 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   for (int qb = 0; qb < 2; ++qb) {
     const int row = qb * 16 + r16;  // staging row: the column's index in the wave
     const float l_col = rows4_sum(l_run[qb]);
-    const float inv = (32 * w + row) / ng < nrows ? 1.f / l_col : 0.f;
+    const float inv = col_info(32 * w + row).valid ? 1.f / l_col : 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const f32x4v a = acc[qb][db];
@@ -790,12 +852,24 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   }
   constexpr int RPI = 64 / CPR;  // rows per 16-byte-per-lane read (a wave's LDS accesses run in order)
   const int c16 = l % CPR;
+  if (ng == 4) {  // four heads: the wave's 32 columns are the 8 rows of unit w
+    const int urow = unit_desc[4 * w + TU_ROW0], unr = unit_desc[4 * w + TU_NROWS];
 #pragma unroll
-  for (int k = 0; k < BN / RPI; ++k) {
-    const int row = k * RPI + l / CPR;  // staging row = column 32 w + row
-    const u32x4v v = *reinterpret_cast<const u32x4v*>(ow + row * (D * 2) + ((c16 ^ (row & 15)) << 4));
-    const int col = 32 * w + row, qr = col / ng, hc = kvh * G + hg0 + col % ng;
-    if (qr < nrows) *reinterpret_cast<u32x4v*>(o + (int64_t(x0 + qr) * Hq + hc) * D + c16 * 8) = v;
+    for (int k = 0; k < BN / RPI; ++k) {
+      const int row = k * RPI + l / CPR;  // staging row = column 32 w + row: row row / 4 of unit w, head row % 4
+      const u32x4v v = *reinterpret_cast<const u32x4v*>(ow + row * (D * 2) + ((c16 ^ (row & 15)) << 4));
+      if (row / 4 < unr)
+        *reinterpret_cast<u32x4v*>(o + (int64_t(urow + row / 4) * Hq + kvh * G + hg0 + row % 4) * D + c16 * 8) = v;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < BN / RPI; ++k) {
+      const int row = k * RPI + l / CPR;  // staging row = column 32 w + row
+      const u32x4v v = *reinterpret_cast<const u32x4v*>(ow + row * (D * 2) + ((c16 ^ (row & 15)) << 4));
+      const int col = 32 * w + row, hc = kvh * G + hg0 + col % ng;
+      const ColInfo ci = col_info(col);
+      if (ci.valid) *reinterpret_cast<u32x4v*>(o + (int64_t(ci.row) * Hq + hc) * D + c16 * 8) = v;
+    }
   }
 }
 
@@ -928,14 +1002,11 @@ int launch_attn_core(const MetaView& mv, const flide_attn_params& p, const RopeA
     const bf16_t* vt = k_rot + int64_t(mv.T_cap) * p.Hkv * p.d;
     const int G = p.Hq / p.Hkv;
     dim3 grid(mv.tile_cap * p.Hkv * ((G + 3) / 4));  // tile_cap is a multiple of kXcdClasses
-    if (p.d == 256)
-      hipLaunchKernelGGL((attn_mfma_kernel<256>), grid, dim3(256), 0, st, mv, (const bf16_t*)q, k_rot, vt,
-                         (const bf16_t*)k_cache, (const bf16_t*)v_cache, (bf16_t*)o, rope.table, rope.max_pos, p.Hq,
-                         p.Hkv, W, p.cache_rows, p.cache_slots);
-    else
-      hipLaunchKernelGGL((attn_mfma_kernel<128>), grid, dim3(256), 0, st, mv, (const bf16_t*)q, k_rot, vt,
-                         (const bf16_t*)k_cache, (const bf16_t*)v_cache, (bf16_t*)o, rope.table, rope.max_pos, p.Hq,
-                         p.Hkv, W, p.cache_rows, p.cache_slots);
+    auto kernel = p.d == 256 ? (G % 4 == 0 ? attn_mfma_kernel<256, true> : attn_mfma_kernel<256, false>)
+                             : (G % 4 == 0 ? attn_mfma_kernel<128, true> : attn_mfma_kernel<128, false>);
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st, mv, (const bf16_t*)q, k_rot, vt, (const bf16_t*)k_cache,
+                       (const bf16_t*)v_cache, (bf16_t*)o, rope.table, rope.max_pos, p.Hq, p.Hkv, W, p.cache_rows,
+                       p.cache_slots);
     return int(hipGetLastError());
   }
   dim3 grid(mv.tile_cap, p.Hq);

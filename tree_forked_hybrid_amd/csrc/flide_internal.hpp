@@ -7,16 +7,26 @@
 
 namespace flide {
 
-// Query rows per attention work tile (rows of one segment; tiles never straddle segments).
+// Query rows per attention work tile: kTileUnits units of kUnitRows rows.  A unit holds rows of one segment;
+// a tile's units are consecutive rows of one trunk, or rows of up to four sibling questions.
 constexpr int kTileRows = 32;
+constexpr int kUnitRows = 8;
+constexpr int kTileUnits = kTileRows / kUnitRows;
 // XCDs of the chip: workgroup i of a grid runs on XCD i mod kXcdClasses.
 constexpr int kXcdClasses = 8;
 // int32 words of one attention work-list descriptor (filled on the device by meta_expand).
-constexpr int kTileDescWords = 16;
+constexpr int kTileDescWords = 48;
 // rows per GDN chunk: an interior checkpoint of a trunk sits at a multiple of it from the resume point
 constexpr int kCheckpointChunk = 64;
-enum TileDesc { TD_SEG, TD_ROW0, TD_NROWS, TD_QPOS0, TD_M, TD_P, TD_CKPT, TD_QUESTION, TD_ROFF_TRUNK, TD_ROFF_OWN,
-                TD_VOFF_TRUNK, TD_VOFF_OWN, TD_POS0 };
+// Descriptor words: the tile (segment of unit 0, -1 for an unused position; question flag; the request's
+// P, m, checkpoint slot, trunk row and value-column offsets; the first and last query position over its
+// units; the number of own-key ranges), then per unit u at TD_UNIT + 4 u: first row, rows (0: no unit),
+// first position, own range; per own range k at TD_OWN + 4 k: row offset, value-column offset, first and
+// one-past-last position.  An own range is one segment's rows (a trunk, or one question).
+enum TileDesc { TD_SEG, TD_QUESTION, TD_P, TD_M, TD_CKPT, TD_ROFF_TRUNK, TD_VOFF_TRUNK, TD_QPOS_MIN, TD_QPOS_MAX,
+                TD_NOWN, TD_UNIT = 16, TD_OWN = 32 };
+enum TileUnit { TU_ROW0, TU_NROWS, TU_QPOS0, TU_OWN };
+enum TileOwn { TO_ROFF, TO_VOFF, TO_LO, TO_HI };
 // Words of the metadata header.
 constexpr int kHdrWords = 64;
 constexpr int32_t kMagic = 0x464C4944;  // 'FLID'

@@ -6,7 +6,7 @@
 // positions continue from P), marks tail rows (-1, -1, -1) (Korean summary
 // §어떻게 쓰나: padding only at the tail), and writes one descriptor per
 // attention work-list position (tile_desc), so that an attention workgroup
-// reads its segment, request and key ranges with one 64-byte load.
+// reads its units, request and key ranges from one record.
 //
 // rope_k rotates every key row once to its metadata position (rotate-half
 // pairs (i, i + d/2), angle t * theta^(-2i/d), host fp64 table stored fp32), so
@@ -22,32 +22,66 @@ __global__ void __launch_bounds__(256) meta_expand_kernel(MetaView mv) {
                    mv.hdr[H_R] < 0 || mv.hdr[H_R] > mv.R_cap || mv.hdr[H_NQST] < 0 ||
                    mv.hdr[H_NQST] > mv.Q_cap || mv.hdr[H_NTILES] < 0 || mv.hdr[H_NTILES] > mv.tile_cap;
   const int stride = gridDim.x * blockDim.x;
-  // attention work-list descriptors: everything a tile's workgroup needs, in one 64-byte record
+  // attention work-list descriptors: everything a tile's workgroup needs, in one record
   const int n_tiles = bad ? 0 : mv.hdr[H_NTILES];
   for (int x = blockIdx.x * blockDim.x + threadIdx.x; x < mv.tile_cap; x += stride) {
     int32_t d[kTileDescWords];
 #pragma unroll
     for (int i = 0; i < kTileDescWords; ++i) d[i] = 0;
     d[TD_SEG] = -1;
-    const int s = x < n_tiles ? mv.tile_seg[x] : -1;
-    if (s >= 0 && s < n_seg) {
-      const int j = mv.seg_req[s];
-      const int row0 = mv.seg_row0[s], pos0 = mv.seg_pos0[s];
-      const int x0 = mv.tile_row0[x];
-      d[TD_SEG] = s;
-      d[TD_ROW0] = x0;
-      d[TD_NROWS] = min(kTileRows, row0 + mv.seg_len[s] - x0);
-      d[TD_QPOS0] = pos0 + (x0 - row0);
-      d[TD_M] = mv.req_m[j];
-      d[TD_P] = mv.req_P[j];
-      d[TD_CKPT] = mv.req_ckpt[j];
-      d[TD_QUESTION] = mv.seg_branch[s] > 0 ? 1 : 0;
-      d[TD_ROFF_TRUNK] = mv.req_trunk_row0[j] - mv.req_m[j];
-      d[TD_ROFF_OWN] = row0 - pos0;
-      d[TD_VOFF_TRUNK] = mv.seg_vcol0[j];  // the trunk segment of request j is segment j
-      d[TD_VOFF_OWN] = mv.seg_vcol0[s];
-      d[TD_POS0] = pos0;
-    } else if (s != -1) {
+    const int s0 = x < n_tiles ? mv.tile_seg[int64_t(x) * kTileUnits] : -1;
+    if (s0 >= 0 && s0 < n_seg) {
+      const int j = mv.seg_req[s0];
+      bool ok = true;
+      int own_seg[kTileUnits];
+      int nown = 0, qmin = INT_MAX, qmax = INT_MIN;
+#pragma unroll
+      for (int u = 0; u < kTileUnits; ++u) {
+        const int s = mv.tile_seg[int64_t(x) * kTileUnits + u];
+        if (s < 0) continue;
+        if (s >= n_seg || mv.seg_req[s] != j) {
+          ok = false;
+          continue;
+        }
+        const int row0 = mv.seg_row0[s], pos0 = mv.seg_pos0[s];
+        const int x0 = mv.tile_row0[int64_t(x) * kTileUnits + u];
+        const int nr = min(kUnitRows, row0 + mv.seg_len[s] - x0);
+        if (x0 < row0 || nr <= 0) {
+          ok = false;
+          continue;
+        }
+        int k = 0;
+        while (k < nown && own_seg[k] != s) ++k;
+        if (k == nown) {
+          own_seg[nown++] = s;
+          d[TD_OWN + 4 * k + TO_ROFF] = row0 - pos0;
+          d[TD_OWN + 4 * k + TO_VOFF] = mv.seg_vcol0[s];
+          d[TD_OWN + 4 * k + TO_LO] = pos0;
+        }
+        const int q0 = pos0 + (x0 - row0);
+        d[TD_OWN + 4 * k + TO_HI] = max(d[TD_OWN + 4 * k + TO_HI], q0 + nr);
+        d[TD_UNIT + 4 * u + TU_ROW0] = x0;
+        d[TD_UNIT + 4 * u + TU_NROWS] = nr;
+        d[TD_UNIT + 4 * u + TU_QPOS0] = q0;
+        d[TD_UNIT + 4 * u + TU_OWN] = k;
+        qmin = min(qmin, q0);
+        qmax = max(qmax, q0 + nr - 1);
+      }
+      if (ok) {
+        d[TD_SEG] = s0;
+        d[TD_QUESTION] = mv.seg_branch[s0] > 0 ? 1 : 0;
+        d[TD_P] = mv.req_P[j];
+        d[TD_M] = mv.req_m[j];
+        d[TD_CKPT] = mv.req_ckpt[j];
+        d[TD_ROFF_TRUNK] = mv.req_trunk_row0[j] - mv.req_m[j];
+        d[TD_VOFF_TRUNK] = mv.seg_vcol0[j];  // the trunk segment of request j is segment j
+        d[TD_QPOS_MIN] = qmin;
+        d[TD_QPOS_MAX] = qmax;
+        d[TD_NOWN] = nown;
+      } else {
+        flag_error(mv.dev_error, E_SEGMENT);
+      }
+    } else if (s0 != -1) {
       flag_error(mv.dev_error, E_SEGMENT);
     }
     int4* dst = reinterpret_cast<int4*>(mv.tile_desc + int64_t(x) * kTileDescWords);

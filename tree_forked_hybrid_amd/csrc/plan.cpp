@@ -45,8 +45,8 @@ flide_status compute_layout(const flide_caps& c, flide_meta_layout& L) {
   L.req_save_m = take(c.R_cap);
   L.req_save_slot = take(c.R_cap);
   L.qfin_row = take(c.Q_cap > 0 ? c.Q_cap : 1);
-  L.tile_seg = take(L.tile_cap);
-  L.tile_row0 = take(L.tile_cap);
+  L.tile_seg = take(int64_t(L.tile_cap) * kTileUnits);
+  L.tile_row0 = take(int64_t(L.tile_cap) * kTileUnits);
   L.gdn_order = take(L.seg_cap);
   L.host_words = o;
   L.tok_j = take(c.T_cap);
@@ -219,8 +219,13 @@ flide_status flide_plan_round(const flide_request* reqs, int32_t R, const flide_
       }
     }
     int32_t n_tiles = 0, tile_group = 0;
-    // Attention work list, indexed by the kernel's tile position x.  Tiles of kTileRows rows aligned to
-    // each segment's start; cost = keys seen by the tile's last row.  A request's tiles (trunk by
+    // Attention work list, indexed by the kernel's tile position x.  A tile is kTileUnits units of
+    // kUnitRows rows (unit u of position x: segment tile_seg[x kTileUnits + u], first row tile_row0[...],
+    // segment -1 for none).  A trunk's tiles are kTileRows rows aligned to its start.  The questions of a
+    // request are cut into units aligned to each question's start, and the request's question units are
+    // packed four to a tile in question order, so a tile may hold rows of up to four sibling questions
+    // (they share the request's cached and trunk keys; each sees its own rows only).  Cost = keys seen by
+    // the tile's last row.  A request's tiles (trunk by
     // position, then its questions, which read the trunk's keys) are cut into contiguous groups of at
     // most about 1/16 of the round's cost; the groups go, heaviest first, to the least loaded of
     // kXcdClasses classes, and class c's tiles take positions c, c + 8, c + 16, ... group by group
@@ -233,23 +238,45 @@ flide_status flide_plan_round(const flide_request* reqs, int32_t R, const flide_
       constexpr int32_t kLongTileGroup = 64;   // positions per run: the workgroups of one XCD (32 CUs x 2)
       struct Tile {
         int64_t cost;
-        int32_t seg, row0;
+        int32_t seg[kTileUnits], row0[kTileUnits];
       };
       std::vector<std::vector<Tile>> per_req(static_cast<size_t>(R));
       int64_t total = 0, n_all = 0;
-      auto add_segment = [&](int32_t s, std::vector<Tile>& out) {
-        const flide_request& r = reqs[s_req[s]];
-        for (int32_t a = 0; a < s_len[s]; a += kTileRows) {
-          const int32_t last = std::min(a + kTileRows, s_len[s]);
-          const int64_t cost = int64_t(r.m) + last + (s_br[s] > 0 ? int64_t(r.P - r.m) : 0);
-          out.push_back({cost, s, s_row0[s] + a});
-          total += cost;
-          ++n_all;
-        }
+      auto push = [&](Tile& t, std::vector<Tile>& out) {
+        out.push_back(t);
+        total += t.cost;
+        ++n_all;
+        t.cost = 0;
+        for (int u = 0; u < kTileUnits; ++u) t.seg[u] = -1, t.row0[u] = 0;
       };
+      Tile cur;
+      cur.cost = 0;
+      for (int u = 0; u < kTileUnits; ++u) cur.seg[u] = -1, cur.row0[u] = 0;
       for (int32_t j = 0; j < R; ++j) {
-        add_segment(j, per_req[size_t(j)]);
-        for (int32_t i = 0; i < reqs[j].n_q; ++i) add_segment(r_qs[j] + i, per_req[size_t(j)]);
+        const flide_request& r = reqs[j];
+        std::vector<Tile>& out = per_req[size_t(j)];
+        for (int32_t a = 0; a < s_len[j]; a += kTileRows) {  // trunk: whole tiles of one segment
+          for (int u = 0; u < kTileUnits && a + u * kUnitRows < s_len[j]; ++u)
+            cur.seg[u] = j, cur.row0[u] = s_row0[j] + a + u * kUnitRows;
+          cur.cost = int64_t(r.m) + std::min(a + kTileRows, s_len[j]);
+          push(cur, out);
+        }
+        int nu = 0;  // question units: packed in question order
+        for (int32_t i = 0; i < r.n_q; ++i) {
+          const int32_t s = r_qs[j] + i;
+          for (int32_t a = 0; a < s_len[s]; a += kUnitRows) {
+            cur.seg[nu] = s, cur.row0[nu] = s_row0[s] + a;
+            cur.cost = std::max(cur.cost, int64_t(r.P) + std::min(a + kUnitRows, s_len[s]));
+            if (++nu == kTileUnits) {
+              push(cur, out);
+              nu = 0;
+            }
+          }
+        }
+        if (nu > 0) {
+          push(cur, out);
+          nu = 0;
+        }
       }
       if (n_all > L.tile_cap) return FLIDE_E_INTERNAL;
       const int64_t target = std::max<int64_t>(1, (total + 15) / 16);
@@ -286,6 +313,12 @@ flide_status flide_plan_round(const flide_request* reqs, int32_t R, const flide_
       for (auto& v : cls) maxlen = std::max(maxlen, v.size());
       int32_t* t_seg = img.data() + L.tile_seg;
       int32_t* t_row = img.data() + L.tile_row0;
+      auto put = [&](int32_t x, const Tile* t) {  // position x of the work list (nullptr: unused)
+        for (int u = 0; u < kTileUnits; ++u) {
+          t_seg[int64_t(x) * kTileUnits + u] = t ? t->seg[u] : -1;
+          t_row[int64_t(x) * kTileUnits + u] = t ? t->row0[u] : 0;
+        }
+      };
       if (int64_t(maxlen) * kXcdClasses <= L.tile_cap) {
         n_tiles = int32_t(maxlen) * kXcdClasses;
         // Rounds whose tiles see thousands of keys each stream long key ranges through L2: there the
@@ -293,15 +326,9 @@ flide_status flide_plan_round(const flide_request* reqs, int32_t R, const flide_
         // workgroups resident on an XCD share one kv head's keys (measured on MI355X: 4-11% faster
         // attention on the fan-out and agent-resume rounds, 5% slower on short rounds).
         if (total >= kLongTileKeys * n_all) tile_group = kLongTileGroup;
-        for (int32_t x = 0; x < n_tiles; ++x) {
-          t_seg[x] = -1;
-          t_row[x] = 0;
-        }
+        for (int32_t x = 0; x < n_tiles; ++x) put(x, nullptr);
         for (int c = 0; c < kXcdClasses; ++c)
-          for (size_t k = 0; k < cls[c].size(); ++k) {
-            t_seg[k * kXcdClasses + size_t(c)] = cls[c][k].seg;
-            t_row[k * kXcdClasses + size_t(c)] = cls[c][k].row0;
-          }
+          for (size_t k = 0; k < cls[c].size(); ++k) put(int32_t(k * kXcdClasses + size_t(c)), &cls[c][k]);
       } else {
         // Unbalanced classes (a few large requests): one list, heaviest first, cut into bands of
         // kXcdClasses x kLongTileGroup tiles of similar cost.  Within a band the tiles are ordered by
@@ -319,11 +346,9 @@ flide_status flide_plan_round(const flide_request* reqs, int32_t R, const flide_
           const size_t nb = std::min(band, all.size() - b0);
           const size_t per = (nb + kXcdClasses - 1) / kXcdClasses;  // positions per class in this band
           std::stable_sort(all.begin() + b0, all.begin() + b0 + nb,
-                           [&](const Tile& x, const Tile& y) { return s_req[x.seg] < s_req[y.seg]; });
+                           [&](const Tile& x, const Tile& y) { return s_req[x.seg[0]] < s_req[y.seg[0]]; });
           for (size_t k = 0; k < per * kXcdClasses; ++k) {
-            const size_t x = (k0 + k % per) * kXcdClasses + k / per;
-            t_seg[x] = k < nb ? all[b0 + k].seg : -1;
-            t_row[x] = k < nb ? all[b0 + k].row0 : 0;
+            put(int32_t((k0 + k % per) * kXcdClasses + k / per), k < nb ? &all[b0 + k] : nullptr);
           }
           k0 += per;
         }

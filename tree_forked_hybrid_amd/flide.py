@@ -307,8 +307,9 @@ def decode_image(image: np.ndarray, caps: flide_caps) -> dict:
         off = getattr(L, name)
         out[name] = image[off:off + R].copy()
     out["qfin_row"] = image[L.qfin_row:L.qfin_row + n_qst].copy()
-    out["tile_seg"] = image[L.tile_seg:L.tile_seg + n_tiles].copy()
-    out["tile_row0"] = image[L.tile_row0:L.tile_row0 + n_tiles].copy()
+    # attention work list: [n_tiles, 4] units (segment -1: no unit)
+    out["tile_seg"] = image[L.tile_seg:L.tile_seg + 4 * n_tiles].reshape(n_tiles, 4).copy()
+    out["tile_row0"] = image[L.tile_row0:L.tile_row0 + 4 * n_tiles].reshape(n_tiles, 4).copy()
     out["gdn_order"] = image[L.gdn_order:L.gdn_order + n_seg].copy()
     return out
 
