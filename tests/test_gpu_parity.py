@@ -148,12 +148,17 @@ def _edge_reqs():
             Request(P=2, m=0, q_len=(4, 1), n_opt=(2, 5), out_slot=2),
             Request(P=9, m=0, q_len=(), n_opt=(), out_slot=3),
             Request(P=104, m=102, q_len=(5, 17), n_opt=(3, 2), ckpt_slot=6, out_slot=4),
-            Request(P=64, m=64, q_len=(2,), n_opt=(2,), ckpt_slot=7, out_slot=5)]
+            Request(P=64, m=64, q_len=(2,), n_opt=(2,), ckpt_slot=7, out_slot=5),
+            # many short siblings: query tiles that hold units of up to four questions
+            Request(P=90, m=0, q_len=(1, 2, 7, 8, 9, 3, 16, 1, 5), n_opt=(2,) * 9, out_slot=9)]
 
 
-@pytest.mark.parametrize("d", [256, 128])
-def test_edge_cases_mfma_path(ctx, d):
-    sh = LayerShapes(H=2, dk=32, dv=32, conv_k=4, Hq=8, Hkv=2, d=d, theta=1e4, hidden=64, swa_window=40)
+@pytest.mark.parametrize("d,Hq", [(256, 8), (128, 8), (256, 12), (128, 4)])
+def test_edge_cases_mfma_path(ctx, d, Hq):
+    """Ragged, empty and resumed requests on the matrix-core attention path.  Four q heads per kv head
+    (G = 4: each wave holds one 8-row unit of a packed tile), six (head groups of four and two) and two
+    (one group of two): the two kernel forms that map query columns to waves."""
+    sh = LayerShapes(H=2, dk=32, dv=32, conv_k=4, Hq=Hq, Hkv=2, d=d, theta=1e4, hidden=64, swa_window=40)
     rnd = custom_round(sh, "bf16", _edge_reqs(), base=23)
     bufs, lay = harness.run_gpu(rnd, ctx, "direct")
     harness.check_round(rnd, harness.outputs(bufs), lay, mode="isolated")
