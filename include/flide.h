@@ -133,6 +133,9 @@ typedef struct {
  *   tile_row0   [tile_cap * 4] ... and its first stream row.  A tile's units
  *                          are consecutive rows of one trunk, or rows of up to
  *                          four questions of one request
+ *   tile_swa    [tile_cap] the windowed layer's order of the same work list:
+ *                          entry i is the position its i-th workgroup (per
+ *                          head group) takes, -1 for none
  *   gdn_order   [seg_cap]  GDN work list: trunk segments, then question segments,
  *                          each by length, longest first (ties in stream order)
  *   tok_j/c/t   [T_cap]    per-row metadata (device only)
@@ -152,7 +155,7 @@ typedef struct {
   int64_t seg_row0, seg_len, seg_req, seg_branch, seg_pos0, seg_state, seg_vcol0;
   int64_t req_trunk_row0, req_P, req_m, req_ckpt, req_out, req_q_seg0, req_nq, req_save_m, req_save_slot;
   int64_t qfin_row;
-  int64_t tile_seg, tile_row0;
+  int64_t tile_seg, tile_row0, tile_swa;
   int64_t gdn_order;
   int64_t tok_j, tok_c, tok_t;
   int64_t tile_desc;

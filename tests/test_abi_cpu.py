@@ -104,6 +104,10 @@ def _assert_same_layout(reqs, caps):
         lens = [int(ref["seg_len"][s]) for s in range(ref["n_seg"]) if ref["seg_req"][s] == j and ref["seg_branch"][s] > 0]
         units = sum((n + 7) // 8 for n in lens)
         assert n_qtiles.get(j, 0) == (units + 3) // 4
+    # the windowed layer's order: every used position exactly once, nothing else
+    used_pos = sorted(int(x) for x in range(len(got["tile_seg"])) if got["tile_seg"][x][0] >= 0)
+    swa = [int(x) for x in got["tile_swa"] if x >= 0]
+    assert sorted(swa) == used_pos
     # the GDN work list: trunks then questions, each a permutation ordered by length (longest first,
     # ties in stream order)
     R, n_seg = ref["R"], ref["n_seg"]

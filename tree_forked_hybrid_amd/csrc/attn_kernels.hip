@@ -402,12 +402,13 @@ attn_mfma_kernel(MetaView mv, const bf16_t* __restrict__ q, const bf16_t* __rest
   const int xcd = int(blockIdx.x % kXcdClasses);
   int tile = kXcdClasses * (i8 / HY) + xcd, yy = i8 % HY;
   // The classes are balanced by the cost of full attention (keys up to a tile's last row).  A windowed layer's
-  // tiles see at most W + 31 keys each, so for it that balance does not hold: it takes the positions in list
-  // order, the head groups of a position one after another, on whichever XCD is free (the long-document
-  // round's window layer: 592 -> 579 us, measured).
+  // tiles see at most W + 31 keys each, so for it that balance does not hold: it takes the positions in the
+  // planner's windowed order (tile_swa: the band order of the same tiles), the head groups of a position one
+  // after another, on whichever XCD is free.
   if (window > 0) {
-    tile = int(blockIdx.x) / HY;
+    tile = mv.tile_swa[int(blockIdx.x) / HY];  // the grid has tile_cap entries per head group
     yy = int(blockIdx.x) % HY;
+    if (tile < 0 || tile >= mv.tile_cap) return;  // no position (the descriptor read below needs one)
   }
 
   // the position's descriptor (written by meta_expand): one 64-byte load instead of a chain of table

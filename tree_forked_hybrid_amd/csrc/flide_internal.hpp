@@ -88,6 +88,7 @@ struct MetaView {
   const int32_t* qfin_row;
   const int32_t* tile_seg;
   const int32_t* tile_row0;
+  const int32_t* tile_swa;
   const int32_t* gdn_order;
   int32_t* tok_j;
   int32_t* tok_c;
@@ -119,6 +120,7 @@ inline MetaView make_view(int32_t* base, const flide_meta_layout& L, const flide
   v.qfin_row = base + L.qfin_row;
   v.tile_seg = base + L.tile_seg;
   v.tile_row0 = base + L.tile_row0;
+  v.tile_swa = base + L.tile_swa;
   v.gdn_order = base + L.gdn_order;
   v.tok_j = base + L.tok_j;
   v.tok_c = base + L.tok_c;

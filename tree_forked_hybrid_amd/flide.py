@@ -50,7 +50,7 @@ class flide_meta_layout(C.Structure):
         "host_words", "dev_words", "hdr", "seg_row0", "seg_len", "seg_req", "seg_branch", "seg_pos0",
         "seg_state", "seg_vcol0", "req_trunk_row0", "req_P", "req_m", "req_ckpt", "req_out", "req_q_seg0", "req_nq",
         "req_save_m", "req_save_slot",
-        "qfin_row", "tile_seg", "tile_row0", "gdn_order", "tok_j", "tok_c", "tok_t", "tile_desc", "dev_error")] + \
+        "qfin_row", "tile_seg", "tile_row0", "tile_swa", "gdn_order", "tok_j", "tok_c", "tok_t", "tile_desc", "dev_error")] + \
         [("seg_cap", C.c_int32), ("tile_cap", C.c_int32), ("tile_rows", C.c_int32), ("reserved", C.c_int32)]
 
 
@@ -310,6 +310,7 @@ def decode_image(image: np.ndarray, caps: flide_caps) -> dict:
     # attention work list: [n_tiles, 4] units (segment -1: no unit)
     out["tile_seg"] = image[L.tile_seg:L.tile_seg + 4 * n_tiles].reshape(n_tiles, 4).copy()
     out["tile_row0"] = image[L.tile_row0:L.tile_row0 + 4 * n_tiles].reshape(n_tiles, 4).copy()
+    out["tile_swa"] = image[L.tile_swa:L.tile_swa + L.tile_cap].copy()  # windowed layer's order, -1: none
     out["gdn_order"] = image[L.gdn_order:L.gdn_order + n_seg].copy()
     return out
 
